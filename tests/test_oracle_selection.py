@@ -1,0 +1,261 @@
+"""Pins for the oracle's block summaries, scores, k computation, Top-k and
+span merge (SparPR news page, "Three decisions rather than one compression
+ratio": Query-Aware key-block selection, Dynamic budget control, On-demand
+local recomputation with cost-aware fallback; DKV abstract for the exact
+recency window).
+
+Every expected value here is fixed independently of the oracle's code: a
+closed form, a hand computation written out in the test, a brute-force
+enumeration, or an exact special case."""
+
+import itertools
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+from query_aware_sparse_block_amd import workloads as wl
+
+
+# ---- k, window and the dense-fallback decision -----------------------------
+
+# (label, L, P, W, top_k, keep_num, keep_den, floor, gamma) -> (n, C, k_eff, dense)
+# Hand arithmetic for each row is in the comment beside it.
+PLAN_TABLE = [
+    # tiny fp32 MHA: n = 1024/16 = 64, C = (1024-32)//16 = 62
+    ("tiny k8", 1024, 16, 32, 8, 1, 1, 4, (1, 1), (64, 62, 8, 0)),
+    ("tiny k2 floor binds", 1024, 16, 32, 2, 1, 1, 4, (1, 1), (64, 62, 4, 0)),
+    ("tiny k64 clamps to C", 1024, 16, 32, 64, 1, 1, 4, (1, 1), (64, 62, 62, 0)),
+    ("tiny k64 gamma 1/10", 1024, 16, 32, 64, 1, 1, 4, (1, 10), (64, 62, 62, 1)),
+    # OPT-like: C = (L-128)//64; keep 1/2 -> ceil(C/2); keep 1/10 -> ceil(C/10)
+    ("opt L1024 1/2", 1024, 64, 128, 0, 1, 2, 1, (1, 1), (16, 14, 7, 0)),
+    ("opt L1024 1/10", 1024, 64, 128, 0, 1, 10, 1, (1, 1), (16, 14, 2, 0)),     # ceil(1.4)
+    ("opt L2048 1/2", 2048, 64, 128, 0, 1, 2, 1, (1, 1), (32, 30, 15, 0)),
+    ("opt L2048 1/10", 2048, 64, 128, 0, 1, 10, 1, (1, 1), (32, 30, 3, 0)),
+    ("opt L4096 1/2", 4096, 64, 128, 0, 1, 2, 1, (1, 1), (64, 62, 31, 0)),
+    ("opt L4096 1/10", 4096, 64, 128, 0, 1, 10, 1, (1, 1), (64, 62, 7, 0)),     # ceil(6.2)
+    ("opt L8192 1/2", 8192, 64, 128, 0, 1, 2, 1, (1, 1), (128, 126, 63, 0)),
+    ("opt L8192 1/10", 8192, 64, 128, 0, 1, 10, 1, (1, 1), (128, 126, 13, 0)),  # ceil(12.6)
+    # MiniCPM-like: C = (131072-256)//64 = 2044; ceil(2044/32)=64, /16 -> 128, /8 -> 256
+    ("minicpm 1/32", 131072, 64, 256, 0, 1, 32, 1, (1, 1), (2048, 2044, 64, 0)),
+    ("minicpm 1/16", 131072, 64, 256, 0, 1, 16, 1, (1, 1), (2048, 2044, 128, 0)),
+    ("minicpm 1/8", 131072, 64, 256, 0, 1, 8, 1, (1, 1), (2048, 2044, 256, 0)),
+    # Qwen-like: C = (L-1024)//256, k = min(16, C)
+    ("qwen 4k", 4096, 256, 1024, 16, 1, 1, 1, (1, 1), (16, 12, 12, 0)),
+    ("qwen 8k", 8192, 256, 1024, 16, 1, 1, 1, (1, 1), (32, 28, 16, 0)),
+    ("qwen 16k", 16384, 256, 1024, 16, 1, 1, 1, (1, 1), (64, 60, 16, 0)),
+    ("qwen 32k", 32768, 256, 1024, 16, 1, 1, 1, (1, 1), (128, 124, 16, 0)),
+    ("qwen 64k", 65536, 256, 1024, 16, 1, 1, 1, (1, 1), (256, 252, 16, 0)),
+    # batched serving: C = 512; 512/32 = 16; ceil(512*7/10) = ceil(358.4) = 359,
+    # 359*5 = 1795 > 3*512 = 1536 -> dense
+    ("serving 1/32", 32768, 64, 0, 0, 1, 32, 1, (3, 5), (512, 512, 16, 0)),
+    ("serving 7/10", 32768, 64, 0, 0, 7, 10, 1, (3, 5), (512, 512, 359, 1)),
+    # edges: context inside the window; ragged tail; gamma equality is not dense
+    ("inside window", 20, 16, 32, 8, 1, 1, 4, (1, 1), (2, 0, 0, 0)),
+    ("ragged tail", 1000, 16, 32, 8, 1, 1, 4, (1, 1), (63, 60, 8, 0)),           # (1000-32)//16
+    ("gamma equal", 640, 64, 0, 6, 1, 1, 1, (3, 5), (10, 10, 6, 0)),             # 6/10 == 3/5
+    ("gamma above", 640, 64, 0, 7, 1, 1, 1, (3, 5), (10, 10, 7, 1)),
+    ("ratio 313/10000", 512 * 64, 64, 0, 0, 313, 10000, 1, (1, 1), (512, 512, 17, 0)),  # ceil(16.03)
+]
+
+
+@pytest.mark.parametrize("row", PLAN_TABLE, ids=[r[0] for r in PLAN_TABLE])
+def test_plan_table(row):
+    _, L, P, W, k, num, den, floor, (gn, gd), (n, C, k_eff, dense) = row
+    p = oracle.plan(L, P, W, top_k=k, keep_num=num, keep_den=den, keep_floor=floor,
+                    gamma_num=gn, gamma_den=gd)
+    assert (p["n"], p["C"], p["k_eff"], p["use_dense"]) == (n, C, k_eff, dense)
+
+
+def test_plan_ratio_is_exact_rational():
+    # ceil(512 * 313 / 10000) = ceil(16.0256) = 17 but ceil(512 * 1/32) = 16:
+    # the "3.13 %" keep is the halving 1/32, not the decimal.
+    assert oracle.plan(32768, 64, 0, keep_num=1, keep_den=32)["k_eff"] == 16
+    assert oracle.plan(32768, 64, 0, keep_num=313, keep_den=10000)["k_eff"] == 17
+
+
+# ---- block summaries ---------------------------------------------------------
+
+def _index_pool(num_phys, Hkv, P, D):
+    """K[phys][g][t][d] = 4096*phys + 256*g + d + t/8 (exact in float32)."""
+    phys = np.arange(num_phys)[:, None, None, None]
+    g = np.arange(Hkv)[None, :, None, None]
+    t = np.arange(P)[None, None, :, None]
+    d = np.arange(D)[None, None, None, :]
+    return (4096.0 * phys + 256.0 * g + d + t / 8.0).astype(np.float32)
+
+
+@pytest.mark.parametrize("P", [1, 4, 16])
+def test_summary_closed_form(P):
+    Hkv, D, num_phys = 3, 8, 5
+    pool = _index_pool(num_phys, Hkv, P, D)
+    for phys in range(num_phys):
+        for g in range(Hkv):
+            s = oracle.block_summary("fp32", pool, Hkv, P, D, phys, g)
+            # mean over t of t/8 is (P-1)/16
+            expect = 4096.0 * phys + 256.0 * g + np.arange(D) + (P - 1) / 16.0
+            assert np.array_equal(s, expect)
+
+
+def test_summary_of_single_token_block_is_the_key():
+    rng = np.random.default_rng(1)
+    pool = wl.f32_to_bf16_bits(rng.standard_normal((4, 2, 1, 16)).astype(np.float32))
+    for phys in range(4):
+        for g in range(2):
+            s = oracle.block_summary("bf16", pool, 2, 1, 16, phys, g)
+            assert np.array_equal(s, oracle.widen("bf16", pool[phys, g, 0]))
+
+
+def test_summaries_follow_block_table_and_skip_partial_blocks():
+    Hkv, P, D = 2, 4, 8
+    pool = _index_pool(10, Hkv, P, D)
+    bt = np.array([[7, 2, 9], [0, 5, 1]], np.int32)
+    ctx = np.array([11, 12], np.int32)          # seq 0: 2 full blocks + 3 tokens
+    s = oracle.summaries("fp32", pool, bt, ctx, Hkv, P, D)
+    for b in range(2):
+        for j in range(3):
+            if j < ctx[b] // P:
+                for g in range(Hkv):
+                    expect = 4096.0 * bt[b, j] + 256.0 * g + np.arange(D) + (P - 1) / 16.0
+                    assert np.array_equal(s[b, j, g], expect)
+            else:
+                assert np.isnan(s[b, j]).all()
+
+
+# ---- scores ------------------------------------------------------------------
+
+@pytest.mark.parametrize("Hq,Hkv", [(4, 4), (8, 2), (6, 2), (12, 1)])
+def test_score_equals_block_mean_of_head_summed_logits(Hq, Hkv):
+    """score_j = (1/P) * sum_t sum_h <q_h, K_{t, g(h)}> (by linearity), computed
+    here by brute force on raw keys, with a different G per case so that a
+    wrong head-to-KV-head map fails."""
+    rng = np.random.default_rng(Hq * 10 + Hkv)
+    B, D, P, nb = 1, 16, 8, 6
+    G = Hq // Hkv
+    # dyadic values: every product and sum below is exact in double
+    pool = (rng.integers(-8, 9, (nb, Hkv, P, D)) / 4.0).astype(np.float32)
+    q = (rng.integers(-8, 9, (B, Hq, D)) / 8.0).astype(np.float32)
+    bt = rng.permutation(nb).astype(np.int32)[None, :]
+    ctx = np.array([nb * P], np.int32)
+    summ = oracle.summaries("fp32", pool, bt, ctx, Hkv, P, D)
+    got = oracle.scores("fp32", q[0], summ[0], Hq, Hkv, D, nb)
+    for j in range(nb):
+        tot = 0.0
+        for h in range(Hq):
+            for t in range(P):
+                tot += float(np.dot(q[0, h].astype(np.float64),
+                                    pool[bt[0, j], h // G, t].astype(np.float64)))
+        assert got[j] == tot / P
+
+
+def test_zero_query_scores_zero_and_selects_lowest_indices():
+    rng = np.random.default_rng(3)
+    pool = rng.standard_normal((12, 2, 4, 8)).astype(np.float32)
+    q = np.zeros((1, 4, 8), np.float32)
+    bt = np.arange(12, dtype=np.int32)[None]
+    summ = oracle.summaries("fp32", pool, bt, np.array([48], np.int32), 2, 4, 8)
+    sc = oracle.scores("fp32", q[0], summ[0], 4, 2, 8, 12)
+    assert np.all(sc == 0.0)
+    for k in range(13):
+        assert oracle.topk(sc, k).tolist() == list(range(k))
+
+
+def test_duplicate_block_tie_goes_to_lower_index():
+    rng = np.random.default_rng(4)
+    pool = rng.standard_normal((6, 1, 4, 8)).astype(np.float32)
+    q = rng.standard_normal((1, 1, 8)).astype(np.float32)
+    bt = np.arange(6, dtype=np.int32)[None]
+    summ = oracle.summaries("fp32", pool, bt, np.array([24], np.int32), 1, 4, 8)
+    sc = oracle.scores("fp32", q[0], summ[0], 1, 1, 8, 6)
+    best = int(np.argmax(sc))
+    # physical block 5 <- copy of the best block: logical 5 now ties with `best`
+    pool2 = pool.copy()
+    pool2[5] = pool[best]
+    summ2 = oracle.summaries("fp32", pool2, bt, np.array([24], np.int32), 1, 4, 8)
+    sc2 = oracle.scores("fp32", q[0], summ2[0], 1, 1, 8, 6)
+    if best != 5:
+        assert sc2[5] == sc2[best]
+        assert oracle.topk(sc2, 1).tolist() == [min(best, 5)]
+
+
+# ---- Top-k -------------------------------------------------------------------
+
+def _outranks(score, a, b):
+    return score[a] > score[b] or (score[a] == score[b] and a < b)
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_topk_matches_subset_enumeration(seed):
+    rng = np.random.default_rng(seed)
+    C = int(rng.integers(1, 11))
+    # dyadic scores with deliberate ties; sums of them are exact in double
+    score = rng.integers(-6, 7, C) / 4.0
+    for k in range(0, C + 1):
+        got = oracle.topk(score, k).tolist()
+        dominating = []
+        for sub in itertools.combinations(range(C), k):
+            rest = [j for j in range(C) if j not in sub]
+            if all(_outranks(score, a, b) for a in sub for b in rest):
+                dominating.append(list(sub))
+        assert len(dominating) == 1
+        assert got == dominating[0]
+        # it also maximises the score sum; ties -> lexicographically smallest
+        best = max(sum(score[list(s)]) for s in itertools.combinations(range(C), k))
+        ties = [list(s) for s in itertools.combinations(range(C), k)
+                if sum(score[list(s)]) == best]
+        assert got == min(ties)
+
+
+def test_topk_matches_sort_by_key():
+    rng = np.random.default_rng(11)
+    for _ in range(20):
+        C = int(rng.integers(1, 300))
+        score = np.round(rng.standard_normal(C), 1)
+        k = int(rng.integers(0, C + 1))
+        ref = sorted(sorted(range(C), key=lambda j: (-score[j], j))[:k])
+        assert oracle.topk(score, k).tolist() == ref
+
+
+def test_topk_treats_signed_zeros_as_equal():
+    score = np.array([0.0, -0.0, 0.0, -0.0, -1.0])
+    assert oracle.topk(score, 2).tolist() == [0, 1]
+    score = np.array([-0.0, 0.0])
+    assert oracle.topk(score, 1).tolist() == [0]
+
+
+# ---- spans -------------------------------------------------------------------
+
+def test_spans_hand_example():
+    got = oracle.spans(np.array([1, 2, 3, 7, 9, 10]), C=12, n=14)
+    assert got.tolist() == [[1, 4], [7, 8], [9, 11], [12, 14]]
+    got = oracle.spans(np.array([1, 2, 3, 7, 9, 10, 11]), C=12, n=14)
+    assert got.tolist() == [[1, 4], [7, 8], [9, 14]]
+    assert oracle.spans(np.array([], np.int32), C=0, n=3).tolist() == [[0, 3]]
+    assert oracle.spans(np.array([0, 1, 2]), C=3, n=3).tolist() == [[0, 3]]
+
+
+def test_spans_invariants_random():
+    rng = np.random.default_rng(5)
+    for _ in range(200):
+        C = int(rng.integers(0, 40))
+        n = C + int(rng.integers(0, 4))
+        k = int(rng.integers(0, C + 1))
+        sel = np.sort(rng.choice(C, k, replace=False)).astype(np.int32) if k else \
+            np.array([], np.int32)
+        sp = oracle.spans(sel, C, n)
+        covered = [j for a, b in sp.tolist() for j in range(a, b)]
+        assert covered == sorted(set(sel.tolist()) | set(range(C, n)))
+        for (a0, b0), (a1, b1) in zip(sp[:-1].tolist(), sp[1:].tolist()):
+            assert b0 < a1            # disjoint, sorted, and maximal (a gap between)
+        assert all(a < b for a, b in sp.tolist())
+
+
+# ---- attended token set ------------------------------------------------------
+
+def test_attended_tokens_sparse_and_dense():
+    toks = oracle.attended_tokens(L=70, P=16, C=2, sel=np.array([1]), use_dense=0)
+    assert toks.tolist() == list(range(16, 32)) + list(range(32, 70))
+    toks = oracle.attended_tokens(L=70, P=16, C=2, sel=np.array([1]), use_dense=1)
+    assert toks.tolist() == list(range(70))
+    assert math.isclose(len(oracle.attended_tokens(1024, 16, 62, np.arange(8), 0)), 160)
