@@ -1,0 +1,263 @@
+#!/usr/bin/env python3
+"""Decode-attention benchmark on one MI355X.
+
+A step is one decode step of query-aware sparse block attention for the
+whole batch: kvsp_score_topk (block scores from the resident summaries, Top-k
+with the keep floor, spans, dense-fallback flags) followed by
+kvsp_sparse_decode (split-KV attention over the kept blocks and the exact
+window, log-sum-exp merge; flagged sequences attend densely). Summaries are
+built once before timing, as they are resident between steps.
+
+Prints ONE JSON line: steps/s for the step, selected-KV GB/s of the attention
+call against the 8 TB/s HBM3E peak, and the CPU oracle timed on this host.
+
+  python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+HBM_PEAK_GBPS = 8000.0
+METRIC = "decode-attn steps/sec + selected-KV GB/s (% of HBM peak) on 1 MI355X"
+
+
+def workloads():
+    from query_aware_sparse_block_amd import workloads as wl
+    return {
+        "opt6.7b-mha-fp16-B4-L8192-keep1/2": lambda: wl.c2(L=8192, keep="1/2"),
+        "opt6.7b-mha-fp16-B4-L8192-keep1/10": lambda: wl.c2(L=8192, keep="1/10"),
+        "minicpm4.1-8b-gqa-bf16-L131072-keep1/32": lambda: wl.c3(keep="1/32"),
+        "minicpm4.1-8b-gqa-bf16-L131072-keep1/8": lambda: wl.c3(keep="1/8"),
+        "qwen2.5-1.5b-gqa-bf16-L65536-top16": lambda: wl.c4(L=65536),
+        "serving-gqa-bf16-B64-L32768-keep1/32": lambda: wl.c5(keep="1/32"),
+        "serving-gqa-bf16-B64-L32768-keep7/10-dense": lambda: wl.c5(keep="7/10"),
+        "tiny-mha-fp32-L1024-top8": lambda: wl.c1("k8"),
+    }
+
+
+DEFAULT_WORKLOAD = "opt6.7b-mha-fp16-B4-L8192-keep1/2"
+
+
+def attended_tokens_per_seq(case, num_selected, use_dense):
+    """Tokens each sequence attends (byte accounting from the step's own
+    outputs: k kept blocks plus the window, or the whole context)."""
+    out = []
+    for b in range(case.B):
+        L = int(case.ctx_lens[b])
+        if int(use_dense[b]):
+            out.append(L)
+            continue
+        C = max(0, L - case.recent_window) // case.P
+        out.append(int(num_selected[b]) * case.P + (L - C * case.P))
+    return out
+
+
+def attention_bytes(case, tokens):
+    """Algorithmic bytes of one attention call: each attended token's key and
+    value rows for every KV head (2*D*E per token per KV head), the queries,
+    the outputs and lse, and the block-table / selection entries read."""
+    E = {"fp32": 4, "fp16": 2, "bf16": 2}[case.dtype]
+    kv = sum(tokens) * case.Hkv * 2 * case.D * E
+    q = case.B * case.Hq * case.D * E
+    out = case.B * case.Hq * (case.D + 1) * 4
+    blocks = sum(-(-t // case.P) for t in tokens)
+    table = blocks * 4 * 2
+    return kv + q + out + table, kv
+
+
+def scoring_bytes(case, plans_C):
+    return sum(plans_C) * case.Hkv * case.D * 4 + case.B * case.Hq * case.D * 2
+
+
+def time_cpu_oracle(case, budget_s=10.0):
+    """The oracle, as it stands, timed on this host: one whole decode step
+    (scores, Top-k, spans, attention for every (sequence, head); summaries
+    precomputed like the GPU's). Repeated until `budget_s` of CPU work."""
+    import oracle
+    summ = oracle.summaries(case.dtype, case.k_pool, case.block_table, case.ctx_lens, case.Hkv,
+                            case.P, case.D)
+    times = []
+    t_start = time.perf_counter()
+    while True:
+        t0 = time.perf_counter()
+        oracle.decode_step(case.dtype, case.q, case.k_pool, case.v_pool, case.block_table,
+                           case.ctx_lens, summ, Hkv=case.Hkv, P=case.P, **case.select_params)
+        times.append(time.perf_counter() - t0)
+        if time.perf_counter() - t_start > budget_s or len(times) >= 50:
+            break
+    times.sort()
+    med = times[len(times) // 2]
+    return dict(value=1.0 / med, unit="steps/s", cores=1, kind="oracle",
+                sample=f"{len(times)} whole steps of the same workload "
+                       f"(median {med * 1e3:.1f} ms/step), single-threaded C++ double")
+
+
+def time_cpu_oracle_sampled(case, n_pairs=64, budget_s=20.0):
+    """For workloads too large for whole oracle steps: scores + Top-k for every
+    sequence, attention for a sample of (sequence, head) pairs, scaled to the
+    whole batch."""
+    import numpy as np
+
+    import oracle
+    summ = oracle.summaries(case.dtype, case.k_pool, case.block_table, case.ctx_lens, case.Hkv,
+                            case.P, case.D)
+    rng = np.random.default_rng(0)
+    pairs = set()
+    while len(pairs) < min(n_pairs, case.B * case.Hq):
+        pairs.add((int(rng.integers(case.B)), int(rng.integers(case.Hq))))
+    mask = np.zeros((case.B, case.Hq), np.uint8)
+    t0 = time.perf_counter()
+    oracle.decode_step(case.dtype, case.q, case.k_pool, case.v_pool, case.block_table,
+                       case.ctx_lens, summ, Hkv=case.Hkv, P=case.P, head_mask=mask,
+                       **case.select_params)
+    t_sel = time.perf_counter() - t0
+    for b, h in pairs:
+        mask[b, h] = 1
+    t0 = time.perf_counter()
+    oracle.decode_step(case.dtype, case.q, case.k_pool, case.v_pool, case.block_table,
+                       case.ctx_lens, summ, Hkv=case.Hkv, P=case.P, head_mask=mask,
+                       **case.select_params)
+    t_with = time.perf_counter() - t0
+    per_pair = max(t_with - t_sel, 1e-9) / len(pairs)
+    total = t_sel + per_pair * case.B * case.Hq
+    return dict(value=1.0 / total, unit="steps/s", cores=1, kind="oracle",
+                sample=f"selection for all {case.B} sequences + attention for {len(pairs)} of "
+                       f"{case.B * case.Hq} (sequence, head) pairs, scaled to the batch; "
+                       f"single-threaded C++ double")
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--replicas", type=int, default=0,
+                    help="device copies of the pool rotated per step (0: enough for 2 GiB)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the library has "
+              "no multi-GPU path.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from query_aware_sparse_block_amd import device as dev
+    from query_aware_sparse_block_amd import kvsp
+
+    kvsp.library()
+    wls = workloads()
+    if args.workload not in wls:
+        sys.exit(f"unknown workload {args.workload}; choose from {sorted(wls)}")
+    print(f"[bench] generating {args.workload}", file=sys.stderr, flush=True)
+    case = wls[args.workload]()
+    dc0 = dev.upload(case)
+    pool_bytes = dc0.k_pool.numel() * dc0.k_pool.element_size() * 2
+    R = args.replicas or max(1, -(-(2 << 30) // pool_bytes))
+    # Distinct device copies (different addresses) so successive steps do not
+    # hit data a previous step left in the 256 MB Infinity Cache.
+    reps = [dc0]
+    for _ in range(R - 1):
+        reps.append(dev.DeviceCase(case, dc0.q.clone(), dc0.k_pool.clone(), dc0.v_pool.clone(),
+                                   dc0.block_table.clone(), dc0.ctx_lens.clone(), dc0.layout,
+                                   dc0.params))
+    bufs = [dev.alloc_buffers(d) for d in reps]
+    for d, bf in zip(reps, bufs):
+        dev.build_summaries(d, bf)
+    torch.cuda.synchronize()
+    print(f"[bench] {R} replica(s) of {pool_bytes / 2**30:.2f} GiB resident", file=sys.stderr,
+          flush=True)
+
+    stream = torch.cuda.current_stream()
+    for i in range(args.warmup):
+        dev.decode_step(reps[i % R], bufs[i % R])
+    torch.cuda.synchronize()
+
+    def timed(fn, n):
+        start = torch.cuda.Event(enable_timing=True)
+        stop = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        start.record(stream)
+        for i in range(n):
+            fn(i)
+        stop.record(stream)
+        torch.cuda.synchronize()
+        return start.elapsed_time(stop) / 1e3  # seconds
+
+    step_s = timed(lambda i: dev.decode_step(reps[i % R], bufs[i % R]), args.steps)
+    attn_s = timed(lambda i: dev.sparse_decode(reps[i % R], bufs[i % R]), args.steps)
+    sel_s = timed(lambda i: dev.score_topk(reps[i % R], bufs[i % R]), args.steps)
+
+    nsel = bufs[0].num_selected.cpu().numpy()
+    dense = bufs[0].use_dense.cpu().numpy()
+    tokens = attended_tokens_per_seq(case, nsel, dense)
+    attn_bytes, kv_bytes = attention_bytes(case, tokens)
+    Cs = [max(0, int(L) - case.recent_window) // case.P for L in case.ctx_lens]
+    attn_avg = attn_s / args.steps
+    achieved = attn_bytes / attn_avg / 1e9
+    ms_per_step = step_s / args.steps * 1e3
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
+        big = sum(tokens) * case.Hq * case.D > 2e9
+        cpu = time_cpu_oracle_sampled(case) if big else time_cpu_oracle(case)
+        cpu["cores_available"] = os.cpu_count()
+
+    E = {"fp32": 4, "fp16": 2, "bf16": 2}[case.dtype]
+    rec = {
+        "metric": METRIC,
+        "value": args.steps / step_s,
+        "unit": "steps/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": case.dtype,
+        "data": "synthetic",
+        "config": {
+            "workload": args.workload,
+            "batch": case.B, "q_heads": case.Hq, "kv_heads": case.Hkv, "head_dim": case.D,
+            "block": case.P, "contexts": sorted(set(int(x) for x in case.ctx_lens)),
+            "top_k": case.top_k, "keep": f"{case.keep_num}/{case.keep_den}",
+            "keep_floor": case.keep_floor, "recent_window": case.recent_window,
+            "gamma": f"{case.gamma_num}/{case.gamma_den}",
+            "attended_tokens_per_seq": sorted(set(tokens)),
+            "dense_sequences": int(dense.sum()), "pool_replicas": R,
+        },
+        "selected_kv_gbps": achieved,
+        "selected_kv_hbm_frac": achieved / HBM_PEAK_GBPS,
+        "kernels_us": {"score_topk": sel_s / args.steps * 1e6,
+                       "sparse_decode": attn_avg * 1e6,
+                       "step": ms_per_step * 1e3},
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "kvsp_sparse_decode (attend + merge)",
+            "achieved": achieved,
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": achieved / HBM_PEAK_GBPS,
+            "bytes_per_launch": attn_bytes,
+            "kv_bytes_per_launch": kv_bytes,
+            "per_unit": f"2*D*E = {2 * case.D * E} B per attended token per KV head",
+            "traffic": None,
+        },
+        "scoring": {"bytes_per_launch": scoring_bytes(case, Cs),
+                    "gbps": scoring_bytes(case, Cs) / (sel_s / args.steps) / 1e9},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

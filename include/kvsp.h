@@ -1,0 +1,196 @@
+/*
+ * kvsp — query-aware sparse block decode attention over a paged KV cache,
+ * for AMD Instinct MI355X (CDNA4, gfx950).
+ *
+ * One decode step for a batch of sequences:
+ *   1. every full KV block keeps a mean-key summary per KV head;
+ *   2. a block's relevance to the current query is the sum, over query heads,
+ *      of the inner product between the head's query and its KV head's
+ *      summary;
+ *   3. the top-k blocks are kept (never fewer than a minimum keep floor),
+ *      and runs of adjacent picks form contiguous spans;
+ *   4. attention runs over the kept blocks plus an exact window of recent
+ *      tokens, as split-KV partial softmaxes merged by log-sum-exp;
+ *   5. a sequence whose kept fraction exceeds the dense-fallback threshold γ
+ *      is attended densely instead.
+ *
+ * Sources (titles and sections of the pages this follows; they define no API):
+ *   SparPR news page ("SparPR: Runtime KV-Cache Recovery for Resource-
+ *     Constrained LLM Inference on Consumer Hardware", aimodeling.com),
+ *     section "Three decisions rather than one compression ratio":
+ *     - paragraph "Query-Aware key-block selection" (steps 1-3: summaries
+ *       resident on the GPU, head-summed inner-product score, Top-k);
+ *     - paragraph "Dynamic budget control" (Minimum Keep Floor);
+ *     - paragraph "On-demand local recomputation with cost-aware fallback"
+ *       (adjacent blocks merged into spans; Dense Fallback Threshold γ).
+ *   DKV abstract ("DKV: Anchor + Low-Rank Differential KV-Cache Compression
+ *     for Scalable Long-Context Inference"): top-K block routing, an exact
+ *     recency window, and the flash-style log-sum-exp merge of partial
+ *     attentions (step 4).
+ *   "KV cache offloading" (aiwiki), section "Why the cache leaves the GPU":
+ *     a dense decode step reads every stored key and value (step 5); the
+ *     paged block pool follows the PagedAttention layout it cites.
+ *
+ * Conventions for every entry point
+ *   - Tensor pointers are DEVICE pointers; struct pointers are HOST pointers.
+ *   - Work is enqueued on `stream` (0 = the null stream) and returns without
+ *     waiting for it. No entry point allocates memory, synchronises the host
+ *     or copies device data to the host. The library keeps no pointer after
+ *     returning and holds no mutable global state, so calls on different
+ *     streams may run concurrently (each with its own workspace).
+ *   - The caller owns every buffer; inputs must stay valid until the stream
+ *     work completes.
+ *   - Host-checkable faults return a negative kvsp_status before anything is
+ *     enqueued: a NULL required pointer, a non-positive size, num_q_heads not
+ *     a multiple of num_kv_heads, an unsupported head_dim / block_size /
+ *     dtype, keep_den or gamma_den <= 0, keep_floor == 0 together with
+ *     recent_window == 0, or a workspace smaller than kvsp_workspace_bytes.
+ *     A failed kernel launch returns KVSP_ERR_HIP.
+ *   - Device data is trusted: block-table entries must lie in
+ *     [0, num_phys_blocks), context_lens in [1, max_blocks_per_seq *
+ *     block_size], values finite. Violations are undefined behaviour.
+ *
+ * Memory layouts (row-major, innermost last)
+ *   q            [batch][num_q_heads][head_dim]                 dtype
+ *   k_pool/v_pool[num_phys_blocks][num_kv_heads][block_size][head_dim] dtype
+ *                 (one (block, KV head) tile is contiguous)
+ *   block_table  [batch][max_blocks_per_seq] int32, logical -> physical block
+ *   context_lens [batch] int32, tokens cached per sequence
+ *   summaries    [num_phys_blocks][num_kv_heads][head_dim] float32
+ *   out          [batch][num_q_heads][head_dim] float32
+ *   lse          [batch][num_q_heads] float32 (natural log), may be NULL
+ *   Query head h attends with KV head h / (num_q_heads / num_kv_heads).
+ */
+#ifndef KVSP_H_
+#define KVSP_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  KVSP_OK = 0,
+  KVSP_ERR_INVALID_ARG = -1,
+  KVSP_ERR_UNSUPPORTED = -2,
+  KVSP_ERR_WORKSPACE = -3,
+  KVSP_ERR_HIP = -4
+} kvsp_status;
+
+typedef enum { KVSP_F32 = 0, KVSP_F16 = 1, KVSP_BF16 = 2 } kvsp_dtype;
+
+/* Shape of the batch and the pool (host struct). */
+typedef struct {
+  int32_t batch;              /* B >= 1 */
+  int32_t num_q_heads;        /* Hq, a multiple of num_kv_heads */
+  int32_t num_kv_heads;       /* Hkv >= 1 */
+  int32_t head_dim;           /* D: 64 or 128 */
+  int32_t block_size;         /* P: 16, 32, 64, 128 or 256 tokens */
+  int32_t num_phys_blocks;    /* pool capacity in blocks */
+  int32_t max_blocks_per_seq; /* row stride of block_table, <= 16384 */
+  int32_t dtype;              /* kvsp_dtype of q, K and V */
+} kvsp_layout;
+
+/* Selection parameters (host struct).
+ * For a sequence of L tokens: n = ceil(L / P) blocks; the exact recent window
+ * is tokens [C*P, L) with C = floor(max(0, L - recent_window) / P), i.e. the
+ * last recent_window tokens widened down to a block boundary; the C blocks
+ * before it are the candidates.
+ *   k_req = top_k                                   if top_k > 0
+ *         = ceil(C * keep_num / keep_den)           otherwise (exact integers)
+ *   k     = min(max(k_req, keep_floor), C)
+ *   dense = C > 0 and k * gamma_den > gamma_num * C (kept fraction above γ) */
+typedef struct {
+  int32_t top_k;         /* > 0: absolute k in blocks; 0: use keep_num/keep_den */
+  int32_t keep_num;      /* keep ratio numerator, >= 0 */
+  int32_t keep_den;      /* keep ratio denominator, > 0 */
+  int32_t keep_floor;    /* minimum blocks kept, >= 0 */
+  int32_t recent_window; /* W tokens attended exactly, >= 0 */
+  int32_t gamma_num;     /* dense fallback threshold γ = gamma_num / gamma_den */
+  int32_t gamma_den;     /* > 0; γ >= 1 never falls back */
+} kvsp_select_params;
+
+/* Bytes of device workspace the calls below need for this layout. One
+ * workspace of this size serves every entry point. Its contents need no
+ * initialisation and carry nothing between calls. */
+size_t kvsp_workspace_bytes(const kvsp_layout* layout, const kvsp_select_params* params);
+
+/* Step 1 (SparPR, "Query-Aware key-block selection"): for every sequence b
+ * and every full logical block j < floor(context_lens[b] / P), write
+ *   summaries[block_table[b][j]][g][d] = (1/P) * sum_t K[block_table[b][j]][g][t][d]
+ * for all KV heads g. The sum is exact-rounded: accumulated in double and
+ * rounded once to float32. Entries of other physical blocks are not touched.
+ * Run it when blocks fill, not per decode step. */
+kvsp_status kvsp_build_summaries(const kvsp_layout* layout, const void* k_pool,
+                                 const int32_t* block_table, const int32_t* context_lens,
+                                 float* summaries, hipStream_t stream);
+
+/* Steps 2-3 and the step-5 decision (SparPR, "Query-Aware key-block
+ * selection", "Dynamic budget control", "On-demand local recomputation with
+ * cost-aware fallback"). For every sequence b:
+ *   scores[b][j]  = sum_{h} <q[b][h], summaries[block_table[b][j]][h / G]>, j < C
+ *                   (computed in double from the float32 summaries, stored as
+ *                   float32; the query heads of a group are summed first);
+ *   selected[b][0..k) = the k candidates ranking highest by (score
+ *                   descending, block index ascending), in ascending order;
+ *                   -0.0 ranks equal to +0.0;
+ *   num_selected[b] = k;
+ *   spans[b][s] = {start, end} (logical blocks, half-open) for the maximal
+ *                   runs of consecutive ids in selected ∪ [C, n), ascending;
+ *                   the window run [C, n) comes last and absorbs a selected
+ *                   run ending at C - 1; num_spans[b] of them;
+ *   use_dense[b] = 1 if the kept fraction k / C exceeds γ, else 0.
+ * The selection is always computed, also for sequences that fall back.
+ * Output shapes: scores and selected [B][max_blocks_per_seq], spans
+ * [B][max_blocks_per_seq + 1][2]; scores may be NULL. Entries past the
+ * counts are left as they are. */
+kvsp_status kvsp_score_topk(const kvsp_layout* layout, const kvsp_select_params* params,
+                            const void* q, const float* summaries, const int32_t* block_table,
+                            const int32_t* context_lens, float* scores, int32_t* selected,
+                            int32_t* num_selected, int32_t* spans, int32_t* num_spans,
+                            int32_t* use_dense, void* workspace, size_t workspace_bytes,
+                            hipStream_t stream);
+
+/* Steps 4-5 (DKV abstract: attention over the routed blocks and the exact
+ * recency window, partial softmaxes merged by a flash-style log-sum-exp;
+ * SparPR, "On-demand local recomputation with cost-aware fallback": the
+ * dense path). For every sequence b and query head h, attends over
+ *   tokens of selected[b][0..num_selected[b]) followed by tokens [C*P, L)
+ * or, if use_dense is non-NULL and use_dense[b] != 0, over all tokens
+ * [0, L), with logits scale * <q, K> (scale <= 0 means 1/sqrt(head_dim)),
+ * accumulating in float32, and writes the normalised output and its
+ * log-sum-exp. `selected` holds ascending candidate ids < C as written by
+ * kvsp_score_topk; params supplies recent_window (C depends on it). */
+kvsp_status kvsp_sparse_decode(const kvsp_layout* layout, const kvsp_select_params* params,
+                               const void* q, const void* k_pool, const void* v_pool,
+                               const int32_t* block_table, const int32_t* context_lens,
+                               const int32_t* selected, const int32_t* num_selected,
+                               const int32_t* use_dense, float scale, float* out, float* lse,
+                               void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Step 5 on its own ("KV cache offloading", "Why the cache leaves the GPU":
+ * dense decode reads every key and value): attention of every query head
+ * over all tokens [0, context_lens[b]) of its sequence. Same numerics and
+ * outputs as kvsp_sparse_decode; the workspace size from
+ * kvsp_workspace_bytes (with any params) covers it. */
+kvsp_status kvsp_dense_decode(const kvsp_layout* layout, const void* q, const void* k_pool,
+                              const void* v_pool, const int32_t* block_table,
+                              const int32_t* context_lens, float scale, float* out, float* lse,
+                              void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Static description of a status code (never NULL). */
+const char* kvsp_status_string(kvsp_status status);
+
+/* ABI version of this header (bumped on any incompatible change). */
+#define KVSP_ABI_VERSION 1
+int32_t kvsp_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVSP_H_ */

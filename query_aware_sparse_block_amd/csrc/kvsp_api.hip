@@ -1,0 +1,272 @@
+// C entry points of libkvsp: argument checks, workspace layout and launch
+// geometry. Every check runs on the host before anything is enqueued; no
+// entry point allocates, synchronises or copies to the host.
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include "kvsp.h"
+#include "kvsp_device.h"
+#include "kvsp_internal.h"
+
+namespace kvsp {
+namespace {
+
+constexpr size_t kAlign = 256;
+constexpr int kMaxBlocksPerSeq = 16384;
+constexpr int kMaxSummaryRow = 8192;   // Hkv * D floats (score kernel stages it in LDS as double)
+constexpr int kDecodeTargetItems = 2048;
+constexpr int kDecodeMaxWaves = 8192;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+bool pow2(int x) { return x > 0 && (x & (x - 1)) == 0; }
+
+kvsp_status check_layout(const kvsp_layout* l) {
+  if (l == nullptr) return KVSP_ERR_INVALID_ARG;
+  if (l->batch < 1 || l->num_q_heads < 1 || l->num_kv_heads < 1 || l->num_phys_blocks < 1 ||
+      l->max_blocks_per_seq < 1)
+    return KVSP_ERR_INVALID_ARG;
+  if (l->num_q_heads % l->num_kv_heads != 0) return KVSP_ERR_INVALID_ARG;
+  if (l->head_dim != 64 && l->head_dim != 128) return KVSP_ERR_UNSUPPORTED;
+  if (!pow2(l->block_size) || l->block_size < 16 || l->block_size > 256) return KVSP_ERR_UNSUPPORTED;
+  if (l->dtype != KVSP_F32 && l->dtype != KVSP_F16 && l->dtype != KVSP_BF16) return KVSP_ERR_UNSUPPORTED;
+  if (l->max_blocks_per_seq > kMaxBlocksPerSeq) return KVSP_ERR_UNSUPPORTED;
+  if (l->num_kv_heads * l->head_dim > kMaxSummaryRow) return KVSP_ERR_UNSUPPORTED;
+  return KVSP_OK;
+}
+
+kvsp_status check_params(const kvsp_select_params* p) {
+  if (p == nullptr) return KVSP_ERR_INVALID_ARG;
+  if (p->top_k < 0 || p->keep_num < 0 || p->keep_den <= 0 || p->keep_floor < 0 ||
+      p->recent_window < 0 || p->gamma_num < 0 || p->gamma_den <= 0)
+    return KVSP_ERR_INVALID_ARG;
+  // With neither a floor nor a window the attended set could be empty.
+  if (p->keep_floor == 0 && p->recent_window == 0) return KVSP_ERR_INVALID_ARG;
+  return KVSP_OK;
+}
+
+struct WorkspaceLayout {
+  size_t part_acc, part_ml, scores, total;
+};
+
+struct DecodeGeometry {
+  int gp, n_head_groups, max_chunks, total_items, num_waves;
+};
+
+DecodeGeometry decode_geometry(const kvsp_layout& l) {
+  DecodeGeometry d;
+  const int G = l.num_q_heads / l.num_kv_heads;
+  d.gp = decode_group_pad(G);
+  d.n_head_groups = (G + d.gp - 1) / d.gp;
+  d.max_chunks = decode_max_chunks(l);
+  d.total_items = l.batch * l.num_kv_heads * d.n_head_groups * d.max_chunks;
+  d.num_waves = d.total_items < kDecodeMaxWaves ? d.total_items : kDecodeMaxWaves;
+  return d;
+}
+
+WorkspaceLayout workspace_layout(const kvsp_layout& l) {
+  const DecodeGeometry d = decode_geometry(l);
+  const size_t slots = static_cast<size_t>(d.total_items);
+  WorkspaceLayout w;
+  size_t off = 0;
+  w.part_acc = off;
+  off += align_up(slots * d.gp * l.head_dim * sizeof(float));
+  w.part_ml = off;
+  off += align_up(slots * d.gp * 2 * sizeof(float));
+  w.scores = off;
+  off += align_up(static_cast<size_t>(l.batch) * l.max_blocks_per_seq * sizeof(float));
+  w.total = off;
+  return w;
+}
+
+kvsp_status from_hip(hipError_t e) { return e == hipSuccess ? KVSP_OK : KVSP_ERR_HIP; }
+
+kvsp_status run_decode(const kvsp_layout* layout, const kvsp_select_params* params, bool all_dense,
+                       const void* q, const void* k_pool, const void* v_pool,
+                       const int32_t* block_table, const int32_t* context_lens,
+                       const int32_t* selected, const int32_t* num_selected,
+                       const int32_t* use_dense, float scale, float* out, float* lse,
+                       void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  kvsp_status st = check_layout(layout);
+  if (st != KVSP_OK) return st;
+  if (!all_dense && (st = check_params(params)) != KVSP_OK) return st;
+  if (!q || !k_pool || !v_pool || !block_table || !context_lens || !out)
+    return KVSP_ERR_INVALID_ARG;
+  if (!all_dense && (!selected || !num_selected)) return KVSP_ERR_INVALID_ARG;
+  const kvsp_layout& l = *layout;
+  const WorkspaceLayout wl = workspace_layout(l);
+  if (workspace == nullptr || workspace_bytes < wl.total) return KVSP_ERR_WORKSPACE;
+  const DecodeGeometry g = decode_geometry(l);
+  DecodeArgs a;
+  a.q = q;
+  a.k_pool = k_pool;
+  a.v_pool = v_pool;
+  a.block_table = block_table;
+  a.context_lens = context_lens;
+  a.selected = all_dense ? nullptr : selected;
+  a.num_selected = all_dense ? nullptr : num_selected;
+  a.use_dense = all_dense ? nullptr : use_dense;
+  a.out = out;
+  a.lse = lse;
+  a.part_acc = reinterpret_cast<float*>(static_cast<char*>(workspace) + wl.part_acc);
+  a.part_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) + wl.part_ml);
+  a.B = l.batch;
+  a.Hq = l.num_q_heads;
+  a.Hkv = l.num_kv_heads;
+  a.D = l.head_dim;
+  a.P = l.block_size;
+  a.max_blocks = l.max_blocks_per_seq;
+  a.recent_window = all_dense ? 0 : params->recent_window;
+  a.all_dense = all_dense ? 1 : 0;
+  a.n_head_groups = g.n_head_groups;
+  a.max_chunks = g.max_chunks;
+  a.total_items = g.total_items;
+  const float s = scale > 0.f ? scale : 1.0f / __builtin_sqrtf(static_cast<float>(l.head_dim));
+  a.scale_log2 = s * 1.4426950408889634f;
+  return from_hip(launch_decode(a, l.dtype, g.gp, g.num_waves, stream));
+}
+
+}  // namespace
+
+int decode_group_pad(int G) {
+  if (G <= 1) return 1;
+  if (G <= 2) return 2;
+  if (G <= 4) return 4;
+  if (G <= 8) return 8;
+  return 16;
+}
+
+// Chunks per (sequence, KV head, head group): enough work items to occupy the
+// chip (about kDecodeTargetItems wavefronts), never more than the longest
+// possible context has sub-tiles.
+int decode_max_chunks(const kvsp_layout& l) {
+  const int G = l.num_q_heads / l.num_kv_heads;
+  const int gp = decode_group_pad(G);
+  const int64_t groups = static_cast<int64_t>(l.batch) * l.num_kv_heads * ((G + gp - 1) / gp);
+  const int sub = decode_sub_tokens(l.dtype, l.head_dim);
+  const int64_t max_sub = (static_cast<int64_t>(l.max_blocks_per_seq) * l.block_size + sub - 1) / sub;
+  int64_t mc = 1;
+  while (groups * mc < kDecodeTargetItems && mc < max_sub) mc *= 2;
+  return static_cast<int>(mc);
+}
+
+}  // namespace kvsp
+
+using namespace kvsp;
+
+extern "C" {
+
+int32_t kvsp_abi_version(void) { return KVSP_ABI_VERSION; }
+
+const char* kvsp_status_string(kvsp_status s) {
+  switch (s) {
+    case KVSP_OK: return "ok";
+    case KVSP_ERR_INVALID_ARG: return "invalid argument";
+    case KVSP_ERR_UNSUPPORTED: return "unsupported shape or dtype";
+    case KVSP_ERR_WORKSPACE: return "workspace missing or too small";
+    case KVSP_ERR_HIP: return "HIP launch failed";
+  }
+  return "unknown status";
+}
+
+size_t kvsp_workspace_bytes(const kvsp_layout* layout, const kvsp_select_params* params) {
+  (void)params;
+  if (check_layout(layout) != KVSP_OK) return 0;
+  return workspace_layout(*layout).total;
+}
+
+kvsp_status kvsp_build_summaries(const kvsp_layout* layout, const void* k_pool,
+                                 const int32_t* block_table, const int32_t* context_lens,
+                                 float* summaries, hipStream_t stream) {
+  kvsp_status st = check_layout(layout);
+  if (st != KVSP_OK) return st;
+  if (!k_pool || !block_table || !context_lens || !summaries) return KVSP_ERR_INVALID_ARG;
+  const kvsp_layout& l = *layout;
+  SummaryArgs a{k_pool, block_table, context_lens, summaries, l.batch, l.num_kv_heads,
+                l.block_size, l.max_blocks_per_seq};
+  return from_hip(launch_build_summaries(a, l.dtype, l.head_dim, stream));
+}
+
+kvsp_status kvsp_score_topk(const kvsp_layout* layout, const kvsp_select_params* params,
+                            const void* q, const float* summaries, const int32_t* block_table,
+                            const int32_t* context_lens, float* scores, int32_t* selected,
+                            int32_t* num_selected, int32_t* spans, int32_t* num_spans,
+                            int32_t* use_dense, void* workspace, size_t workspace_bytes,
+                            hipStream_t stream) {
+  kvsp_status st = check_layout(layout);
+  if (st != KVSP_OK) return st;
+  if ((st = check_params(params)) != KVSP_OK) return st;
+  if (!q || !summaries || !block_table || !context_lens || !selected || !num_selected || !spans ||
+      !num_spans || !use_dense)
+    return KVSP_ERR_INVALID_ARG;
+  const kvsp_layout& l = *layout;
+  const kvsp_select_params& p = *params;
+  if (scores == nullptr) {
+    const WorkspaceLayout wl = workspace_layout(l);
+    if (workspace == nullptr || workspace_bytes < wl.total) return KVSP_ERR_WORKSPACE;
+    scores = reinterpret_cast<float*>(static_cast<char*>(workspace) + wl.scores);
+  }
+  ScoreArgs sa;
+  sa.q = q;
+  sa.summaries = summaries;
+  sa.block_table = block_table;
+  sa.context_lens = context_lens;
+  sa.scores = scores;
+  sa.B = l.batch;
+  sa.Hq = l.num_q_heads;
+  sa.Hkv = l.num_kv_heads;
+  sa.D = l.head_dim;
+  sa.P = l.block_size;
+  sa.max_blocks = l.max_blocks_per_seq;
+  int64_t bpw = static_cast<int64_t>(l.batch) * l.max_blocks_per_seq / 16384;
+  sa.blocks_per_wave = static_cast<int>(bpw < 1 ? 1 : (bpw > 16 ? 16 : bpw));
+  sa.top_k = p.top_k;
+  sa.keep_num = p.keep_num;
+  sa.keep_den = p.keep_den;
+  sa.keep_floor = p.keep_floor;
+  sa.recent_window = p.recent_window;
+  sa.gamma_num = p.gamma_num;
+  sa.gamma_den = p.gamma_den;
+  hipError_t e = launch_score(sa, l.dtype, stream);
+  if (e != hipSuccess) return KVSP_ERR_HIP;
+  TopkArgs ta;
+  ta.scores = scores;
+  ta.context_lens = context_lens;
+  ta.selected = selected;
+  ta.num_selected = num_selected;
+  ta.spans = spans;
+  ta.num_spans = num_spans;
+  ta.use_dense = use_dense;
+  ta.B = l.batch;
+  ta.P = l.block_size;
+  ta.max_blocks = l.max_blocks_per_seq;
+  ta.top_k = p.top_k;
+  ta.keep_num = p.keep_num;
+  ta.keep_den = p.keep_den;
+  ta.keep_floor = p.keep_floor;
+  ta.recent_window = p.recent_window;
+  ta.gamma_num = p.gamma_num;
+  ta.gamma_den = p.gamma_den;
+  return from_hip(launch_topk(ta, stream));
+}
+
+kvsp_status kvsp_sparse_decode(const kvsp_layout* layout, const kvsp_select_params* params,
+                               const void* q, const void* k_pool, const void* v_pool,
+                               const int32_t* block_table, const int32_t* context_lens,
+                               const int32_t* selected, const int32_t* num_selected,
+                               const int32_t* use_dense, float scale, float* out, float* lse,
+                               void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return run_decode(layout, params, false, q, k_pool, v_pool, block_table, context_lens, selected,
+                    num_selected, use_dense, scale, out, lse, workspace, workspace_bytes, stream);
+}
+
+kvsp_status kvsp_dense_decode(const kvsp_layout* layout, const void* q, const void* k_pool,
+                              const void* v_pool, const int32_t* block_table,
+                              const int32_t* context_lens, float scale, float* out, float* lse,
+                              void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return run_decode(layout, nullptr, true, q, k_pool, v_pool, block_table, context_lens, nullptr,
+                    nullptr, nullptr, scale, out, lse, workspace, workspace_bytes, stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,81 @@
+// Kernel argument blocks and launchers shared between the kvsp kernels and the
+// C entry points. Internal header: not part of the public C ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "kvsp.h"
+
+namespace kvsp {
+
+struct SummaryArgs {
+  const void* k_pool;
+  const int32_t* block_table;
+  const int32_t* context_lens;
+  float* summaries;
+  int32_t B, Hkv, P, max_blocks;
+};
+
+struct ScoreArgs {
+  const void* q;
+  const float* summaries;
+  const int32_t* block_table;
+  const int32_t* context_lens;
+  float* scores;  // [B][max_blocks]
+  int32_t B, Hq, Hkv, D, P, max_blocks;
+  int32_t blocks_per_wave;
+  int32_t top_k, keep_num, keep_den, keep_floor, recent_window, gamma_num, gamma_den;
+};
+
+struct TopkArgs {
+  const float* scores;
+  const int32_t* context_lens;
+  int32_t* selected;
+  int32_t* num_selected;
+  int32_t* spans;
+  int32_t* num_spans;
+  int32_t* use_dense;
+  int32_t B, P, max_blocks;
+  int32_t top_k, keep_num, keep_den, keep_floor, recent_window, gamma_num, gamma_den;
+};
+
+// Split-KV decode. The attended token sequence of sequence b (selected blocks
+// then the window, or every block when dense) is cut into at most `max_chunks`
+// chunks of whole sub-tiles; each (sequence, KV head, head group, chunk) is one
+// work item for one wavefront. Partials live at slot
+//   ((b * Hkv + g) * n_head_groups + hg) * max_chunks + c.
+struct DecodeArgs {
+  const void* q;
+  const void* k_pool;
+  const void* v_pool;
+  const int32_t* block_table;
+  const int32_t* context_lens;
+  const int32_t* selected;      // NULL when every sequence is dense
+  const int32_t* num_selected;  // NULL when every sequence is dense
+  const int32_t* use_dense;     // may be NULL
+  float* out;
+  float* lse;                   // may be NULL
+  float* part_acc;              // [slots][GP][D]
+  float* part_ml;               // [slots][GP][2]
+  int32_t B, Hq, Hkv, D, P, max_blocks;
+  int32_t recent_window;
+  int32_t all_dense;            // 1: ignore selection, attend every token
+  int32_t n_head_groups;        // ceil(G / GP)
+  int32_t max_chunks;
+  int32_t total_items;          // B * Hkv * n_head_groups * max_chunks
+  float scale_log2;             // softmax scale * log2(e)
+};
+
+hipError_t launch_build_summaries(const SummaryArgs& a, int dtype, int D, hipStream_t stream);
+hipError_t launch_score(const ScoreArgs& a, int dtype, hipStream_t stream);
+hipError_t launch_topk(const TopkArgs& a, hipStream_t stream);
+hipError_t launch_decode(const DecodeArgs& a, int dtype, int group_pad, int num_waves,
+                         hipStream_t stream);
+
+// Host-side sizing shared by the entry points and kvsp_workspace_bytes.
+int decode_group_pad(int G);        // GP: heads per work item (1, 2, 4, 8 or 16)
+int decode_max_chunks(const kvsp_layout& l);
+int decode_sub_tokens(int dtype, int D);
+
+}  // namespace kvsp

@@ -1,0 +1,73 @@
+// Step 1: per-block mean-key summaries (SparPR news page, "Three decisions
+// rather than one compression ratio", paragraph "Query-Aware key-block
+// selection": every historical block keeps a compact precomputed summary, the
+// mean key vector, resident on the GPU).
+//
+// One workgroup per (sequence, logical block); its four waves split the KV
+// heads. A (block, KV head) tile is P rows of D elements, contiguous in the
+// pool, so a wave streams it with 16-byte loads: LPR lanes cover one row and
+// the wave covers 64 / LPR rows per load. Each lane accumulates its slice of
+// the row in double, the row groups are folded with lane shuffles, and the
+// mean is rounded once to float32. HBM-bound: P*D*E bytes read and D*4 bytes
+// written per (block, KV head).
+
+#include "kvsp_device.h"
+#include "kvsp_internal.h"
+
+namespace kvsp {
+
+template <typename T, int D>
+__global__ __launch_bounds__(256) void build_summaries_kernel(SummaryArgs a) {
+  constexpr int E = T::kBytes;
+  constexpr int EPV = T::kPerVec;
+  constexpr int LPR = D * E / 16;  // lanes per row
+  constexpr int RPL = kWave / LPR; // rows per wave-load
+  const int b = blockIdx.y;
+  const int j = blockIdx.x;
+  const int L = a.context_lens[b];
+  if (j >= L / a.P) return;  // only full blocks have a summary
+  const int64_t phys = a.block_table[static_cast<int64_t>(b) * a.max_blocks + j];
+  const int lane = threadIdx.x % kWave;
+  const int wave = threadIdx.x / kWave;
+  const int col = (lane % LPR) * EPV;
+  const int row0 = lane / LPR;
+  const char* pool = static_cast<const char*>(a.k_pool);
+  for (int g = wave; g < a.Hkv; g += 4) {
+    const char* tile = pool + ((phys * a.Hkv + g) * a.P) * static_cast<int64_t>(D) * E;
+    double acc[EPV];
+#pragma unroll
+    for (int e = 0; e < EPV; ++e) acc[e] = 0.0;
+    for (int t = row0; t < a.P; t += RPL) {
+      float v[EPV];
+      T::widen(load16(tile + (static_cast<int64_t>(t) * D + col) * E), v);
+#pragma unroll
+      for (int e = 0; e < EPV; ++e) acc[e] += static_cast<double>(v[e]);
+    }
+#pragma unroll
+    for (int m = LPR; m < kWave; m <<= 1) {
+#pragma unroll
+      for (int e = 0; e < EPV; ++e) acc[e] += lane_xor(acc[e], m);
+    }
+    if (lane < LPR) {
+      float* dst = a.summaries + (phys * a.Hkv + g) * D + col;
+      const double inv_p = 1.0 / static_cast<double>(a.P);  // P is a power of two: exact
+#pragma unroll
+      for (int e = 0; e < EPV; ++e) dst[e] = static_cast<float>(acc[e] * inv_p);
+    }
+  }
+}
+
+template <typename T, int D>
+static hipError_t launch_summaries_t(const SummaryArgs& a, hipStream_t stream) {
+  dim3 grid(a.max_blocks, a.B);
+  hipLaunchKernelGGL((build_summaries_kernel<T, D>), grid, dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_build_summaries(const SummaryArgs& a, int dtype, int D, hipStream_t stream) {
+  if (dtype == KVSP_F32) return D == 64 ? launch_summaries_t<F32, 64>(a, stream) : launch_summaries_t<F32, 128>(a, stream);
+  if (dtype == KVSP_F16) return D == 64 ? launch_summaries_t<F16, 64>(a, stream) : launch_summaries_t<F16, 128>(a, stream);
+  return D == 64 ? launch_summaries_t<BF16, 64>(a, stream) : launch_summaries_t<BF16, 128>(a, stream);
+}
+
+}  // namespace kvsp

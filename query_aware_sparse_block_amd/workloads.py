@@ -19,6 +19,7 @@ patterns as uint16, rounded to nearest-even from float32 draws.
 from __future__ import annotations
 
 import os
+import threading
 from concurrent.futures import ThreadPoolExecutor
 from dataclasses import dataclass, field
 from fractions import Fraction
@@ -106,24 +107,46 @@ class Case:
 _CHUNK_BLOCKS_TARGET = 1 << 22   # elements per generation chunk
 
 
+def _encode_into(x: np.ndarray, dtype: str, dst: np.ndarray, tmp: np.ndarray | None):
+    """Round float32 `x` into `dst` (same shape) without large temporaries."""
+    if dtype == "fp32":
+        dst[...] = x
+    elif dtype == "fp16":
+        dst.view(np.float16)[...] = x
+    else:
+        u = x.view(np.uint32)
+        np.right_shift(u, np.uint32(16), out=tmp)
+        np.bitwise_and(tmp, np.uint32(1), out=tmp)
+        np.add(tmp, u, out=tmp)
+        np.add(tmp, np.uint32(0x7FFF), out=tmp)
+        np.right_shift(tmp, np.uint32(16), out=tmp)
+        dst[...] = tmp
+
+
 def _gen_pool(seed, stream, num_phys, Hkv, P, D, dtype, transform=None, workers=None):
     """Draw a [num_phys][Hkv][P][D] pool of N(0,1) values in independent
     chunks of whole physical blocks (chunk i uses its own PCG64 stream), apply
-    `transform(first_block, f32_chunk)` in float32 and round to `dtype`."""
+    `transform(first_block, f32_chunk)` in float32 and round to `dtype`.
+    The result does not depend on `workers`."""
     per_block = Hkv * P * D
     blocks_per_chunk = max(1, _CHUNK_BLOCKS_TARGET // per_block)
     n_chunks = (num_phys + blocks_per_chunk - 1) // blocks_per_chunk
     out_dtype = np.float32 if dtype == "fp32" else np.uint16
     out = np.empty((num_phys, Hkv, P, D), out_dtype)
+    local = threading.local()
 
     def work(ci):
         b0 = ci * blocks_per_chunk
         b1 = min(num_phys, b0 + blocks_per_chunk)
-        x = np.empty((b1 - b0, Hkv, P, D), np.float32)
+        nb = b1 - b0
+        if getattr(local, "x", None) is None:
+            local.x = np.empty((blocks_per_chunk, Hkv, P, D), np.float32)
+            local.t = np.empty((blocks_per_chunk, Hkv, P, D), np.uint32)
+        x, t = local.x[:nb], local.t[:nb]
         _rng(seed, stream, ci).standard_normal(out=x.reshape(-1), dtype=np.float32)
         if transform is not None:
             transform(b0, x)
-        out[b0:b1] = encode(x, dtype)
+        _encode_into(x, dtype, out[b0:b1], t)
 
     if workers is None:
         workers = min(16, os.cpu_count() or 1)
@@ -137,10 +160,11 @@ def _gen_pool(seed, stream, num_phys, Hkv, P, D, dtype, transform=None, workers=
 
 
 def _block_table(B, max_blocks, num_phys, shuffle, rng):
+    if num_phys < B * max_blocks:
+        raise ValueError(f"pool of {num_phys} blocks cannot hold {B} x {max_blocks} blocks")
     if shuffle:
         perm = rng.permutation(num_phys)[: B * max_blocks].astype(np.int32)
         return perm.reshape(B, max_blocks).copy()
-    assert num_phys >= B * max_blocks
     return np.arange(B * max_blocks, dtype=np.int32).reshape(B, max_blocks)
 
 

@@ -1,0 +1,147 @@
+"""GPU parity: the HIP path through the C ABI against the oracle on the same
+seeded inputs, for every workload family (scaled so the oracle finishes in
+seconds where the full size would not), every dtype and head-dim variant, and
+the edge cases: ragged contexts, contexts inside the window, 100 % keep, the
+dense fallback, mixed dense/sparse batches, partial head groups and shuffled
+physical pools. Full-size runs live in test_gpu_fullsize.py."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from query_aware_sparse_block_amd import workloads as wl
+from tests import gpu_helpers as H
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("variant", ["k8", "k2", "k64", "gamma", "shuffled"])
+def test_tiny_fp32(variant):
+    H.full_parity(wl.c1(variant))
+
+
+@pytest.mark.parametrize("L", [1024, 2048])
+@pytest.mark.parametrize("keep", ["1/2", "1/10"])
+def test_opt_like_fp16_scaled(L, keep):
+    gpu, r_or = H.full_parity(wl.c2(L=L, keep=keep, B=2, H=8))
+    for b, needles in enumerate(wl.c2(L=L, keep=keep, B=2, H=8).meta["needles"]):
+        k = int(gpu["num_selected"][b])
+        sel = set(gpu["selected"][b, :k].tolist())
+        assert set(needles) <= sel or sel <= set(needles)
+
+
+@pytest.mark.parametrize("keep", ["1/32", "1/8"])
+def test_minicpm_like_bf16_scaled(keep):
+    H.full_parity(wl.c3(keep=keep, L=16384))
+
+
+@pytest.mark.parametrize("L", [4096, 8192])
+def test_qwen_like_bf16(L):
+    case = wl.c4(L=L)
+    gpu, _ = H.full_parity(case)
+    k = int(gpu["num_selected"][0])
+    assert case.meta["buried"][0] in gpu["selected"][0, :k].tolist()
+
+
+@pytest.mark.parametrize("keep", ["1/32", "7/10"])
+def test_serving_bf16_scaled(keep):
+    case = wl.c5(keep=keep, B=8, L=4096)
+    gpu, r_or = H.full_parity(case)
+    assert (gpu["use_dense"] == (1 if keep == "7/10" else 0)).all()
+
+
+@pytest.mark.parametrize("dtype,D", [("fp32", 128), ("fp16", 64), ("bf16", 64), ("fp32", 64)])
+def test_dtype_and_head_dim_variants(dtype, D):
+    case = wl.make_case(f"var-{dtype}-D{D}", seed=61, B=3, Hq=8, Hkv=2, D=D, P=32, dtype=dtype,
+                        ctx_lens=[1000, 517, 64], shuffle=True, num_phys=100, top_k=5,
+                        keep_floor=2, recent_window=100)
+    H.full_parity(case)
+
+
+def test_ragged_mixed_dense_and_partial_groups():
+    # G = 3 (padded to 4), P = 16; short sequences fall back to dense (gamma 1/2)
+    case = wl.make_case("ragged", seed=62, B=6, Hq=6, Hkv=2, D=128, P=16, dtype="fp16",
+                        ctx_lens=[1, 15, 200, 1000, 777, 48], shuffle=True, num_phys=400,
+                        top_k=3, keep_floor=1, recent_window=32, gamma_num=1, gamma_den=2)
+    gpu, r_or = H.full_parity(case)
+    assert set(r_or["plan"][:, 4].tolist()) == {0, 1}   # both paths in one batch
+
+
+def test_large_group_over_sixteen_heads():
+    # G = 24 -> two head groups of 16
+    case = wl.make_case("g24", seed=63, B=2, Hq=48, Hkv=2, D=128, P=64, dtype="bf16",
+                        ctx_lens=[2048, 1500], keep_num=1, keep_den=4, recent_window=64)
+    H.full_parity(case)
+
+
+def test_full_keep_equals_dense_api():
+    case = wl.make_case("full-keep", seed=64, B=3, Hq=8, Hkv=4, D=128, P=64, dtype="bf16",
+                        ctx_lens=[3000, 640, 129], shuffle=True, num_phys=150, top_k=10 ** 6,
+                        keep_floor=1, recent_window=64)
+    sparse, _ = H.full_parity(case)
+    dense, _, _ = H.run_gpu(case, dense_api=True)
+    np.testing.assert_allclose(sparse["out"], dense["out"], rtol=0, atol=2e-6)
+    # and the dense entry point against the oracle's textbook dense attention
+    summ = H.oracle_summaries(case)
+    r = oracle.decode_step(case.dtype, case.q, case.k_pool, case.v_pool, case.block_table,
+                           case.ctx_lens, summ, Hkv=case.Hkv, P=case.P, top_k=10 ** 6,
+                           recent_window=64)
+    assert np.max(np.abs(dense["out"] - r["out"])) <= 2e-3
+
+
+def test_context_inside_window_and_single_token():
+    case = wl.make_case("tiny-ctx", seed=65, B=4, Hq=4, Hkv=4, D=64, P=16, dtype="bf16",
+                        ctx_lens=[1, 5, 16, 31], top_k=2, keep_floor=1, recent_window=32)
+    gpu, r_or = H.full_parity(case)
+    assert (r_or["plan"][:, 1] == 0).all()
+    # one cached token: the output is that token's value
+    v0 = wl.decode_f32(case.v_pool[case.block_table[0, 0], :, 0], "bf16")
+    np.testing.assert_allclose(gpu["out"][0], v0, atol=1e-6)
+
+
+def test_dense_decode_api_matches_oracle():
+    case = wl.c5(keep="1/32", B=4, L=2048)
+    H.note("[dense api] c5 B=4 L=2048")
+    gpu, _, _ = H.run_gpu(case, dense_api=True)
+    summ = H.oracle_summaries(case)
+    r = oracle.decode_step(case.dtype, case.q, case.k_pool, case.v_pool, case.block_table,
+                           case.ctx_lens, summ, Hkv=case.Hkv, P=case.P, top_k=10 ** 6,
+                           recent_window=0)
+    assert np.max(np.abs(gpu["out"] - r["out"])) <= 2e-3
+    assert np.max(np.abs(gpu["lse"] - r["lse"])) <= 1e-4
+
+
+def test_deterministic_and_layout_invariant():
+    case = wl.c5(keep="1/32", B=4, L=2048)
+    H.note("[determinism] c5 B=4 L=2048")
+    a, _, _ = H.run_gpu(case)
+    b, _, _ = H.run_gpu(case)
+    for key in ("selected", "spans", "out", "lse", "scores"):
+        assert np.array_equal(a[key], b[key]), key
+    # same logical cache through an identity table
+    ident = wl.Case(**{**case.__dict__,
+                       "k_pool": np.ascontiguousarray(case.k_pool[case.block_table.reshape(-1)]),
+                       "v_pool": np.ascontiguousarray(case.v_pool[case.block_table.reshape(-1)]),
+                       "block_table": np.arange(case.block_table.size, dtype=np.int32)
+                       .reshape(case.block_table.shape)})
+    c, _, _ = H.run_gpu(ident)
+    for key in ("selected", "spans", "out", "lse", "scores"):
+        assert np.array_equal(a[key], c[key]), key
+
+
+def test_scale_argument():
+    case = wl.c1("k8")
+    H.note("[scale] c1")
+    from query_aware_sparse_block_amd import device as dev
+    dc = dev.upload(case)
+    buf = dev.alloc_buffers(dc)
+    dev.build_summaries(dc, buf)
+    dev.score_topk(dc, buf)
+    dev.sparse_decode(dc, buf, scale=0.3)
+    torch.cuda.synchronize()
+    sel = buf.selected.cpu().numpy()[0, :8]
+    ref, _ = H.oracle_attention_on(case, 0, sel, 0, heads=[0, 5], scale=0.3)
+    out = buf.out.cpu().numpy()
+    for h in (0, 5):
+        assert np.max(np.abs(out[0, h] - ref[h])) <= 1e-5
