@@ -115,8 +115,12 @@ typedef struct {
 } kvsp_select_params;
 
 /* Bytes of device workspace the calls below need for this layout. One
- * workspace of this size serves every entry point. Its contents need no
- * initialisation and carry nothing between calls. */
+ * workspace of this size serves every entry point of one stream at a time.
+ * It holds per-(sequence, KV head) completion counters for the split-KV
+ * merge: zero-fill it once before its first use (any zero fill, e.g. a
+ * zero-initialised allocation); every call that returns KVSP_OK leaves the
+ * counters at zero again, so no per-call clearing is needed. Calls that share
+ * one workspace must not overlap in time. */
 size_t kvsp_workspace_bytes(const kvsp_layout* layout, const kvsp_select_params* params);
 
 /* Step 1 (SparPR, "Query-Aware key-block selection"): for every sequence b

@@ -15,8 +15,16 @@ namespace {
 constexpr size_t kAlign = 256;
 constexpr int kMaxBlocksPerSeq = 16384;
 constexpr int kMaxSummaryRow = 8192;   // Hkv * D floats (score kernel stages it in LDS as double)
-constexpr int kDecodeTargetItems = 2048;
-constexpr int kDecodeMaxWaves = 8192;
+// Workgroup items per decode launch (about one per resident workgroup) and the
+// cap on launched workgroups; items beyond it are taken in grid-stride order.
+#ifndef KVSP_DECODE_TARGET_ITEMS
+#define KVSP_DECODE_TARGET_ITEMS 256
+#endif
+#ifndef KVSP_DECODE_MAX_WORKGROUPS
+#define KVSP_DECODE_MAX_WORKGROUPS 2048
+#endif
+constexpr int kDecodeTargetItems = KVSP_DECODE_TARGET_ITEMS;
+constexpr int kDecodeMaxWorkgroups = KVSP_DECODE_MAX_WORKGROUPS;
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
@@ -47,11 +55,11 @@ kvsp_status check_params(const kvsp_select_params* p) {
 }
 
 struct WorkspaceLayout {
-  size_t part_acc, part_ml, scores, total;
+  size_t counters, part_acc, part_ml, scores, total;
 };
 
 struct DecodeGeometry {
-  int gp, n_head_groups, max_chunks, total_items, num_waves;
+  int gp, n_head_groups, max_chunks, total_items, num_wgs;
 };
 
 DecodeGeometry decode_geometry(const kvsp_layout& l) {
@@ -61,7 +69,7 @@ DecodeGeometry decode_geometry(const kvsp_layout& l) {
   d.n_head_groups = (G + d.gp - 1) / d.gp;
   d.max_chunks = decode_max_chunks(l);
   d.total_items = l.batch * l.num_kv_heads * d.n_head_groups * d.max_chunks;
-  d.num_waves = d.total_items < kDecodeMaxWaves ? d.total_items : kDecodeMaxWaves;
+  d.num_wgs = d.total_items < kDecodeMaxWorkgroups ? d.total_items : kDecodeMaxWorkgroups;
   return d;
 }
 
@@ -70,6 +78,8 @@ WorkspaceLayout workspace_layout(const kvsp_layout& l) {
   const size_t slots = static_cast<size_t>(d.total_items);
   WorkspaceLayout w;
   size_t off = 0;
+  w.counters = off;
+  off += align_up(static_cast<size_t>(l.batch) * l.num_kv_heads * d.n_head_groups * sizeof(int32_t));
   w.part_acc = off;
   off += align_up(slots * d.gp * l.head_dim * sizeof(float));
   w.part_ml = off;
@@ -111,6 +121,7 @@ kvsp_status run_decode(const kvsp_layout* layout, const kvsp_select_params* para
   a.lse = lse;
   a.part_acc = reinterpret_cast<float*>(static_cast<char*>(workspace) + wl.part_acc);
   a.part_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) + wl.part_ml);
+  a.counters = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + wl.counters);
   a.B = l.batch;
   a.Hq = l.num_q_heads;
   a.Hkv = l.num_kv_heads;
@@ -124,7 +135,7 @@ kvsp_status run_decode(const kvsp_layout* layout, const kvsp_select_params* para
   a.total_items = g.total_items;
   const float s = scale > 0.f ? scale : 1.0f / __builtin_sqrtf(static_cast<float>(l.head_dim));
   a.scale_log2 = s * 1.4426950408889634f;
-  return from_hip(launch_decode(a, l.dtype, g.gp, g.num_waves, stream));
+  return from_hip(launch_decode(a, l.dtype, g.gp, g.num_wgs, stream));
 }
 
 }  // namespace
@@ -137,15 +148,15 @@ int decode_group_pad(int G) {
   return 16;
 }
 
-// Chunks per (sequence, KV head, head group): enough work items to occupy the
-// chip (about kDecodeTargetItems wavefronts), never more than the longest
-// possible context has sub-tiles.
+// Chunks per (sequence, KV head, head group): enough workgroup items to
+// occupy the chip (about kDecodeTargetItems), never more than the longest
+// possible context has chunk quanta.
 int decode_max_chunks(const kvsp_layout& l) {
   const int G = l.num_q_heads / l.num_kv_heads;
   const int gp = decode_group_pad(G);
   const int64_t groups = static_cast<int64_t>(l.batch) * l.num_kv_heads * ((G + gp - 1) / gp);
-  const int sub = decode_sub_tokens(l.dtype, l.head_dim);
-  const int64_t max_sub = (static_cast<int64_t>(l.max_blocks_per_seq) * l.block_size + sub - 1) / sub;
+  const int quantum = decode_chunk_quantum(l.dtype, l.head_dim);
+  const int64_t max_sub = (static_cast<int64_t>(l.max_blocks_per_seq) * l.block_size + quantum - 1) / quantum;
   int64_t mc = 1;
   while (groups * mc < kDecodeTargetItems && mc < max_sub) mc *= 2;
   return static_cast<int>(mc);

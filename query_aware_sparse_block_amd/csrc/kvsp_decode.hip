@@ -9,26 +9,41 @@
 // sequence: the tokens of selected[b][0..k) followed by the window [C*P, L)
 // (or all of [0, L) when dense). Attended token i lives in attended block
 // i / P at offset i % P, because every attended block but the last is full.
-// That sequence is cut into at most max_chunks chunks of whole sub-tiles
-// (SUB tokens); one wavefront handles one (sequence, KV head, head group,
-// chunk) work item and loops over its sub-tiles with an online softmax.
-// Waves walk the work items with a grid stride, so any mix of sparse and
+// That sequence is cut into at most max_chunks chunks of whole sub-tiles.
+// One workgroup handles one (sequence, KV head, head group, chunk) item: its
+// four wavefronts take the chunk's sub-tiles (SUB tokens, 8 KiB of keys) in
+// turn, each with its own online softmax, and merge through LDS at the end.
+// Workgroups walk the items with a grid stride, so any mix of sparse and
 // dense sequences fills the chip.
 //
-// Per sub-tile (SUB tokens, 8 KiB of keys):
+// Per sub-tile and wavefront:
 //   K: 16-byte loads laid out as the A operand of v_mfma_f32_16x16x32_{bf16,
 //      f16} (16x16x4 f32 for fp32 caches): row = token, contraction = head
-//      dim. The B operand is the group's queries (up to 16 heads), so the
-//      logits of all heads that share this KV head come from one read of K.
-//   softmax: base-2 online softmax per head, probabilities staged in LDS.
+//      dim. The B operand holds the group's queries (up to 16 heads), so the
+//      logits of all heads that share a KV head come from one read of K.
+//   softmax: base-2 online softmax per head; probabilities staged in LDS.
 //   V: 16-byte row-major loads (LPR lanes per row); each lane accumulates
 //      acc[head][its EPV channels] += p * v in float32.
+// A chunk's result is written as a partial (m, l, acc). The last workgroup to
+// finish a (sequence, KV head, head group) — counted with one atomic per
+// group in the workspace, which that workgroup resets to zero — merges the
+// partials by log-sum-exp and writes the output. A sequence that fits in one
+// chunk writes its output directly.
 // HBM-bound: 2 * D * E bytes per attended token per KV head.
 
 #include "kvsp_device.h"
 #include "kvsp_internal.h"
 
 namespace kvsp {
+
+// Bytes of keys a wavefront loads per sub-tile (the same again for values).
+#ifndef KVSP_SUB_TILE_BYTES
+#define KVSP_SUB_TILE_BYTES 4096
+#endif
+// 1: each wavefront loads sub-tile i+1 while it computes sub-tile i.
+#ifndef KVSP_PIPELINE
+#define KVSP_PIPELINE 0
+#endif
 
 template <typename T, int D>
 struct DecodeShape {
@@ -37,18 +52,22 @@ struct DecodeShape {
   static constexpr int LPR = D * E / 16;      // lanes per K/V row
   static constexpr int RPL = kWave / LPR;     // rows per wave-wide load
   static constexpr int NRG = RPL;             // row groups in a wave
-  static constexpr int SUB = 8192 / (D * E);  // tokens per sub-tile
+  static constexpr int SUB = KVSP_SUB_TILE_BYTES / (D * E) < 16 ? 16 : KVSP_SUB_TILE_BYTES / (D * E);
   static constexpr int TILES = SUB / 16;      // 16-token MFMA tiles per sub-tile
   static constexpr int KLD = D * E / 64;      // K loads per lane per tile
   static constexpr int VLD = SUB / RPL;       // V loads per lane per sub-tile
   static constexpr int PROW = 16;             // floats per token row of p in LDS
 };
 
+constexpr int kDecodeWaves = 4;
+
 struct SeqWork {
   int32_t L, Cw, k, dense, A, T, CT, nc;
 };
 
-__device__ __forceinline__ SeqWork seq_work(const DecodeArgs& a, int b, int sub) {
+// Chunking of sequence b's attended tokens: chunks are whole multiples of
+// `quantum` tokens (one sub-tile per wavefront), at most max_chunks of them.
+__device__ __forceinline__ SeqWork seq_work(const DecodeArgs& a, int b, int quantum) {
   SeqWork w;
   w.L = a.context_lens[b];
   const int n = (w.L + a.P - 1) / a.P;
@@ -58,11 +77,11 @@ __device__ __forceinline__ SeqWork seq_work(const DecodeArgs& a, int b, int sub)
   w.A = w.dense ? n : w.k + (n - w.Cw);
   w.T = w.dense ? w.L : w.k * a.P + (w.L - w.Cw * a.P);
   if (w.T > 0) {
-    const int per = (w.T + sub * a.max_chunks - 1) / (sub * a.max_chunks);
-    w.CT = per * sub;
+    const int per = (w.T + quantum * a.max_chunks - 1) / (quantum * a.max_chunks);
+    w.CT = per * quantum;
     w.nc = (w.T + w.CT - 1) / w.CT;
   } else {
-    w.CT = sub;
+    w.CT = quantum;
     w.nc = 1;
   }
   return w;
@@ -128,27 +147,32 @@ template <typename T, int D, int GP>
 __global__ __launch_bounds__(256) void attend_kernel(DecodeArgs a) {
   using S = DecodeShape<T, D>;
   constexpr int E = S::E;
-  __shared__ float p_lds[4][S::SUB * S::PROW];
-  __shared__ float alpha_lds[4][16];
-  __shared__ float ml_lds[4][2][16];
+  constexpr int QUANTUM = kDecodeWaves * S::SUB;
+  __shared__ float p_lds[kDecodeWaves][S::SUB * S::PROW];
+  __shared__ float alpha_lds[kDecodeWaves][16];
+  __shared__ float ml_lds[kDecodeWaves][2][16];
+  __shared__ float xacc[kDecodeWaves - 1][GP * D];
+  __shared__ int last_flag;
 
   const int lane = threadIdx.x % kWave;
-  const int wave = threadIdx.x / kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int hl = lane % 16;  // head within the group (MFMA column)
+  const int rg = lane / S::LPR;
+  const int col = (lane % S::LPR) * S::EPV;
   const int G = a.Hq / a.Hkv;
   const float NEG_INF = -__builtin_huge_valf();
-  const int nwaves = gridDim.x * 4;
 
-  for (int item = blockIdx.x * 4 + wave; item < a.total_items; item += nwaves) {
+  for (int item = blockIdx.x; item < a.total_items; item += gridDim.x) {
     int rest = item;
     const int c = rest % a.max_chunks;
     rest /= a.max_chunks;
+    const int grp = rest;  // (b * Hkv + g) * n_head_groups + hg
     const int hg = rest % a.n_head_groups;
     rest /= a.n_head_groups;
     const int g = rest % a.Hkv;
     const int b = rest / a.Hkv;
-    const SeqWork w = seq_work(a, b, S::SUB);
-    if (c >= w.nc) continue;
+    const SeqWork w = seq_work(a, b, QUANTUM);
+    if (c >= w.nc) continue;  // uniform over the workgroup
     const int start = c * w.CT;
     const int end = min(w.T, start + w.CT);
 
@@ -176,7 +200,8 @@ __global__ __launch_bounds__(256) void attend_kernel(DecodeArgs a) {
       for (int e = 0; e < S::EPV; ++e) acc[h][e] = 0.f;
 
     // Physical ids of 64 consecutive attended blocks, one per lane.
-    int gbase = start / a.P;
+    const int first_tok = start + wave * S::SUB;
+    int gbase = min(first_tok, max(end - 1, 0)) / a.P;
     int phys_v = 0;
     {
       const int ab = gbase + lane;
@@ -185,59 +210,66 @@ __global__ __launch_bounds__(256) void attend_kernel(DecodeArgs a) {
 
     const char* kbase = static_cast<const char*>(a.k_pool);
     const char* vbase = static_cast<const char*>(a.v_pool);
-    for (int i0 = start; i0 < end; i0 += S::SUB) {
+
+    struct SubTile {
+      uint4 kv[S::TILES][S::KLD];
+      uint4 vv[S::VLD];
+    };
+
+    // Per-lane byte offsets inside a 16-row tile (loop invariant): K in the MFMA
+    // A-operand layout (row hl, 16 bytes per lane group, 64 bytes per step),
+    // V row-major (row group rg, channels col..col+EPV).
+    const uint32_t k_lane_off = static_cast<uint32_t>(hl * D * E + (lane / 16) * 16);
+    const uint32_t v_lane_off = static_cast<uint32_t>((rg * D + col) * E);
+
+    // Enqueue the K and V loads of the sub-tile starting at attended token i0.
+    // Tile bases are wave-uniform, so every load is base + lane offset.
+    auto issue = [&](int i0, SubTile& st) {
       const int a_last = (min(i0 + S::SUB, end) - 1) / a.P;
       if (a_last - gbase >= kWave) {
         gbase = i0 / a.P;
         const int ab = gbase + lane;
         phys_v = ab < w.A ? attended_phys(a, b, w, ab) : 0;
       }
-      int64_t tile_row0[S::TILES];  // element index of the tile's first row
-      bool tile_ok[S::TILES];
+      int64_t tile_byte0[S::TILES];  // byte offset of the tile's first row in the pool
 #pragma unroll
       for (int t = 0; t < S::TILES; ++t) {
         const int ti = i0 + 16 * t;
-        tile_ok[t] = ti < end;
         const int ab = min(ti, end - 1) / a.P;
         const int64_t phys = __builtin_amdgcn_readlane(phys_v, ab - gbase);
-        tile_row0[t] = ((phys * a.Hkv + g) * a.P + (ti % a.P)) * static_cast<int64_t>(D);
+        tile_byte0[t] = ((phys * a.Hkv + g) * a.P + (ti % a.P)) * static_cast<int64_t>(D * E);
       }
-
-      uint4 kv[S::TILES][S::KLD];
+      // Rows past `end` still lie inside a valid physical block (tiles are
+      // 16-row aligned, P >= 16): they are loaded unconditionally, their
+      // logits are masked to -inf and their values zeroed before use.
 #pragma unroll
       for (int t = 0; t < S::TILES; ++t) {
-        const int row = i0 + 16 * t + hl;
-        const bool ok = tile_ok[t] && row < end;
+        const char* tk = kbase + tile_byte0[t];
 #pragma unroll
-        for (int s = 0; s < S::KLD; ++s) {
-          kv[t][s] = ok ? load16(kbase + (tile_row0[t] + static_cast<int64_t>(hl) * D +
-                                          k_elem_offset<T>(lane, s)) * E)
-                        : make_uint4(0, 0, 0, 0);
-        }
+        for (int s = 0; s < S::KLD; ++s) st.kv[t][s] = load16(tk + k_lane_off + 64 * s);
       }
-      uint4 vv[S::VLD];
 #pragma unroll
       for (int r = 0; r < S::VLD; ++r) {
-        const int rr = r * S::RPL + lane / S::LPR;  // row within the sub-tile
         const int t = (r * S::RPL) / 16;
-        const bool ok = i0 + rr < end;
-        vv[r] = ok ? load16(vbase + (tile_row0[t] + static_cast<int64_t>(rr - 16 * t) * D +
-                                     (lane % S::LPR) * S::EPV) * E)
-                   : make_uint4(0, 0, 0, 0);
+        const char* tv = vbase + tile_byte0[t] + (r * S::RPL - 16 * t) * D * E;
+        st.vv[r] = load16(tv + v_lane_off);
       }
+    };
 
-      // Logits (base 2) of the sub-tile: lane holds head hl, tokens 4*(lane/16)+i.
+    // Online-softmax update with the sub-tile starting at attended token i0.
+    auto consume = [&](int i0, const SubTile& st) {
+      // Logits (base 2): lane holds head hl, tokens 16*t + 4*(lane/16) + i.
       float s2[S::TILES][4];
       float mloc = NEG_INF;
 #pragma unroll
       for (int t = 0; t < S::TILES; ++t) {
-        floatx4 st = {0.f, 0.f, 0.f, 0.f};
+        floatx4 sc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int s = 0; s < S::KLD; ++s) st = QkMfma<T>::step(kv[t][s], qop[s], st);
+        for (int s = 0; s < S::KLD; ++s) sc = QkMfma<T>::step(st.kv[t][s], qop[s], sc);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int tok = i0 + 16 * t + 4 * (lane / 16) + i;
-          s2[t][i] = tok < end ? st[i] * a.scale_log2 : NEG_INF;
+          s2[t][i] = tok < end ? sc[i] * a.scale_log2 : NEG_INF;
           mloc = fmaxf(mloc, s2[t][i]);
         }
       }
@@ -269,11 +301,16 @@ __global__ __launch_bounds__(256) void attend_kernel(DecodeArgs a) {
 #pragma unroll
         for (int e = 0; e < S::EPV; ++e) acc[h][e] *= al;
       }
+      const bool partial = i0 + S::SUB > end;  // wave-uniform
 #pragma unroll
       for (int r = 0; r < S::VLD; ++r) {
-        const int rr = r * S::RPL + lane / S::LPR;
+        const int rr = r * S::RPL + rg;
         float vf[S::EPV];
-        T::widen(vv[r], vf);
+        T::widen(st.vv[r], vf);
+        if (partial && i0 + rr >= end) {
+#pragma unroll
+          for (int e = 0; e < S::EPV; ++e) vf[e] = 0.f;  // stale rows may hold any bits
+        }
         const float* prow = &p_lds[wave][rr * S::PROW];
 #pragma unroll
         for (int h = 0; h < GP; ++h) {
@@ -283,9 +320,32 @@ __global__ __launch_bounds__(256) void attend_kernel(DecodeArgs a) {
         }
       }
       wave_lds_sync();
+    };
+
+    constexpr int STRIDE = kDecodeWaves * S::SUB;  // the four waves take turns
+    SubTile buf0, buf1;
+    int i0 = first_tok;
+    if (i0 < end) issue(i0, buf0);
+    if constexpr (KVSP_PIPELINE) {
+      while (i0 < end) {
+        int i1 = i0 + STRIDE;
+        if (i1 < end) issue(i1, buf1);
+        consume(i0, buf0);
+        if (i1 >= end) break;
+        const int i2 = i1 + STRIDE;
+        if (i2 < end) issue(i2, buf0);
+        consume(i1, buf1);
+        i0 = i2;
+      }
+    } else {
+      while (i0 < end) {
+        consume(i0, buf0);
+        i0 += STRIDE;
+        if (i0 < end) issue(i0, buf0);
+      }
     }
 
-    // Fold the row groups: every lane then holds the chunk's sums for its channels.
+    // Fold the row groups: every lane then holds its wave's sums for its channels.
 #pragma unroll
     for (int m = S::LPR; m < kWave; m <<= 1)
 #pragma unroll
@@ -293,136 +353,170 @@ __global__ __launch_bounds__(256) void attend_kernel(DecodeArgs a) {
 #pragma unroll
         for (int e = 0; e < S::EPV; ++e) acc[h][e] += lane_xor(acc[h][e], m);
 
+    // Merge the four wavefronts: M = max_w m_w, weights 2^(m_w - M).
     if (lane < 16) {
       ml_lds[wave][0][hl] = m_run;
       ml_lds[wave][1][hl] = l_run;
     }
-    wave_lds_sync();
-
-    const int rg = lane / S::LPR;
-    const int col = (lane % S::LPR) * S::EPV;
-    if (w.nc == 1) {
+    __syncthreads();
+    float scale_h[GP];
+#pragma unroll
+    for (int h = 0; h < GP; ++h) {
+      float M = NEG_INF;
+#pragma unroll
+      for (int v = 0; v < kDecodeWaves; ++v) M = fmaxf(M, ml_lds[v][0][h]);
+      scale_h[h] = M == NEG_INF ? 0.f : __builtin_amdgcn_exp2f(ml_lds[wave][0][h] - M);
+    }
+    if (wave > 0) {
+#pragma unroll
+      for (int h = 0; h < GP; ++h) {
+        if (h % S::NRG != rg) continue;
+#pragma unroll
+        for (int e = 0; e < S::EPV; ++e) xacc[wave - 1][h * D + col + e] = acc[h][e] * scale_h[h];
+      }
+    }
+    __syncthreads();
+    if (wave == 0) {
+      // lanes of row group rg own heads h with h % NRG == rg
+      float mh_lane, lh_lane;  // merged (m, l) of head hl
+      {
+        float M = NEG_INF;
+#pragma unroll
+        for (int v = 0; v < kDecodeWaves; ++v) M = fmaxf(M, ml_lds[v][0][hl]);
+        float Ls = 0.f;
+        if (M != NEG_INF) {
+#pragma unroll
+          for (int v = 0; v < kDecodeWaves; ++v)
+            Ls += ml_lds[v][1][hl] * __builtin_amdgcn_exp2f(ml_lds[v][0][hl] - M);
+        }
+        mh_lane = M;
+        lh_lane = Ls;
+      }
+      if (lane < 16) alpha_lds[0][hl] = lh_lane;  // l of every head, for the normalisation
+      wave_lds_sync();
+      const int64_t slot = static_cast<int64_t>(grp) * a.max_chunks + c;
 #pragma unroll
       for (int h = 0; h < GP; ++h) {
         if (h % S::NRG != rg || hg * GP + h >= G) continue;
-        const float lh = ml_lds[wave][1][h];
-        const float inv = lh > 0.f ? 1.f / lh : 0.f;
-        float* dst = a.out + (static_cast<int64_t>(b) * a.Hq + g * G + hg * GP + h) * D + col;
+        float o[S::EPV];
 #pragma unroll
-        for (int e = 0; e < S::EPV; ++e) dst[e] = acc[h][e] * inv;
-      }
-      if (a.lse != nullptr && head_ok && lane < 16) {
-        a.lse[static_cast<int64_t>(b) * a.Hq + hq_lane] =
-            l_run > 0.f ? (m_run + __builtin_log2f(l_run)) * 0.69314718055994531f : NEG_INF;
-      }
-    } else {
-      const int64_t slot =
-          ((static_cast<int64_t>(b) * a.Hkv + g) * a.n_head_groups + hg) * a.max_chunks + c;
+        for (int e = 0; e < S::EPV; ++e) {
+          float s = acc[h][e] * scale_h[h];
 #pragma unroll
-      for (int h = 0; h < GP; ++h) {
-        if (h % S::NRG != rg || hg * GP + h >= G) continue;
-        float* dst = a.part_acc + (slot * GP + h) * D + col;
+          for (int v = 1; v < kDecodeWaves; ++v) s += xacc[v - 1][h * D + col + e];
+          o[e] = s;
+        }
+        if (w.nc == 1) {
+          const float lh = alpha_lds[0][h];
+          const float inv = lh > 0.f ? 1.f / lh : 0.f;
+          float* dst = a.out + (static_cast<int64_t>(b) * a.Hq + g * G + hg * GP + h) * D + col;
 #pragma unroll
-        for (int e = 0; e < S::EPV; ++e) dst[e] = acc[h][e];
+          for (int e = 0; e < S::EPV; ++e) dst[e] = o[e] * inv;
+        } else {
+          float* dst = a.part_acc + (slot * GP + h) * D + col;
+#pragma unroll
+          for (int e = 0; e < S::EPV; ++e) store_coherent(dst + e, o[e]);
+        }
       }
-      if (lane < GP) {
-        a.part_ml[(slot * GP + lane) * 2 + 0] = m_run;
-        a.part_ml[(slot * GP + lane) * 2 + 1] = l_run;
+      if (w.nc == 1) {
+        if (a.lse != nullptr && head_ok && lane < 16)
+          a.lse[static_cast<int64_t>(b) * a.Hq + hq_lane] =
+              lh_lane > 0.f ? (mh_lane + __builtin_log2f(lh_lane)) * 0.69314718055994531f
+                            : NEG_INF;
+      } else {
+        if (lane < GP) {
+          store_coherent(a.part_ml + (slot * GP + lane) * 2 + 0, mh_lane);
+          store_coherent(a.part_ml + (slot * GP + lane) * 2 + 1, lh_lane);
+        }
+        wait_stores_done();  // the partial is at the device coherence point before it is counted
       }
     }
-    wave_lds_sync();
-  }
-}
-
-// Log-sum-exp merge of a (sequence, KV head, head group)'s chunk partials:
-//   M = max_c m_c, Lsum = sum_c l_c 2^(m_c - M), out = sum_c acc_c 2^(m_c - M) / Lsum.
-template <int D, int GP>
-__global__ __launch_bounds__(256) void combine_kernel(DecodeArgs a, int sub) {
-  const int lane = threadIdx.x % kWave;
-  const int grp = blockIdx.x * 4 + threadIdx.x / kWave;
-  const int n_groups = a.B * a.Hkv * a.n_head_groups;
-  if (grp >= n_groups) return;
-  const int hg = grp % a.n_head_groups;
-  const int g = (grp / a.n_head_groups) % a.Hkv;
-  const int b = grp / (a.n_head_groups * a.Hkv);
-  const SeqWork w = seq_work(a, b, sub);
-  if (w.nc <= 1) return;
-  const int G = a.Hq / a.Hkv;
-  const int64_t slot0 = static_cast<int64_t>(grp) * a.max_chunks;
-  const float NEG_INF = -__builtin_huge_valf();
-  for (int v = lane; v < GP * D / 4; v += kWave) {
-    const int h = (4 * v) / D;
-    const int d = (4 * v) % D;
-    if (hg * GP + h >= G) continue;
-    float M = NEG_INF;
-    for (int c = 0; c < w.nc; ++c) {
-      const float mc = a.part_ml[((slot0 + c) * GP + h) * 2];
-      if (a.part_ml[((slot0 + c) * GP + h) * 2 + 1] > 0.f) M = fmaxf(M, mc);
-    }
-    float Ls = 0.f;
-    float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (M != NEG_INF) {
-      for (int c = 0; c < w.nc; ++c) {
-        const float lc = a.part_ml[((slot0 + c) * GP + h) * 2 + 1];
-        if (!(lc > 0.f)) continue;
-        const float sc = __builtin_amdgcn_exp2f(a.part_ml[((slot0 + c) * GP + h) * 2] - M);
-        Ls += lc * sc;
-        const float4 pa = *reinterpret_cast<const float4*>(a.part_acc + ((slot0 + c) * GP + h) * D + d);
-        o.x = fmaf(pa.x, sc, o.x);
-        o.y = fmaf(pa.y, sc, o.y);
-        o.z = fmaf(pa.z, sc, o.z);
-        o.w = fmaf(pa.w, sc, o.w);
+    if (w.nc > 1) {
+      __syncthreads();
+      if (threadIdx.x == 0) {
+        const int old = __hip_atomic_fetch_add(a.counters + grp, 1, __ATOMIC_RELAXED,
+                                               __HIP_MEMORY_SCOPE_AGENT);
+        last_flag = old == w.nc - 1;
+      }
+      __syncthreads();
+      if (last_flag) {
+        // Every chunk of this group is published: merge by log-sum-exp,
+        // reading the partials at the device coherence point.
+        const int64_t slot0 = static_cast<int64_t>(grp) * a.max_chunks;
+        for (int v = threadIdx.x; v < GP * D / 4; v += blockDim.x) {
+          const int h = (4 * v) / D;
+          const int d = (4 * v) % D;
+          if (hg * GP + h >= G) continue;
+          float M = NEG_INF, Ls = 0.f;
+          float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll 4
+          for (int cc = 0; cc < w.nc; ++cc) {
+            const float mc = load_coherent(a.part_ml + ((slot0 + cc) * GP + h) * 2);
+            const float lc = load_coherent(a.part_ml + ((slot0 + cc) * GP + h) * 2 + 1);
+            const float* pp = a.part_acc + ((slot0 + cc) * GP + h) * D + d;
+            const float4 pa = make_float4(load_coherent(pp), load_coherent(pp + 1),
+                                          load_coherent(pp + 2), load_coherent(pp + 3));
+            if (!(lc > 0.f)) continue;
+            const float Mn = fmaxf(M, mc);
+            const float so = __builtin_amdgcn_exp2f(M - Mn);  // 0 while M is -inf
+            const float sn = __builtin_amdgcn_exp2f(mc - Mn);
+            Ls = Ls * so + lc * sn;
+            o.x = o.x * so + pa.x * sn;
+            o.y = o.y * so + pa.y * sn;
+            o.z = o.z * so + pa.z * sn;
+            o.w = o.w * so + pa.w * sn;
+            M = Mn;
+          }
+          const float inv = Ls > 0.f ? 1.f / Ls : 0.f;
+          const int hq = g * G + hg * GP + h;
+          *reinterpret_cast<float4*>(a.out + (static_cast<int64_t>(b) * a.Hq + hq) * D + d) =
+              make_float4(o.x * inv, o.y * inv, o.z * inv, o.w * inv);
+          if (d == 0 && a.lse != nullptr)
+            a.lse[static_cast<int64_t>(b) * a.Hq + hq] =
+                Ls > 0.f ? (M + __builtin_log2f(Ls)) * 0.69314718055994531f : NEG_INF;
+        }
+        if (threadIdx.x == 0) store_coherent_i(a.counters + grp, 0);  // ready for the next call
       }
     }
-    const float inv = Ls > 0.f ? 1.f / Ls : 0.f;
-    const int hq = g * G + hg * GP + h;
-    *reinterpret_cast<float4*>(a.out + (static_cast<int64_t>(b) * a.Hq + hq) * D + d) =
-        make_float4(o.x * inv, o.y * inv, o.z * inv, o.w * inv);
-    if (d == 0 && a.lse != nullptr)
-      a.lse[static_cast<int64_t>(b) * a.Hq + hq] =
-          Ls > 0.f ? (M + __builtin_log2f(Ls)) * 0.69314718055994531f : NEG_INF;
+    __syncthreads();  // LDS is reused by the next item
   }
 }
 
 template <typename T, int D, int GP>
-static hipError_t launch_decode_t(const DecodeArgs& a, int num_waves, hipStream_t stream) {
-  const int wgs = (num_waves + 3) / 4;
-  hipLaunchKernelGGL((attend_kernel<T, D, GP>), dim3(wgs), dim3(256), 0, stream, a);
-  hipError_t err = hipGetLastError();
-  if (err != hipSuccess || a.max_chunks == 1) return err;
-  const int n_groups = a.B * a.Hkv * a.n_head_groups;
-  hipLaunchKernelGGL((combine_kernel<D, GP>), dim3((n_groups + 3) / 4), dim3(256), 0, stream, a,
-                     DecodeShape<T, D>::SUB);
+static hipError_t launch_decode_t(const DecodeArgs& a, int num_wgs, hipStream_t stream) {
+  hipLaunchKernelGGL((attend_kernel<T, D, GP>), dim3(num_wgs), dim3(kDecodeWaves * kWave), 0,
+                     stream, a);
   return hipGetLastError();
 }
 
 template <typename T, int D>
-static hipError_t launch_decode_d(const DecodeArgs& a, int gp, int num_waves, hipStream_t stream) {
+static hipError_t launch_decode_d(const DecodeArgs& a, int gp, int num_wgs, hipStream_t stream) {
   switch (gp) {
-    case 1: return launch_decode_t<T, D, 1>(a, num_waves, stream);
-    case 2: return launch_decode_t<T, D, 2>(a, num_waves, stream);
-    case 4: return launch_decode_t<T, D, 4>(a, num_waves, stream);
-    case 8: return launch_decode_t<T, D, 8>(a, num_waves, stream);
-    default: return launch_decode_t<T, D, 16>(a, num_waves, stream);
+    case 1: return launch_decode_t<T, D, 1>(a, num_wgs, stream);
+    case 2: return launch_decode_t<T, D, 2>(a, num_wgs, stream);
+    case 4: return launch_decode_t<T, D, 4>(a, num_wgs, stream);
+    case 8: return launch_decode_t<T, D, 8>(a, num_wgs, stream);
+    default: return launch_decode_t<T, D, 16>(a, num_wgs, stream);
   }
 }
 
 template <typename T>
-static hipError_t launch_decode_dt(const DecodeArgs& a, int gp, int num_waves, hipStream_t stream) {
-  return a.D == 64 ? launch_decode_d<T, 64>(a, gp, num_waves, stream)
-                   : launch_decode_d<T, 128>(a, gp, num_waves, stream);
+static hipError_t launch_decode_dt(const DecodeArgs& a, int gp, int num_wgs, hipStream_t stream) {
+  return a.D == 64 ? launch_decode_d<T, 64>(a, gp, num_wgs, stream)
+                   : launch_decode_d<T, 128>(a, gp, num_wgs, stream);
 }
 
-hipError_t launch_decode(const DecodeArgs& a, int dtype, int group_pad, int num_waves,
+hipError_t launch_decode(const DecodeArgs& a, int dtype, int group_pad, int num_wgs,
                          hipStream_t stream) {
-  if (dtype == KVSP_F32) return launch_decode_dt<F32>(a, group_pad, num_waves, stream);
-  if (dtype == KVSP_F16) return launch_decode_dt<F16>(a, group_pad, num_waves, stream);
-  return launch_decode_dt<BF16>(a, group_pad, num_waves, stream);
+  if (dtype == KVSP_F32) return launch_decode_dt<F32>(a, group_pad, num_wgs, stream);
+  if (dtype == KVSP_F16) return launch_decode_dt<F16>(a, group_pad, num_wgs, stream);
+  return launch_decode_dt<BF16>(a, group_pad, num_wgs, stream);
 }
 
-int decode_sub_tokens(int dtype, int D) {
+int decode_chunk_quantum(int dtype, int D) {
   const int E = dtype == KVSP_F32 ? 4 : 2;
-  return 8192 / (D * E);
+  const int sub = KVSP_SUB_TILE_BYTES / (D * E) < 16 ? 16 : KVSP_SUB_TILE_BYTES / (D * E);
+  return kDecodeWaves * sub;
 }
 
 }  // namespace kvsp

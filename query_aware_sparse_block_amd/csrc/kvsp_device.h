@@ -91,6 +91,31 @@ __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
 }
 
+// ---- device-coherent accesses ------------------------------------------------------
+// Workgroups on different XCDs exchange split-KV partials through memory. The
+// partials are stored and loaded with device-scope (sc1) accesses, which reach
+// the device coherence point without write-back or invalidation of the whole
+// L2; the completion counter is a device-scope atomic.
+
+__device__ __forceinline__ void store_coherent(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ void store_coherent_i(int32_t* p, int32_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ float load_coherent(const float* p) {
+  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Waits until every memory access this wavefront issued has completed.
+__device__ __forceinline__ void wait_stores_done() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0);
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
 // ---- per-sequence integer plan ----------------------------------------------------
 // n blocks, C candidate blocks before the exact window [C*P, L), k kept blocks
 // and the dense-fallback decision; see kvsp_select_params in kvsp.h.

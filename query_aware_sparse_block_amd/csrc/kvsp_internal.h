@@ -43,8 +43,9 @@ struct TopkArgs {
 // Split-KV decode. The attended token sequence of sequence b (selected blocks
 // then the window, or every block when dense) is cut into at most `max_chunks`
 // chunks of whole sub-tiles; each (sequence, KV head, head group, chunk) is one
-// work item for one wavefront. Partials live at slot
-//   ((b * Hkv + g) * n_head_groups + hg) * max_chunks + c.
+// work item for one workgroup. Partials live at slot
+//   ((b * Hkv + g) * n_head_groups + hg) * max_chunks + c,
+// and counters[(b * Hkv + g) * n_head_groups + hg] counts finished chunks.
 struct DecodeArgs {
   const void* q;
   const void* k_pool;
@@ -58,6 +59,7 @@ struct DecodeArgs {
   float* lse;                   // may be NULL
   float* part_acc;              // [slots][GP][D]
   float* part_ml;               // [slots][GP][2]
+  int32_t* counters;            // [B * Hkv * n_head_groups], zero between calls
   int32_t B, Hq, Hkv, D, P, max_blocks;
   int32_t recent_window;
   int32_t all_dense;            // 1: ignore selection, attend every token
@@ -70,12 +72,12 @@ struct DecodeArgs {
 hipError_t launch_build_summaries(const SummaryArgs& a, int dtype, int D, hipStream_t stream);
 hipError_t launch_score(const ScoreArgs& a, int dtype, hipStream_t stream);
 hipError_t launch_topk(const TopkArgs& a, hipStream_t stream);
-hipError_t launch_decode(const DecodeArgs& a, int dtype, int group_pad, int num_waves,
+hipError_t launch_decode(const DecodeArgs& a, int dtype, int group_pad, int num_wgs,
                          hipStream_t stream);
 
 // Host-side sizing shared by the entry points and kvsp_workspace_bytes.
 int decode_group_pad(int G);        // GP: heads per work item (1, 2, 4, 8 or 16)
 int decode_max_chunks(const kvsp_layout& l);
-int decode_sub_tokens(int dtype, int D);
+int decode_chunk_quantum(int dtype, int D);  // tokens per chunk unit
 
 }  // namespace kvsp

@@ -17,7 +17,8 @@ from dataclasses import dataclass
 import torch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libkvsp.so")
+# KVSP_LIBRARY selects another build of the same library (e.g. a tuning variant).
+LIB_PATH = os.environ.get("KVSP_LIBRARY") or os.path.join(_PKG, "libkvsp.so")
 HEADER_PATH = os.path.join(os.path.dirname(_PKG), "include", "kvsp.h")
 
 KVSP_OK = 0
@@ -140,7 +141,7 @@ def kvsp_workspace_bytes(layout: kvsp_layout, params: SelectParams | None = None
 def alloc_workspace(layout: kvsp_layout, params: SelectParams | None = None,
                     device="cuda") -> torch.Tensor:
     n = kvsp_workspace_bytes(layout, params)
-    return torch.empty(max(n, 1), dtype=torch.uint8, device=device)
+    return torch.zeros(max(n, 1), dtype=torch.uint8, device=device)  # counters start at zero
 
 
 def kvsp_build_summaries(layout, k_pool, block_table, context_lens, summaries, stream=None):
