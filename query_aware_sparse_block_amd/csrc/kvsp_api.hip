@@ -14,7 +14,7 @@ namespace {
 
 constexpr size_t kAlign = 256;
 constexpr int kMaxBlocksPerSeq = 16384;
-constexpr int kMaxSummaryRow = 8192;   // Hkv * D floats (score kernel stages it in LDS as double)
+constexpr int kMaxSummaryRow = 7168;   // Hkv * D: the score kernel stages it in LDS as double
 // Workgroup items per decode launch (about one per resident workgroup) and the
 // cap on launched workgroups; items beyond it are taken in grid-stride order.
 #ifndef KVSP_DECODE_TARGET_ITEMS
@@ -24,6 +24,7 @@ constexpr int kMaxSummaryRow = 8192;   // Hkv * D floats (score kernel stages it
 #define KVSP_DECODE_MAX_WORKGROUPS 2048
 #endif
 constexpr int kDecodeTargetItems = KVSP_DECODE_TARGET_ITEMS;
+constexpr int kScoreTargetWorkgroups = 512;
 constexpr int kDecodeMaxWorkgroups = KVSP_DECODE_MAX_WORKGROUPS;
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
@@ -230,8 +231,12 @@ kvsp_status kvsp_score_topk(const kvsp_layout* layout, const kvsp_select_params*
   sa.D = l.head_dim;
   sa.P = l.block_size;
   sa.max_blocks = l.max_blocks_per_seq;
-  int64_t bpw = static_cast<int64_t>(l.batch) * l.max_blocks_per_seq / 16384;
-  sa.blocks_per_wave = static_cast<int>(bpw < 1 ? 1 : (bpw > 16 ? 16 : bpw));
+  // About kScoreTargetWorkgroups workgroups of four waves over all candidates.
+  const int64_t total_blocks = static_cast<int64_t>(l.batch) * l.max_blocks_per_seq;
+  int64_t bpw = (total_blocks + 4 * kScoreTargetWorkgroups - 1) / (4 * kScoreTargetWorkgroups);
+  const int per_pass = 64 / score_group_lanes(l.num_kv_heads, l.head_dim);  // blocks per wave pass
+  bpw = (bpw + per_pass - 1) / per_pass * per_pass;
+  sa.blocks_per_wave = static_cast<int>(bpw > 256 ? 256 : bpw);
   sa.top_k = p.top_k;
   sa.keep_num = p.keep_num;
   sa.keep_den = p.keep_den;

@@ -273,8 +273,7 @@ __global__ __launch_bounds__(256) void attend_kernel(DecodeArgs a) {
           mloc = fmaxf(mloc, s2[t][i]);
         }
       }
-      mloc = fmaxf(mloc, lane_xor(mloc, 16));
-      mloc = fmaxf(mloc, lane_xor(mloc, 32));
+      mloc = fold_max<16>(mloc);  // over the four lanes holding head hl
       const float m_new = fmaxf(m_run, mloc);
       const bool none = m_new == NEG_INF;
       const float alpha = none ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
@@ -288,8 +287,7 @@ __global__ __launch_bounds__(256) void attend_kernel(DecodeArgs a) {
           p_lds[wave][(16 * t + 4 * (lane / 16) + i) * S::PROW + hl] = pv;
         }
       }
-      psum += lane_xor(psum, 16);
-      psum += lane_xor(psum, 32);
+      psum = fold_sum<16>(psum);
       l_run = l_run * alpha + psum;
       m_run = m_new;
       if (lane < 16) alpha_lds[wave][hl] = alpha;
@@ -347,11 +345,9 @@ __global__ __launch_bounds__(256) void attend_kernel(DecodeArgs a) {
 
     // Fold the row groups: every lane then holds its wave's sums for its channels.
 #pragma unroll
-    for (int m = S::LPR; m < kWave; m <<= 1)
+    for (int h = 0; h < GP; ++h)
 #pragma unroll
-      for (int h = 0; h < GP; ++h)
-#pragma unroll
-        for (int e = 0; e < S::EPV; ++e) acc[h][e] += lane_xor(acc[h][e], m);
+      for (int e = 0; e < S::EPV; ++e) acc[h][e] = fold_sum<S::LPR>(acc[h][e]);
 
     // Merge the four wavefronts: M = max_w m_w, weights 2^(m_w - M).
     if (lane < 16) {

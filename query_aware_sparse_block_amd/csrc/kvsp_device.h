@@ -70,6 +70,8 @@ __device__ __forceinline__ uint4 load16(const void* p) {
 }
 
 // ---- cross-lane -----------------------------------------------------------------
+// DPP row permutations and the gfx950 permlane16/32 swaps move data between
+// lanes inside the VALU, without the LDS round trip of ds_bpermute.
 
 __device__ __forceinline__ float lane_xor(float v, int mask) { return __shfl_xor(v, mask, kWave); }
 
@@ -77,10 +79,113 @@ __device__ __forceinline__ double lane_xor(double v, int mask) {
   return __shfl_xor(v, mask, kWave);
 }
 
-__device__ __forceinline__ double wave_sum(double v) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) v += lane_xor(v, m);
+template <int CTRL, int ROW_MASK = 0xf, int BANK_MASK = 0xf, bool BOUND_ZERO = true>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t x) {
+  return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(x), CTRL, ROW_MASK,
+                                                           BANK_MASK, BOUND_ZERO));
+}
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float x) {
+  return __uint_as_float(dpp_u32<CTRL, 0xf, 0xf, false>(__float_as_uint(x)));
+}
+
+template <int CTRL>
+__device__ __forceinline__ double dpp_f64(double x) {
+  const uint64_t u = __builtin_bit_cast(uint64_t, x);
+  const uint32_t lo = dpp_u32<CTRL, 0xf, 0xf, false>(static_cast<uint32_t>(u));
+  const uint32_t hi = dpp_u32<CTRL, 0xf, 0xf, false>(static_cast<uint32_t>(u >> 32));
+  return __builtin_bit_cast(double, (static_cast<uint64_t>(hi) << 32) | lo);
+}
+
+template <int CTRL, typename F>
+__device__ __forceinline__ F dpp_f(F x) {
+  if constexpr (sizeof(F) == 8) {
+    return dpp_f64<CTRL>(x);
+  } else {
+    return dpp_f32<CTRL>(x);
+  }
+}
+
+// Partner values across 16-lane rows: lane l receives lane l ^ 16 (resp. l ^ 32).
+__device__ __forceinline__ float xor16(float x) {
+  const auto s = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  // s[0] = rows (0,0,2,2), s[1] = rows (1,1,3,3): the partner is whichever is not x.
+  return __uint_as_float((threadIdx.x & 16) ? s[0] : s[1]);
+}
+
+__device__ __forceinline__ float xor32(float x) {
+  const auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float((threadIdx.x & 32) ? s[0] : s[1]);
+}
+
+__device__ __forceinline__ double xor16(double x) {
+  const uint64_t u = __builtin_bit_cast(uint64_t, x);
+  const uint32_t lo = static_cast<uint32_t>(u), hi = static_cast<uint32_t>(u >> 32);
+  const auto sl = __builtin_amdgcn_permlane16_swap(lo, lo, false, false);
+  const auto sh = __builtin_amdgcn_permlane16_swap(hi, hi, false, false);
+  const bool up = threadIdx.x & 16;
+  return __builtin_bit_cast(double, (static_cast<uint64_t>(up ? sh[0] : sh[1]) << 32) | (up ? sl[0] : sl[1]));
+}
+
+__device__ __forceinline__ double xor32(double x) {
+  const uint64_t u = __builtin_bit_cast(uint64_t, x);
+  const uint32_t lo = static_cast<uint32_t>(u), hi = static_cast<uint32_t>(u >> 32);
+  const auto sl = __builtin_amdgcn_permlane32_swap(lo, lo, false, false);
+  const auto sh = __builtin_amdgcn_permlane32_swap(hi, hi, false, false);
+  const bool up = threadIdx.x & 32;
+  return __builtin_bit_cast(double, (static_cast<uint64_t>(up ? sh[0] : sh[1]) << 32) | (up ? sl[0] : sl[1]));
+}
+
+// Partner l ^ 8 (rotate each 16-lane row by 8).
+template <typename F>
+__device__ __forceinline__ F xor8(F x) { return dpp_f<0x128>(x); }
+
+// Sum over the lanes that share lane % STRIDE (STRIDE = 8, 16 or 32): every
+// lane receives the total of its residue class.
+template <int STRIDE, typename F>
+__device__ __forceinline__ F fold_sum(F v) {
+  if constexpr (STRIDE <= 8) v += xor8(v);
+  if constexpr (STRIDE <= 16) v += xor16(v);
+  if constexpr (STRIDE <= 32) v += xor32(v);
   return v;
+}
+
+template <int STRIDE>
+__device__ __forceinline__ float fold_max(float v) {
+  if constexpr (STRIDE <= 8) v = fmaxf(v, xor8(v));
+  if constexpr (STRIDE <= 16) v = fmaxf(v, xor16(v));
+  if constexpr (STRIDE <= 32) v = fmaxf(v, xor32(v));
+  return v;
+}
+
+// Sum over aligned groups of LANES consecutive lanes (1, 2, ..., 64); every
+// lane of a group receives the group's total. Butterfly order: quad swaps,
+// half-row mirror, row mirror, then the cross-row swaps.
+template <int LANES, typename F>
+__device__ __forceinline__ F group_sum(F v) {
+  if constexpr (LANES >= 2) v += dpp_f<0xB1>(v);   // quad_perm [1,0,3,2]
+  if constexpr (LANES >= 4) v += dpp_f<0x4E>(v);   // quad_perm [2,3,0,1]
+  if constexpr (LANES >= 8) v += dpp_f<0x141>(v);  // row_half_mirror
+  if constexpr (LANES >= 16) v += dpp_f<0x140>(v); // row_mirror
+  if constexpr (LANES >= 32) v += xor16(v);
+  if constexpr (LANES >= 64) v += xor32(v);
+  return v;
+}
+
+__device__ __forceinline__ double wave_sum(double v) { return group_sum<kWave>(v); }
+
+// Inclusive prefix sum over the wave (DPP row shifts and row broadcasts).
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x) {
+  const uint32_t t = x;
+  x += dpp_u32<0x111>(t);             // row_shr:1
+  x += dpp_u32<0x112>(t);             // row_shr:2
+  x += dpp_u32<0x113>(t);             // row_shr:3
+  x += dpp_u32<0x114, 0xf, 0xe>(x);   // row_shr:4, banks 1-3
+  x += dpp_u32<0x118, 0xf, 0xc>(x);   // row_shr:8, banks 2-3
+  x += dpp_u32<0x142, 0xa>(x);        // row_bcast:15 into rows 1 and 3
+  x += dpp_u32<0x143, 0xc>(x);        // row_bcast:31 into rows 2 and 3
+  return x;
 }
 
 // Orders LDS traffic between lanes of one wavefront (no workgroup barrier:

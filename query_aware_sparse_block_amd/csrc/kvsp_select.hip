@@ -26,58 +26,133 @@ namespace kvsp {
 
 // ---- scores ---------------------------------------------------------------------
 
-template <typename T>
+// A group of LG lanes scores one block: the block's summary row (Hkv * D
+// floats = LG * VPL 16-byte vectors) is split across the group, so a wave
+// scores 64 / LG blocks per pass, and one DPP butterfly over LG lanes reduces
+// all of them at once. The prologue issues its independent loads together
+// (context length, the workgroup's block-table entries, the queries); the
+// passes are double-buffered so one pass's loads fly while the previous one
+// is reduced.
+template <typename T, int LG, int VPL>
 __global__ __launch_bounds__(256) void score_kernel(ScoreArgs a) {
-  extern __shared__ double qbar[];  // [Hkv * D]
+  extern __shared__ double qbar[];  // [Hkv * D] group-summed queries, then [4 * bpw] ints
   const int b = blockIdx.y;
   const int lane = threadIdx.x % kWave;
-  const int wave = threadIdx.x / kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int per_wg = 4 * a.blocks_per_wave;
+  const int first = blockIdx.x * per_wg;
+  const int row = a.Hkv * a.D;
+  int32_t* phys_lds = reinterpret_cast<int32_t*>(qbar + row);
+  const int64_t trow = static_cast<int64_t>(b) * a.max_blocks;
+  // Block-table entries of this workgroup's range (in bounds of the row
+  // whatever the context length; entries past C are never used).
+  for (int i = threadIdx.x; i < per_wg; i += blockDim.x)
+    phys_lds[i] = first + i < a.max_blocks ? a.block_table[trow + first + i] : 0;
+
+  // qbar[g][d] = sum over the group's query heads, ascending, in double
+  // (exact for 16-bit inputs). One 16-byte vector of q per head and thread.
+  const int G = a.Hq / a.Hkv;
+  constexpr int EPV = T::kPerVec;
+  const char* qb = static_cast<const char*>(a.q) + static_cast<int64_t>(b) * a.Hq * a.D * T::kBytes;
+  for (int v = threadIdx.x; v < row / EPV; v += blockDim.x) {
+    const int g = (v * EPV) / a.D;
+    const int d0 = (v * EPV) % a.D;
+    double s[EPV];
+#pragma unroll
+    for (int e = 0; e < EPV; ++e) s[e] = 0.0;
+    for (int h = 0; h < G; ++h) {
+      float f[EPV];
+      T::widen(load16(qb + (static_cast<int64_t>(g * G + h) * a.D + d0) * T::kBytes), f);
+#pragma unroll
+      for (int e = 0; e < EPV; ++e) s[e] += static_cast<double>(f[e]);
+    }
+#pragma unroll
+    for (int e = 0; e < EPV; ++e) qbar[v * EPV + e] = s[e];
+  }
   const SelectArgs sel{a.top_k, a.keep_num, a.keep_den, a.keep_floor, a.recent_window,
                        a.gamma_num, a.gamma_den};
-  const int L = a.context_lens[b];
-  const int C = plan_sequence(L, a.P, sel).C;
-  const int first = blockIdx.x * 4 * a.blocks_per_wave;
+  const int C = plan_sequence(a.context_lens[b], a.P, sel).C;
+  __syncthreads();
   if (first >= C) return;  // uniform over the workgroup
 
-  const int G = a.Hq / a.Hkv;
-  const int row = a.Hkv * a.D;
-  const void* qb = static_cast<const char*>(a.q) + static_cast<int64_t>(b) * a.Hq * a.D * T::kBytes;
-  for (int p = threadIdx.x; p < row; p += blockDim.x) {
-    const int g = p / a.D;
-    const int d = p % a.D;
-    double s = 0.0;
-    for (int h = 0; h < G; ++h) s += static_cast<double>(T::load1(qb, static_cast<int64_t>(g * G + h) * a.D + d));
-    qbar[p] = s;
-  }
-  __syncthreads();
+  constexpr int BPP = kWave / LG;  // blocks per wave pass
+  const int gl = lane % LG;
+  const int slot = lane / LG;
+  const int w0 = wave * a.blocks_per_wave;  // offset of this wave's blocks in the range
+  const int j1 = min(C, first + w0 + a.blocks_per_wave);
 
-  const int j0 = first + wave * a.blocks_per_wave;
-  const int j1 = min(C, j0 + a.blocks_per_wave);
-  const int nvec = row / 4;
-  for (int j = j0; j < j1; ++j) {
-    const int64_t phys = a.block_table[static_cast<int64_t>(b) * a.max_blocks + j];
+  auto issue = [&](int jb, float4 (&sv)[VPL]) {
+    const int j = jb + slot;
+    const int64_t phys = j < j1 ? phys_lds[j - first] : 0;
     const float4* srow = reinterpret_cast<const float4*>(a.summaries + phys * row);
+#pragma unroll
+    for (int v = 0; v < VPL; ++v)
+      sv[v] = j < j1 ? srow[gl + LG * v] : make_float4(0.f, 0.f, 0.f, 0.f);
+  };
+  auto consume = [&](int jb, const float4 (&sv)[VPL]) {
     double acc = 0.0;
-    for (int v = lane; v < nvec; v += kWave) {
-      const float4 s = srow[v];
-      const double* qv = qbar + 4 * v;
-      acc += qv[0] * static_cast<double>(s.x);
-      acc += qv[1] * static_cast<double>(s.y);
-      acc += qv[2] * static_cast<double>(s.z);
-      acc += qv[3] * static_cast<double>(s.w);
+#pragma unroll
+    for (int v = 0; v < VPL; ++v) {
+      const double* qv = qbar + 4 * (gl + LG * v);
+      acc += qv[0] * static_cast<double>(sv[v].x);
+      acc += qv[1] * static_cast<double>(sv[v].y);
+      acc += qv[2] * static_cast<double>(sv[v].z);
+      acc += qv[3] * static_cast<double>(sv[v].w);
     }
-    acc = wave_sum(acc);
-    if (lane == 0) a.scores[static_cast<int64_t>(b) * a.max_blocks + j] = static_cast<float>(acc);
+    acc = group_sum<LG>(acc);
+    const int j = jb + slot;
+    if (gl == 0 && j < j1) a.scores[trow + j] = static_cast<float>(acc);
+  };
+
+  float4 buf0[VPL], buf1[VPL];
+  int jb = first + w0;
+  if (jb < j1) issue(jb, buf0);
+  while (jb < j1) {
+    const int jn = jb + BPP;
+    if (jn < j1) issue(jn, buf1);
+    consume(jb, buf0);
+    if (jn >= j1) break;
+    const int jn2 = jn + BPP;
+    if (jn2 < j1) issue(jn2, buf0);
+    consume(jn, buf1);
+    jb = jn2;
   }
+}
+
+template <typename T, int LG, int VPL>
+static hipError_t launch_score_v(const ScoreArgs& a, hipStream_t stream) {
+  const int per_wg = 4 * a.blocks_per_wave;
+  dim3 grid((a.max_blocks + per_wg - 1) / per_wg, a.B);
+  const size_t lds = static_cast<size_t>(a.Hkv) * a.D * sizeof(double) + per_wg * sizeof(int32_t);
+  hipLaunchKernelGGL((score_kernel<T, LG, VPL>), grid, dim3(256), lds, stream, a);
+  return hipGetLastError();
+}
+
+// Group width from the summary row length: 8 vectors per lane (more for the
+// longest rows), at most one wave per block.
+constexpr int kScoreVecPerLane = 8;
+int score_group_lanes(int Hkv, int D) {
+  const int nvec = Hkv * D / 4;
+  const int lg = nvec / kScoreVecPerLane;
+  return lg < 1 ? 1 : (lg > kWave ? kWave : lg);
 }
 
 template <typename T>
 static hipError_t launch_score_t(const ScoreArgs& a, hipStream_t stream) {
-  const int per_wg = 4 * a.blocks_per_wave;
-  dim3 grid((a.max_blocks + per_wg - 1) / per_wg, a.B);
-  const size_t lds = static_cast<size_t>(a.Hkv) * a.D * sizeof(double);
-  hipLaunchKernelGGL((score_kernel<T>), grid, dim3(256), lds, stream, a);
-  return hipGetLastError();
+  constexpr int V = kScoreVecPerLane;
+  const int nvec = a.Hkv * a.D / 4;
+  switch (score_group_lanes(a.Hkv, a.D)) {
+    case 1: return launch_score_v<T, 1, V>(a, stream);   // nvec >= 16 always: not reached
+    case 2: return launch_score_v<T, 2, V>(a, stream);
+    case 4: return launch_score_v<T, 4, V>(a, stream);
+    case 8: return launch_score_v<T, 8, V>(a, stream);
+    case 16: return launch_score_v<T, 16, V>(a, stream);
+    case 32: return launch_score_v<T, 32, V>(a, stream);
+    default:
+      if (nvec > kWave * 2 * V) return launch_score_v<T, 64, 4 * V>(a, stream);
+      if (nvec > kWave * V) return launch_score_v<T, 64, 2 * V>(a, stream);
+      return launch_score_v<T, 64, V>(a, stream);
+  }
 }
 
 hipError_t launch_score(const ScoreArgs& a, int dtype, hipStream_t stream) {
@@ -88,9 +163,7 @@ hipError_t launch_score(const ScoreArgs& a, int dtype, hipStream_t stream) {
 
 // ---- Top-k, spans, dense flag -------------------------------------------------------
 
-constexpr int kTopkThreads = 1024;
-constexpr int kTopkWaves = kTopkThreads / kWave;
-constexpr int kTopkMaxPerThread = 16;  // max_blocks <= 16384
+constexpr int kTopkMaxPerThread = 16;  // candidates per thread: C <= 16 * threads
 
 // Larger float <=> larger key; -0.0 and +0.0 map to the same key.
 __device__ __forceinline__ uint32_t order_key(float f) {
@@ -99,41 +172,40 @@ __device__ __forceinline__ uint32_t order_key(float f) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x, int lane) {
-#pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) {
-    const uint32_t y = __shfl_up(x, o, kWave);
-    if (lane >= o) x += y;
-  }
-  return x;
-}
-
 // Exclusive prefix sum of v over the workgroup in thread order; `total` gets
 // the sum over all threads. Every thread must call it. tmp holds
-// 2 * (kTopkWaves + 1) words: wave totals, then their exclusive scan.
+// 2 * (WAVES + 1) words: wave totals, then their exclusive scan.
+template <int WAVES>
 __device__ uint32_t block_excl_scan(uint32_t v, uint32_t* tmp, uint32_t& total) {
   const int lane = threadIdx.x % kWave;
-  const int wave = threadIdx.x / kWave;
-  const uint32_t incl = wave_incl_scan(v, lane);
-  if (lane == kWave - 1) tmp[wave] = incl;
-  __syncthreads();
-  uint32_t* offs = tmp + kTopkWaves + 1;
-  if (wave == 0) {
-    const uint32_t w = lane < kTopkWaves ? tmp[lane] : 0u;
-    const uint32_t wi = wave_incl_scan(w, lane);
-    if (lane < kTopkWaves) offs[lane] = wi - w;
-    if (lane == kTopkWaves - 1) offs[kTopkWaves] = wi;
+  const uint32_t incl = wave_incl_scan(v);
+  if constexpr (WAVES == 1) {
+    total = __builtin_amdgcn_readlane(incl, kWave - 1);
+    return incl - v;
+  } else {
+    const int wave = threadIdx.x / kWave;
+    if (lane == kWave - 1) tmp[wave] = incl;
+    __syncthreads();
+    uint32_t* offs = tmp + WAVES + 1;
+    if (wave == 0) {
+      const uint32_t w = lane < WAVES ? tmp[lane] : 0u;
+      const uint32_t wi = wave_incl_scan(w);
+      if (lane < WAVES) offs[lane] = wi - w;
+      if (lane == WAVES - 1) offs[WAVES] = wi;
+    }
+    __syncthreads();
+    const uint32_t res = offs[wave] + incl - v;
+    total = offs[WAVES];
+    __syncthreads();
+    return res;
   }
-  __syncthreads();
-  const uint32_t res = offs[wave] + incl - v;
-  total = offs[kTopkWaves];
-  __syncthreads();
-  return res;
 }
 
-__global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkArgs a) {
+template <int WAVES>
+__global__ __launch_bounds__(WAVES * kWave) void topk_kernel(TopkArgs a) {
+  constexpr int kTopkThreads = WAVES * kWave;
   __shared__ uint32_t hist[256];
-  __shared__ uint32_t scan_tmp[2 * (kTopkWaves + 1)];
+  __shared__ uint32_t scan_tmp[2 * (WAVES + 1)];
   __shared__ uint32_t bcast[2];
   extern __shared__ uint8_t kept[];  // [max_blocks] 0/1 per candidate
   const int b = blockIdx.x;
@@ -141,19 +213,27 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkArgs a) {
   const int lane = t % kWave;
   const SelectArgs sel{a.top_k, a.keep_num, a.keep_den, a.keep_floor, a.recent_window,
                        a.gamma_num, a.gamma_den};
+  // Candidates are assigned from the row capacity, so the score loads do not
+  // wait for the context length.
+  const int R = (a.max_blocks + kTopkThreads - 1) / kTopkThreads;  // consecutive per thread
+  const int jbase = t * R;
+  const int64_t row = static_cast<int64_t>(b) * a.max_blocks;
+  float raw[kTopkMaxPerThread];
+#pragma unroll
+  for (int r = 0; r < kTopkMaxPerThread; ++r) {
+    const int j = jbase + r;
+    raw[r] = (r < R && j < a.max_blocks) ? a.scores[row + j] : 0.f;
+  }
   const int L = a.context_lens[b];
   const SeqPlan p = plan_sequence(L, a.P, sel);
   const int C = p.C;
   const int k = p.k;
-  const int R = (C + kTopkThreads - 1) / kTopkThreads;  // consecutive candidates per thread
-  const int jbase = t * R;
-  const int64_t row = static_cast<int64_t>(b) * a.max_blocks;
 
   uint32_t key[kTopkMaxPerThread];
 #pragma unroll
   for (int r = 0; r < kTopkMaxPerThread; ++r) {
     const int j = jbase + r;
-    key[r] = (r < R && j < C) ? order_key(a.scores[row + j]) : 0u;
+    key[r] = (r < R && j < C) ? order_key(raw[r]) : 0u;
   }
 
   // Radix select of the k-th largest key (only when 0 < k < C).
@@ -165,7 +245,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkArgs a) {
     int krem = k;
     for (int pass = 0; pass < 4; ++pass) {
       const int shift = 24 - 8 * pass;
-      if (t < 256) hist[t] = 0;
+      for (int i = t; i < 256; i += kTopkThreads) hist[i] = 0;
       __syncthreads();
 #pragma unroll
       for (int r = 0; r < kTopkMaxPerThread; ++r) {
@@ -179,10 +259,9 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkArgs a) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) h[i] = hist[4 * lane + i];
         const uint32_t local = h[0] + h[1] + h[2] + h[3];
-        const uint32_t rev = __shfl(local, kWave - 1 - lane, kWave);
-        const uint32_t rev_incl = wave_incl_scan(rev, lane);
-        const uint32_t suffix_incl = __shfl(rev_incl, kWave - 1 - lane, kWave);
-        uint32_t above = suffix_incl - local;  // keys in digits owned by higher lanes
+        const uint32_t incl = wave_incl_scan(local);
+        const uint32_t total = __builtin_amdgcn_readlane(incl, kWave - 1);
+        uint32_t above = total - incl;  // keys in digits owned by higher lanes
         for (int i = 3; i >= 0; --i) {
           if (above < static_cast<uint32_t>(krem) && static_cast<uint32_t>(krem) <= above + h[i]) {
             bcast[0] = 4u * lane + i;
@@ -210,7 +289,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkArgs a) {
     if (partial && r < R && j < C && key[r] == thresh) ++n_eq;
   }
   uint32_t eq_total;
-  uint32_t eq_before = block_excl_scan(n_eq, scan_tmp, eq_total);
+  uint32_t eq_before = block_excl_scan<WAVES>(n_eq, scan_tmp, eq_total);
   uint32_t keep_bits = 0, n_keep = 0;
 #pragma unroll
   for (int r = 0; r < kTopkMaxPerThread; ++r) {
@@ -235,7 +314,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkArgs a) {
     }
   }
   uint32_t keep_total;
-  const uint32_t pos0 = block_excl_scan(n_keep, scan_tmp, keep_total);
+  const uint32_t pos0 = block_excl_scan<WAVES>(n_keep, scan_tmp, keep_total);
   uint32_t pos = pos0;
 #pragma unroll
   for (int r = 0; r < kTopkMaxPerThread; ++r) {
@@ -261,7 +340,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkArgs a) {
     }
   }
   uint32_t se_total;
-  const uint32_t se_before = block_excl_scan((n_start << 16) | n_end, scan_tmp, se_total);
+  const uint32_t se_before = block_excl_scan<WAVES>((n_start << 16) | n_end, scan_tmp, se_total);
   uint32_t s_idx = se_before >> 16, e_idx = se_before & 0xFFFFu;
   int32_t* sp = a.spans + row * 2 + static_cast<int64_t>(b) * 2;  // [B][max_blocks+1][2]
 #pragma unroll
@@ -288,10 +367,22 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkArgs a) {
   (void)lane;
 }
 
-hipError_t launch_topk(const TopkArgs& a, hipStream_t stream) {
+template <int WAVES>
+static hipError_t launch_topk_w(const TopkArgs& a, hipStream_t stream) {
   const size_t lds = static_cast<size_t>((a.max_blocks + 3) / 4 * 4);
-  hipLaunchKernelGGL(topk_kernel, dim3(a.B), dim3(kTopkThreads), lds, stream, a);
+  hipLaunchKernelGGL((topk_kernel<WAVES>), dim3(a.B), dim3(WAVES * kWave), lds, stream, a);
   return hipGetLastError();
+}
+
+// The fewest wavefronts that hold every candidate at 16 per thread.
+hipError_t launch_topk(const TopkArgs& a, hipStream_t stream) {
+  const int per_wave = kWave * kTopkMaxPerThread;
+  const int waves = (a.max_blocks + per_wave - 1) / per_wave;
+  if (waves <= 1) return launch_topk_w<1>(a, stream);
+  if (waves <= 2) return launch_topk_w<2>(a, stream);
+  if (waves <= 4) return launch_topk_w<4>(a, stream);
+  if (waves <= 8) return launch_topk_w<8>(a, stream);
+  return launch_topk_w<16>(a, stream);
 }
 
 }  // namespace kvsp

@@ -44,10 +44,7 @@ __global__ __launch_bounds__(256) void build_summaries_kernel(SummaryArgs a) {
       for (int e = 0; e < EPV; ++e) acc[e] += static_cast<double>(v[e]);
     }
 #pragma unroll
-    for (int m = LPR; m < kWave; m <<= 1) {
-#pragma unroll
-      for (int e = 0; e < EPV; ++e) acc[e] += lane_xor(acc[e], m);
-    }
+    for (int e = 0; e < EPV; ++e) acc[e] = fold_sum<LPR>(acc[e]);
     if (lane < LPR) {
       float* dst = a.summaries + (phys * a.Hkv + g) * D + col;
       const double inv_p = 1.0 / static_cast<double>(a.P);  // P is a power of two: exact

@@ -66,7 +66,7 @@ def test_workspace_bytes():
     (dict(num_q_heads=6, num_kv_heads=4), -1),
     (dict(batch=0), -1),
     (dict(max_blocks_per_seq=20000), -2),
-    (dict(num_kv_heads=128, num_q_heads=128), -2),
+    (dict(num_kv_heads=64, num_q_heads=64), -2),
 ])
 def test_bad_layout_rejected(over, code):
     lib = kvsp.library()
