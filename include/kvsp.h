@@ -150,8 +150,9 @@ kvsp_status kvsp_build_summaries(const kvsp_layout* layout, const void* k_pool,
  *   use_dense[b] = 1 if the kept fraction k / C exceeds γ, else 0.
  * The selection is always computed, also for sequences that fall back.
  * Output shapes: scores and selected [B][max_blocks_per_seq], spans
- * [B][max_blocks_per_seq + 1][2]; scores may be NULL. Entries past the
- * counts are left as they are. */
+ * [B][max_blocks_per_seq + 1][2]; scores may be NULL (they then live in the
+ * workspace). Entries past the counts are left as they are. The workspace is
+ * required (kvsp_workspace_bytes): it also holds per-sequence counters. */
 kvsp_status kvsp_score_topk(const kvsp_layout* layout, const kvsp_select_params* params,
                             const void* q, const float* summaries, const int32_t* block_table,
                             const int32_t* context_lens, float* scores, int32_t* selected,

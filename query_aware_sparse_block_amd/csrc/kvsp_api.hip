@@ -56,7 +56,7 @@ kvsp_status check_params(const kvsp_select_params* p) {
 }
 
 struct WorkspaceLayout {
-  size_t counters, part_acc, part_ml, scores, total;
+  size_t counters, select_counters, part_acc, part_ml, scores, total;
 };
 
 struct DecodeGeometry {
@@ -81,6 +81,8 @@ WorkspaceLayout workspace_layout(const kvsp_layout& l) {
   size_t off = 0;
   w.counters = off;
   off += align_up(static_cast<size_t>(l.batch) * l.num_kv_heads * d.n_head_groups * sizeof(int32_t));
+  w.select_counters = off;
+  off += align_up(static_cast<size_t>(l.batch) * sizeof(int32_t));
   w.part_acc = off;
   off += align_up(slots * d.gp * l.head_dim * sizeof(float));
   w.part_ml = off;
@@ -214,11 +216,9 @@ kvsp_status kvsp_score_topk(const kvsp_layout* layout, const kvsp_select_params*
     return KVSP_ERR_INVALID_ARG;
   const kvsp_layout& l = *layout;
   const kvsp_select_params& p = *params;
-  if (scores == nullptr) {
-    const WorkspaceLayout wl = workspace_layout(l);
-    if (workspace == nullptr || workspace_bytes < wl.total) return KVSP_ERR_WORKSPACE;
-    scores = reinterpret_cast<float*>(static_cast<char*>(workspace) + wl.scores);
-  }
+  const WorkspaceLayout wl = workspace_layout(l);
+  if (workspace == nullptr || workspace_bytes < wl.total) return KVSP_ERR_WORKSPACE;
+  if (scores == nullptr) scores = reinterpret_cast<float*>(static_cast<char*>(workspace) + wl.scores);
   ScoreArgs sa;
   sa.q = q;
   sa.summaries = summaries;
@@ -244,8 +244,6 @@ kvsp_status kvsp_score_topk(const kvsp_layout* layout, const kvsp_select_params*
   sa.recent_window = p.recent_window;
   sa.gamma_num = p.gamma_num;
   sa.gamma_den = p.gamma_den;
-  hipError_t e = launch_score(sa, l.dtype, stream);
-  if (e != hipSuccess) return KVSP_ERR_HIP;
   TopkArgs ta;
   ta.scores = scores;
   ta.context_lens = context_lens;
@@ -264,6 +262,12 @@ kvsp_status kvsp_score_topk(const kvsp_layout* layout, const kvsp_select_params*
   ta.recent_window = p.recent_window;
   ta.gamma_num = p.gamma_num;
   ta.gamma_den = p.gamma_den;
+  if (fused_select_supported(l.max_blocks_per_seq)) {
+    int32_t* counters = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + wl.select_counters);
+    return from_hip(launch_score_select(sa, ta, counters, l.dtype, stream));
+  }
+  hipError_t e = launch_score(sa, l.dtype, stream);
+  if (e != hipSuccess) return KVSP_ERR_HIP;
   return from_hip(launch_topk(ta, stream));
 }
 

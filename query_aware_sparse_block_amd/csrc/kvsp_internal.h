@@ -72,6 +72,11 @@ struct DecodeArgs {
 hipError_t launch_build_summaries(const SummaryArgs& a, int dtype, int D, hipStream_t stream);
 hipError_t launch_score(const ScoreArgs& a, int dtype, hipStream_t stream);
 hipError_t launch_topk(const TopkArgs& a, hipStream_t stream);
+// Scores and Top-k in one launch (max_blocks within fused_select_supported);
+// counters: [B] ints, zero between calls.
+bool fused_select_supported(int max_blocks);
+hipError_t launch_score_select(const ScoreArgs& sa, const TopkArgs& ta, int32_t* counters,
+                               int dtype, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs& a, int dtype, int group_pad, int num_wgs,
                          hipStream_t stream);
 

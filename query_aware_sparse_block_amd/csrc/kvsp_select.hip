@@ -32,11 +32,11 @@ namespace kvsp {
 // all of them at once. The prologue issues its independent loads together
 // (context length, the workgroup's block-table entries, the queries); the
 // passes are double-buffered so one pass's loads fly while the previous one
-// is reduced.
-template <typename T, int LG, int VPL>
-__global__ __launch_bounds__(256) void score_kernel(ScoreArgs a) {
-  extern __shared__ double qbar[];  // [Hkv * D] group-summed queries, then [4 * bpw] ints
-  const int b = blockIdx.y;
+// is reduced. This scores the workgroup's block range of sequence b and
+// returns C (the sequence's candidate count). COHERENT stores make the scores
+// visible to other workgroups of the same launch.
+template <typename T, int LG, int VPL, bool COHERENT>
+__device__ int score_blocks(const ScoreArgs& a, double* qbar, int b) {
   const int lane = threadIdx.x % kWave;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int per_wg = 4 * a.blocks_per_wave;
@@ -73,7 +73,7 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreArgs a) {
                        a.gamma_num, a.gamma_den};
   const int C = plan_sequence(a.context_lens[b], a.P, sel).C;
   __syncthreads();
-  if (first >= C) return;  // uniform over the workgroup
+  if (first >= C) return C;  // uniform over the workgroup
 
   constexpr int BPP = kWave / LG;  // blocks per wave pass
   const int gl = lane % LG;
@@ -101,7 +101,13 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreArgs a) {
     }
     acc = group_sum<LG>(acc);
     const int j = jb + slot;
-    if (gl == 0 && j < j1) a.scores[trow + j] = static_cast<float>(acc);
+    if (gl == 0 && j < j1) {
+      if constexpr (COHERENT) {
+        store_coherent(a.scores + trow + j, static_cast<float>(acc));
+      } else {
+        a.scores[trow + j] = static_cast<float>(acc);
+      }
+    }
   };
 
   float4 buf0[VPL], buf1[VPL];
@@ -117,6 +123,13 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreArgs a) {
     consume(jn, buf1);
     jb = jn2;
   }
+  return C;
+}
+
+template <typename T, int LG, int VPL>
+__global__ __launch_bounds__(256) void score_kernel(ScoreArgs a) {
+  extern __shared__ double qbar[];  // [Hkv * D] group-summed queries, then [4 * bpw] ints
+  score_blocks<T, LG, VPL, false>(a, qbar, blockIdx.y);
 }
 
 template <typename T, int LG, int VPL>
@@ -201,14 +214,21 @@ __device__ uint32_t block_excl_scan(uint32_t v, uint32_t* tmp, uint32_t& total) 
   }
 }
 
-template <int WAVES>
-__global__ __launch_bounds__(WAVES * kWave) void topk_kernel(TopkArgs a) {
+struct TopkShared {
+  uint32_t hist[256];
+  uint32_t scan_tmp[2 * (16 + 1)];
+  uint32_t bcast[2];
+};
+
+// Top-k, spans and the dense flag of sequence b, by a workgroup of WAVES
+// wavefronts (every thread calls it). `kept` holds max_blocks bytes of LDS.
+// COHERENT reads scores written by other workgroups of the same launch.
+template <int WAVES, bool COHERENT>
+__device__ void select_sequence(const TopkArgs& a, int b, TopkShared& sh, uint8_t* kept) {
   constexpr int kTopkThreads = WAVES * kWave;
-  __shared__ uint32_t hist[256];
-  __shared__ uint32_t scan_tmp[2 * (WAVES + 1)];
-  __shared__ uint32_t bcast[2];
-  extern __shared__ uint8_t kept[];  // [max_blocks] 0/1 per candidate
-  const int b = blockIdx.x;
+  uint32_t* hist = sh.hist;
+  uint32_t* scan_tmp = sh.scan_tmp;
+  uint32_t* bcast = sh.bcast;
   const int t = threadIdx.x;
   const int lane = t % kWave;
   const SelectArgs sel{a.top_k, a.keep_num, a.keep_den, a.keep_floor, a.recent_window,
@@ -222,7 +242,11 @@ __global__ __launch_bounds__(WAVES * kWave) void topk_kernel(TopkArgs a) {
 #pragma unroll
   for (int r = 0; r < kTopkMaxPerThread; ++r) {
     const int j = jbase + r;
-    raw[r] = (r < R && j < a.max_blocks) ? a.scores[row + j] : 0.f;
+    if constexpr (COHERENT) {
+      raw[r] = (r < R && j < a.max_blocks) ? load_coherent(a.scores + row + j) : 0.f;
+    } else {
+      raw[r] = (r < R && j < a.max_blocks) ? a.scores[row + j] : 0.f;
+    }
   }
   const int L = a.context_lens[b];
   const SeqPlan p = plan_sequence(L, a.P, sel);
@@ -368,10 +392,90 @@ __global__ __launch_bounds__(WAVES * kWave) void topk_kernel(TopkArgs a) {
 }
 
 template <int WAVES>
+__global__ __launch_bounds__(WAVES * kWave) void topk_kernel(TopkArgs a) {
+  __shared__ TopkShared sh;
+  extern __shared__ uint8_t kept[];  // [max_blocks] 0/1 per candidate
+  select_sequence<WAVES, false>(a, blockIdx.x, sh, kept);
+}
+
+template <int WAVES>
 static hipError_t launch_topk_w(const TopkArgs& a, hipStream_t stream) {
   const size_t lds = static_cast<size_t>((a.max_blocks + 3) / 4 * 4);
   hipLaunchKernelGGL((topk_kernel<WAVES>), dim3(a.B), dim3(WAVES * kWave), lds, stream, a);
   return hipGetLastError();
+}
+
+// Scores and selection in one launch: each workgroup scores its block range;
+// the last workgroup of a sequence to finish (counted with a self-resetting
+// device-scope atomic) runs that sequence's Top-k on the scores the others
+// published. Workgroup 0 of every sequence takes part even with no
+// candidates, so every sequence gets its counts and spans.
+template <typename T, int LG, int VPL>
+__global__ __launch_bounds__(256) void score_select_kernel(ScoreArgs sa, TopkArgs ta,
+                                                           int32_t* counters) {
+  extern __shared__ double lds[];
+  const int b = blockIdx.y;
+  const int C = score_blocks<T, LG, VPL, true>(sa, lds, b);
+  const int per_wg = 4 * sa.blocks_per_wave;
+  const int first = blockIdx.x * per_wg;
+  if (first >= C && blockIdx.x != 0) return;  // uniform: no blocks, not the anchor
+  const int expected = C > 0 ? (C + per_wg - 1) / per_wg : 1;
+  __shared__ int is_last;
+  wait_stores_done();
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const int old = __hip_atomic_fetch_add(counters + b, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    is_last = old == expected - 1;
+  }
+  __syncthreads();
+  if (!is_last) return;
+  TopkShared& sh = *reinterpret_cast<TopkShared*>(lds);
+  uint8_t* kept = reinterpret_cast<uint8_t*>(lds) + sizeof(TopkShared);
+  select_sequence<4, true>(ta, b, sh, kept);
+  if (threadIdx.x == 0) store_coherent_i(counters + b, 0);
+}
+
+constexpr int kFusedSelectMaxBlocks = 4 * kWave * kTopkMaxPerThread;
+
+template <typename T, int LG, int VPL>
+static hipError_t launch_fused_v(const ScoreArgs& sa, const TopkArgs& ta, int32_t* counters,
+                                 hipStream_t stream) {
+  const int per_wg = 4 * sa.blocks_per_wave;
+  dim3 grid((sa.max_blocks + per_wg - 1) / per_wg, sa.B);
+  const size_t score_lds = static_cast<size_t>(sa.Hkv) * sa.D * sizeof(double) + per_wg * sizeof(int32_t);
+  const size_t topk_lds = sizeof(TopkShared) + static_cast<size_t>(sa.max_blocks);
+  const size_t lds = (score_lds > topk_lds ? score_lds : topk_lds + 7) / 8 * 8;
+  hipLaunchKernelGGL((score_select_kernel<T, LG, VPL>), grid, dim3(256), lds, stream, sa, ta,
+                     counters);
+  return hipGetLastError();
+}
+
+template <typename T>
+static hipError_t launch_fused_t(const ScoreArgs& sa, const TopkArgs& ta, int32_t* counters,
+                                 hipStream_t stream) {
+  constexpr int V = kScoreVecPerLane;
+  const int nvec = sa.Hkv * sa.D / 4;
+  switch (score_group_lanes(sa.Hkv, sa.D)) {
+    case 1: return launch_fused_v<T, 1, V>(sa, ta, counters, stream);
+    case 2: return launch_fused_v<T, 2, V>(sa, ta, counters, stream);
+    case 4: return launch_fused_v<T, 4, V>(sa, ta, counters, stream);
+    case 8: return launch_fused_v<T, 8, V>(sa, ta, counters, stream);
+    case 16: return launch_fused_v<T, 16, V>(sa, ta, counters, stream);
+    case 32: return launch_fused_v<T, 32, V>(sa, ta, counters, stream);
+    default:
+      if (nvec > kWave * 2 * V) return launch_fused_v<T, 64, 4 * V>(sa, ta, counters, stream);
+      if (nvec > kWave * V) return launch_fused_v<T, 64, 2 * V>(sa, ta, counters, stream);
+      return launch_fused_v<T, 64, V>(sa, ta, counters, stream);
+  }
+}
+
+bool fused_select_supported(int max_blocks) { return max_blocks <= kFusedSelectMaxBlocks; }
+
+hipError_t launch_score_select(const ScoreArgs& sa, const TopkArgs& ta, int32_t* counters,
+                               int dtype, hipStream_t stream) {
+  if (dtype == KVSP_F32) return launch_fused_t<F32>(sa, ta, counters, stream);
+  if (dtype == KVSP_F16) return launch_fused_t<F16>(sa, ta, counters, stream);
+  return launch_fused_t<BF16>(sa, ta, counters, stream);
 }
 
 // The fewest wavefronts that hold every candidate at 16 per thread.

@@ -145,3 +145,11 @@ def test_scale_argument():
     out = buf.out.cpu().numpy()
     for h in (0, 5):
         assert np.max(np.abs(out[0, h] - ref[h])) <= 1e-5
+
+
+def test_long_block_table_uses_two_kernel_selection():
+    # 4400 blocks of 16 tokens: beyond what one workgroup selects in the fused
+    # score+select launch, so scoring and Top-k run as separate kernels.
+    case = wl.make_case("long-table", seed=66, B=1, Hq=2, Hkv=1, D=64, P=16, dtype="fp16",
+                        ctx_lens=[70400], top_k=12, keep_floor=1, recent_window=40)
+    H.full_parity(case)
