@@ -151,6 +151,7 @@ def main():
 
     from query_aware_sparse_block_amd import device as dev
     from query_aware_sparse_block_amd import kvsp
+    from query_aware_sparse_block_amd import profiling
 
     kvsp.library()
     wls = workloads()
@@ -242,7 +243,7 @@ def main():
                        "step": ms_per_step * 1e3},
         "roofline": {
             "bound": "hbm",
-            "kernel": "kvsp_sparse_decode (attend + merge)",
+            "kernel": "attend_kernel (the whole kvsp_sparse_decode call)",
             "achieved": achieved,
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
@@ -250,7 +251,9 @@ def main():
             "bytes_per_launch": attn_bytes,
             "kv_bytes_per_launch": kv_bytes,
             "per_unit": f"2*D*E = {2 * case.D * E} B per attended token per KV head",
-            "traffic": None,
+            "traffic": profiling.recorded_traffic(args.workload),
+            "traffic_source": "profiles/attend_traffic.txt (rocprofv3 FETCH_SIZE*2 + "
+                              "WRITE_SIZE*1 per launch; null if the decode sources changed)",
         },
         "scoring": {"bytes_per_launch": scoring_bytes(case, Cs),
                     "gbps": scoring_bytes(case, Cs) / (sel_s / args.steps) / 1e9},

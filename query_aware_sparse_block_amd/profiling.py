@@ -1,0 +1,149 @@
+"""Profiling helpers: rocprofv3 summaries, counter-based HBM traffic, and the
+plain-copy reference the counters are scaled by.
+
+  python -m query_aware_sparse_block_amd.profiling copy-probe
+      One device-to-device copy of exactly 1 GiB (after a warm-up copy): the
+      known-size reference for FETCH_SIZE / WRITE_SIZE scaling.
+  python -m query_aware_sparse_block_amd.profiling stats STATS_CSV OUT_TXT "COMMAND"
+      Text summary of a `rocprofv3 --kernel-trace --stats` kernel_stats.csv.
+  python -m query_aware_sparse_block_amd.profiling traffic WORKLOAD FETCH_CSV WRITE_CSV \
+          COPY_FETCH_CSV COPY_WRITE_CSV OUT_TXT "COMMANDS"
+      Per-launch HBM bytes of the decode kernel from two --pmc runs, scaled by
+      the copy reference, stamped with the digest of the decode sources.
+"""
+
+from __future__ import annotations
+
+import csv
+import hashlib
+import os
+import statistics
+import sys
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(_PKG)
+PROFILES = os.path.join(ROOT, "profiles")
+TRAFFIC_FILE = os.path.join(PROFILES, "attend_traffic.txt")
+DECODE_SOURCES = ["csrc/kvsp_decode.hip", "csrc/kvsp_device.h", "csrc/kvsp_api.hip",
+                  "csrc/kvsp_internal.h"]
+COPY_BYTES = 1 << 30
+DECODE_KERNEL = "attend_kernel"
+COPY_KERNEL = "__amd_rocclr_copyBuffer"
+
+
+def decode_source_digest() -> str:
+    h = hashlib.sha256()
+    for rel in DECODE_SOURCES:
+        with open(os.path.join(_PKG, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def copy_probe():
+    import torch
+    n = COPY_BYTES // 4
+    a = torch.ones(n, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    b.copy_(a)  # warm-up
+    torch.cuda.synchronize()
+    b.copy_(a)
+    torch.cuda.synchronize()
+    print(f"copied {COPY_BYTES} bytes twice", flush=True)
+
+
+def _rows(path):
+    with open(path) as f:
+        return list(csv.DictReader(f))
+
+
+def counter_per_dispatch(path, kernel_substr, counter):
+    vals = [float(r["Counter_Value"]) for r in _rows(path)
+            if kernel_substr in r["Kernel_Name"] and r["Counter_Name"] == counter]
+    return vals
+
+
+def copy_scale(copy_csv, counter):
+    """Bytes per counter unit, from the largest copy dispatch (the 1 GiB one)."""
+    vals = counter_per_dispatch(copy_csv, COPY_KERNEL, counter)
+    if not vals:
+        raise RuntimeError(f"no {COPY_KERNEL} dispatch with {counter} in {copy_csv}")
+    return COPY_BYTES / max(vals)
+
+
+def write_traffic(workload, fetch_csv, write_csv, copy_fetch_csv, copy_write_csv, out_txt,
+                  commands):
+    fetch = counter_per_dispatch(fetch_csv, DECODE_KERNEL, "FETCH_SIZE")
+    write = counter_per_dispatch(write_csv, DECODE_KERNEL, "WRITE_SIZE")
+    fs = copy_scale(copy_fetch_csv, "FETCH_SIZE")
+    ws = copy_scale(copy_write_csv, "WRITE_SIZE")
+    f_med = statistics.median(fetch)
+    w_med = statistics.median(write)
+    traffic = f_med * fs + w_med * ws
+    lines = [
+        "# HBM traffic of the decode kernel (attend_kernel), per launch",
+        f"workload = {workload}",
+        f"decode_source_digest = {decode_source_digest()}",
+        f"fetch_size_median = {f_med:.1f}",
+        f"write_size_median = {w_med:.1f}",
+        f"dispatches = {len(fetch)} / {len(write)}",
+        f"fetch_scale_bytes_per_unit = {fs:.4f}",
+        f"write_scale_bytes_per_unit = {ws:.4f}",
+        f"traffic_bytes = {traffic:.0f}",
+        f"commands = {commands}",
+    ]
+    with open(out_txt, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+def recorded_traffic(workload, path=TRAFFIC_FILE):
+    """Traffic bytes recorded for `workload`, or None when absent or when the
+    decode sources changed since the counters were taken."""
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        if "=" in line and not line.startswith("#"):
+            k, v = line.split("=", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("workload") != workload or kv.get("decode_source_digest") != decode_source_digest():
+        return None
+    return float(kv["traffic_bytes"])
+
+
+def write_stats(stats_csv, out_txt, command, top=12):
+    rows = _rows(stats_csv)
+    rows.sort(key=lambda r: -float(r["TotalDurationNs"]))
+    lines = [f"# rocprofv3 --kernel-trace --stats: {command}", "",
+             f"{'kernel':<72} {'calls':>6} {'avg_us':>10} {'min_us':>10} {'max_us':>10} {'pct':>6}"]
+    for r in rows[:top]:
+        name = r["Name"]
+        if len(name) > 72:
+            name = name[:69] + "..."
+        lines.append(f"{name:<72} {int(r['Calls']):>6} {float(r['AverageNs']) / 1e3:>10.2f} "
+                     f"{float(r['MinNs']) / 1e3:>10.2f} {float(r['MaxNs']) / 1e3:>10.2f} "
+                     f"{float(r['Percentage']):>6.2f}")
+    with open(out_txt, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+def main(argv):
+    if not argv:
+        print(__doc__)
+        return 2
+    cmd = argv[0]
+    if cmd == "copy-probe":
+        copy_probe()
+    elif cmd == "stats":
+        write_stats(argv[1], argv[2], argv[3])
+    elif cmd == "traffic":
+        write_traffic(*argv[1:8])
+    else:
+        print(__doc__)
+        return 2
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main(sys.argv[1:]))
