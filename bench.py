@@ -176,25 +176,42 @@ def main():
     print(f"[bench] {R} replica(s) of {pool_bytes / 2**30:.2f} GiB resident", file=sys.stderr,
           flush=True)
 
-    stream = torch.cuda.current_stream()
     for i in range(args.warmup):
         dev.decode_step(reps[i % R], bufs[i % R])
     torch.cuda.synchronize()
 
-    def timed(fn, n):
+    # Each timed region is one HIP graph holding all K calls (replicas taken
+    # in turn), so host launch overhead does not enter the measurement. The
+    # kernels reset their own completion counters, so the graphs hold kernel
+    # nodes only.
+    def capture(fn):
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            fn(0)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for i in range(args.steps):
+                fn(i)
+        graph.replay()  # warm
+        torch.cuda.synchronize()
+        return graph
+
+    def timed(graph):
         start = torch.cuda.Event(enable_timing=True)
         stop = torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
-        start.record(stream)
-        for i in range(n):
-            fn(i)
-        stop.record(stream)
+        start.record()
+        graph.replay()
+        stop.record()
         torch.cuda.synchronize()
         return start.elapsed_time(stop) / 1e3  # seconds
 
-    step_s = timed(lambda i: dev.decode_step(reps[i % R], bufs[i % R]), args.steps)
-    attn_s = timed(lambda i: dev.sparse_decode(reps[i % R], bufs[i % R]), args.steps)
-    sel_s = timed(lambda i: dev.score_topk(reps[i % R], bufs[i % R]), args.steps)
+    step_s = timed(capture(lambda i: dev.decode_step(reps[i % R], bufs[i % R])))
+    attn_s = timed(capture(lambda i: dev.sparse_decode(reps[i % R], bufs[i % R])))
+    sel_s = timed(capture(lambda i: dev.score_topk(reps[i % R], bufs[i % R])))
 
     nsel = bufs[0].num_selected.cpu().numpy()
     dense = bufs[0].use_dense.cpu().numpy()
@@ -226,6 +243,7 @@ def main():
         "vs_baseline": None,
         "dtype": case.dtype,
         "data": "synthetic",
+        "launch": "hipGraph of all K steps",
         "config": {
             "workload": args.workload,
             "batch": case.B, "q_heads": case.Hq, "kv_heads": case.Hkv, "head_dim": case.D,

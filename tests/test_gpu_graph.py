@@ -1,0 +1,66 @@
+"""The decode step captured in a HIP graph (through torch.cuda.CUDAGraph)
+replays to the same bits as the eager step. The library records no memset
+into a graph: its completion counters reset themselves inside the kernels.
+Each replay follows eager work (output buffers cleared, another eager step)
+and a synchronization, and is checked on its own."""
+
+import numpy as np
+import pytest
+import torch
+
+from query_aware_sparse_block_amd import device as dev
+from query_aware_sparse_block_amd import workloads as wl
+from tests import gpu_helpers as H
+
+pytestmark = pytest.mark.gpu
+
+KEYS = ("selected", "num_selected", "spans", "num_spans", "use_dense", "scores", "out", "lse")
+
+
+def _snapshot(buf):
+    return {k: getattr(buf, k).cpu().numpy().copy() for k in KEYS}
+
+
+@pytest.mark.parametrize("name,make", [
+    ("serving-small", lambda: wl.c5(keep="1/32", B=8, L=4096)),
+    ("serving-small-dense", lambda: wl.c5(keep="7/10", B=8, L=4096)),
+    ("minicpm-small", lambda: wl.c3(keep="1/16", L=16384)),
+])
+def test_graph_replays_match_eager(name, make):
+    H.note(f"[graph] {name}")
+    case = make()
+    dc = dev.upload(case)
+    buf = dev.alloc_buffers(dc)
+    other = dev.alloc_buffers(dc)
+    dev.build_summaries(dc, buf)
+    dev.build_summaries(dc, other)
+    dev.decode_step(dc, buf)
+    torch.cuda.synchronize()
+    eager = _snapshot(buf)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        dev.decode_step(dc, buf)  # warm-up on the capture stream's side
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        dev.decode_step(dc, buf)
+    torch.cuda.synchronize()
+
+    for rep in range(3):
+        # eager work between replays: reset the outputs to their initial fill
+        # (entries past the counts are never written), run another step
+        buf.selected.fill_(-1)
+        buf.spans.fill_(-1)
+        for k in ("out", "lse", "scores", "num_selected", "num_spans", "use_dense"):
+            getattr(buf, k).zero_()
+        dev.decode_step(dc, other)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        got = _snapshot(buf)
+        for k in KEYS:
+            assert np.array_equal(got[k], eager[k]), f"replay {rep}: {k} differs"
+    assert np.array_equal(_snapshot(other)["out"], eager["out"])
