@@ -24,6 +24,10 @@ constexpr int kMaxSummaryRow = 7168;   // Hkv * D: the score kernel stages it in
 #define KVSP_DECODE_MAX_WORKGROUPS 2048
 #endif
 constexpr int kDecodeTargetItems = KVSP_DECODE_TARGET_ITEMS;
+// The merge stages (m, l) of every chunk of a group in the kernel's LDS (the
+// 3 * GP * D floats of its wave-merge buffer): 2 * chunks * GP + 2 * GP must
+// fit, i.e. chunks <= 95 at D = 64.
+constexpr int kDecodeMaxChunks = 64;
 constexpr int kScoreTargetWorkgroups = 512;
 constexpr int kDecodeMaxWorkgroups = KVSP_DECODE_MAX_WORKGROUPS;
 
@@ -161,7 +165,7 @@ int decode_max_chunks(const kvsp_layout& l) {
   const int quantum = decode_chunk_quantum(l.dtype, l.head_dim);
   const int64_t max_sub = (static_cast<int64_t>(l.max_blocks_per_seq) * l.block_size + quantum - 1) / quantum;
   int64_t mc = 1;
-  while (groups * mc < kDecodeTargetItems && mc < max_sub) mc *= 2;
+  while (groups * mc < kDecodeTargetItems && mc < max_sub && mc < kDecodeMaxChunks) mc *= 2;
   return static_cast<int>(mc);
 }
 

@@ -44,6 +44,10 @@ namespace kvsp {
 #ifndef KVSP_PIPELINE
 #define KVSP_PIPELINE 0
 #endif
+// 1: items are numbered chunk-major (see the item loop of attend_kernel).
+#ifndef KVSP_CHUNK_MAJOR
+#define KVSP_CHUNK_MAJOR 1
+#endif
 
 template <typename T, int D>
 struct DecodeShape {
@@ -161,22 +165,29 @@ __global__ __launch_bounds__(256) void attend_kernel(DecodeArgs a) {
   const int col = (lane % S::LPR) * S::EPV;
   const int G = a.Hq / a.Hkv;
   const float NEG_INF = -__builtin_huge_valf();
+  const __amdgpu_buffer_rsrc_t part_rsrc =
+      coherent_rsrc(a.part_acc, static_cast<uint32_t>(static_cast<int64_t>(a.total_items) * GP * D * sizeof(float)));
 
+  const int n_groups = a.total_items / a.max_chunks;
   for (int item = blockIdx.x; item < a.total_items; item += gridDim.x) {
+#if KVSP_CHUNK_MAJOR
+    // Chunk-major order: consecutive workgroups (which the dispatcher deals
+    // round-robin to the XCDs) take the same chunk of different groups, so
+    // every XCD gets an equal share of first and last chunks.
+    const int c = item / n_groups;
+    int rest = item - c * n_groups;
+#else
     int rest = item;
     const int c = rest % a.max_chunks;
     rest /= a.max_chunks;
+#endif
     const int grp = rest;  // (b * Hkv + g) * n_head_groups + hg
     const int hg = rest % a.n_head_groups;
     rest /= a.n_head_groups;
     const int g = rest % a.Hkv;
     const int b = rest / a.Hkv;
-    const SeqWork w = seq_work(a, b, QUANTUM);
-    if (c >= w.nc) continue;  // uniform over the workgroup
-    const int start = c * w.CT;
-    const int end = min(w.T, start + w.CT);
-
-    // Queries of this head group as the MFMA B operand.
+    // Queries of this head group as the MFMA B operand, loaded before the
+    // sequence's plan so both travel in the same round trip.
     const int head_in_group = hg * GP + hl;
     const bool head_ok = hl < GP && head_in_group < G;
     const int hq_lane = g * G + head_in_group;
@@ -191,6 +202,10 @@ __global__ __launch_bounds__(256) void attend_kernel(DecodeArgs a) {
         qop[s] = make_uint4(0, 0, 0, 0);
       }
     }
+    const SeqWork w = seq_work(a, b, QUANTUM);
+    if (c >= w.nc) continue;  // uniform over the workgroup
+    const int start = c * w.CT;
+    const int end = min(w.T, start + w.CT);
 
     float m_run = NEG_INF, l_run = 0.f;
     float acc[GP][S::EPV];
@@ -409,9 +424,10 @@ __global__ __launch_bounds__(256) void attend_kernel(DecodeArgs a) {
 #pragma unroll
           for (int e = 0; e < S::EPV; ++e) dst[e] = o[e] * inv;
         } else {
-          float* dst = a.part_acc + (slot * GP + h) * D + col;
+          const uint32_t off = static_cast<uint32_t>(((slot * GP + h) * D + col) * sizeof(float));
 #pragma unroll
-          for (int e = 0; e < S::EPV; ++e) store_coherent(dst + e, o[e]);
+          for (int e = 0; e < S::EPV; e += 4)
+            store_coherent4(part_rsrc, off + e * sizeof(float), make_float4(o[e], o[e + 1], o[e + 2], o[e + 3]));
         }
       }
       if (w.nc == 1) {
@@ -438,38 +454,87 @@ __global__ __launch_bounds__(256) void attend_kernel(DecodeArgs a) {
       if (last_flag) {
         // Every chunk of this group is published: merge by log-sum-exp,
         // reading the partials at the device coherence point.
+        //   1. (m, l) of every (chunk, head) into LDS in one round trip;
+        //   2. per head M = max m and Lsum = sum l 2^(m - M);
+        //   3. out = sum acc 2^(m - M) / Lsum, the chunks split over CG
+        //      thread groups (16-byte loads), folded through LDS.
+        // The merge reuses the LDS of the main loop (xacc and p_lds).
         const int64_t slot0 = static_cast<int64_t>(grp) * a.max_chunks;
-        for (int v = threadIdx.x; v < GP * D / 4; v += blockDim.x) {
-          const int h = (4 * v) / D;
-          const int d = (4 * v) % D;
-          if (hg * GP + h >= G) continue;
-          float M = NEG_INF, Ls = 0.f;
+        float* ml_s = &xacc[0][0];                    // [nc][GP][2]
+        float* head_s = ml_s + 2 * a.max_chunks * GP;  // [GP][2]: M, Lsum
+        float4* red_s = reinterpret_cast<float4*>(&p_lds[0][0]);
+        constexpr int PAIRS = GP * D / 4;                     // (head, 4 channels) outputs
+        constexpr int CG = PAIRS >= 256 ? 1 : 256 / PAIRS;    // chunk groups per output
+        constexpr int PER = PAIRS >= 256 ? PAIRS / 256 : 1;   // outputs per thread
+        const int cg = threadIdx.x / (PAIRS >= 256 ? 256 : PAIRS);
+        const int pbase = threadIdx.x % (PAIRS >= 256 ? 256 : PAIRS);
+        for (int i = threadIdx.x; i < w.nc * GP; i += blockDim.x) {
+          ml_s[2 * i] = load_coherent(a.part_ml + (slot0 * GP + i) * 2);
+          ml_s[2 * i + 1] = load_coherent(a.part_ml + (slot0 * GP + i) * 2 + 1);
+        }
+        __syncthreads();
+        if (threadIdx.x < GP) {
+          const int h = threadIdx.x;
+          float M = NEG_INF;
+          for (int cc = 0; cc < w.nc; ++cc)
+            if (ml_s[2 * (cc * GP + h) + 1] > 0.f) M = fmaxf(M, ml_s[2 * (cc * GP + h)]);
+          float Ls = 0.f;
+          if (M != NEG_INF)
+            for (int cc = 0; cc < w.nc; ++cc) {
+              const float lc = ml_s[2 * (cc * GP + h) + 1];
+              if (lc > 0.f) Ls += lc * __builtin_amdgcn_exp2f(ml_s[2 * (cc * GP + h)] - M);
+            }
+          head_s[2 * h] = M;
+          head_s[2 * h + 1] = Ls;
+        }
+        __syncthreads();
+        auto weight = [&](int cc, int h, float M) {
+          const float lc = ml_s[2 * (cc * GP + h) + 1];
+          return lc > 0.f ? __builtin_amdgcn_exp2f(ml_s[2 * (cc * GP + h)] - M) : 0.f;
+        };
+#pragma unroll
+        for (int q = 0; q < PER; ++q) {
+          const int pv = pbase + q * 256;
+          const int h = (4 * pv) / D;
+          const int d = (4 * pv) % D;
+          const float M = head_s[2 * h];
           float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
-#pragma unroll 4
-          for (int cc = 0; cc < w.nc; ++cc) {
-            const float mc = load_coherent(a.part_ml + ((slot0 + cc) * GP + h) * 2);
-            const float lc = load_coherent(a.part_ml + ((slot0 + cc) * GP + h) * 2 + 1);
-            const float* pp = a.part_acc + ((slot0 + cc) * GP + h) * D + d;
-            const float4 pa = make_float4(load_coherent(pp), load_coherent(pp + 1),
-                                          load_coherent(pp + 2), load_coherent(pp + 3));
-            if (!(lc > 0.f)) continue;
-            const float Mn = fmaxf(M, mc);
-            const float so = __builtin_amdgcn_exp2f(M - Mn);  // 0 while M is -inf
-            const float sn = __builtin_amdgcn_exp2f(mc - Mn);
-            Ls = Ls * so + lc * sn;
-            o.x = o.x * so + pa.x * sn;
-            o.y = o.y * so + pa.y * sn;
-            o.z = o.z * so + pa.z * sn;
-            o.w = o.w * so + pa.w * sn;
-            M = Mn;
+          if (M != NEG_INF) {
+#pragma unroll 8
+            for (int cc = cg; cc < w.nc; cc += CG) {
+              const float wgt = weight(cc, h, M);
+              const float4 pa = load_coherent4(
+                  part_rsrc, static_cast<uint32_t>((((slot0 + cc) * GP + h) * D + d) * sizeof(float)));
+              o.x += wgt * pa.x;
+              o.y += wgt * pa.y;
+              o.z += wgt * pa.z;
+              o.w += wgt * pa.w;
+            }
           }
-          const float inv = Ls > 0.f ? 1.f / Ls : 0.f;
-          const int hq = g * G + hg * GP + h;
-          *reinterpret_cast<float4*>(a.out + (static_cast<int64_t>(b) * a.Hq + hq) * D + d) =
-              make_float4(o.x * inv, o.y * inv, o.z * inv, o.w * inv);
-          if (d == 0 && a.lse != nullptr)
-            a.lse[static_cast<int64_t>(b) * a.Hq + hq] =
-                Ls > 0.f ? (M + __builtin_log2f(Ls)) * 0.69314718055994531f : NEG_INF;
+          if constexpr (CG > 1) {
+            red_s[threadIdx.x] = o;
+          }
+          __syncthreads();
+          if (cg == 0 && hg * GP + h < G) {
+            if constexpr (CG > 1) {
+              for (int k = 1; k < CG; ++k) {
+                const float4 r = red_s[k * PAIRS + pbase];
+                o.x += r.x;
+                o.y += r.y;
+                o.z += r.z;
+                o.w += r.w;
+              }
+            }
+            const float Ls = head_s[2 * h + 1];
+            const float inv = Ls > 0.f ? 1.f / Ls : 0.f;
+            const int hq = g * G + hg * GP + h;
+            *reinterpret_cast<float4*>(a.out + (static_cast<int64_t>(b) * a.Hq + hq) * D + d) =
+                make_float4(o.x * inv, o.y * inv, o.z * inv, o.w * inv);
+            if (d == 0 && a.lse != nullptr)
+              a.lse[static_cast<int64_t>(b) * a.Hq + hq] =
+                  Ls > 0.f ? (M + __builtin_log2f(Ls)) * 0.69314718055994531f : NEG_INF;
+          }
+          __syncthreads();
         }
         if (threadIdx.x == 0) store_coherent_i(a.counters + grp, 0);  // ready for the next call
       }

@@ -14,6 +14,7 @@ constexpr int kWave = 64;
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((__vector_size__(16)));
 typedef _Float16 f16x8 __attribute__((__vector_size__(16)));
+typedef uint32_t u32x4 __attribute__((__vector_size__(16)));
 
 // ---- element types ------------------------------------------------------------
 // A 16-byte global load is the unit of every K/V/q access: 8 halves or 4 floats.
@@ -212,6 +213,23 @@ __device__ __forceinline__ void store_coherent_i(int32_t* p, int32_t v) {
 
 __device__ __forceinline__ float load_coherent(const float* p) {
   return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// 16-byte device-coherent accesses through a buffer resource (range-checked:
+// an offset past `bytes` reads zero and drops the write).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t coherent_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, static_cast<int>(bytes),
+                                           0x00020000);
+}
+
+constexpr int kCachePolicySc1 = 16;  // device scope
+
+__device__ __forceinline__ float4 load_coherent4(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
+  return __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, kCachePolicySc1));
+}
+
+__device__ __forceinline__ void store_coherent4(__amdgpu_buffer_rsrc_t r, uint32_t byte_off, float4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, byte_off, 0, kCachePolicySc1);
 }
 
 // Waits until every memory access this wavefront issued has completed.
