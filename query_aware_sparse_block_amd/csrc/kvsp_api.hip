@@ -24,10 +24,21 @@ constexpr int kMaxSummaryRow = 7168;   // Hkv * D: the score kernel stages it in
 #define KVSP_DECODE_MAX_WORKGROUPS 2048
 #endif
 constexpr int kDecodeTargetItems = KVSP_DECODE_TARGET_ITEMS;
-// The merge stages (m, l) of every chunk of a group in the kernel's LDS (the
-// 3 * GP * D floats of its wave-merge buffer): 2 * chunks * GP + 2 * GP must
-// fit, i.e. chunks <= 95 at D = 64.
+// The merge gives each chunk of a group one lane of a wavefront, and keeps a
+// weight per (chunk, head) plus (M, Lsum) per head in the kernel's LDS (the
+// 3 * GP * D floats of its wave-merge buffer): at most 64 chunks.
 constexpr int kDecodeMaxChunks = 64;
+// Heads per work item: the group's query heads padded to a power of two (at
+// most 16). With few (sequence, KV head) pairs the heads are split into
+// smaller groups, down to KVSP_DECODE_MIN_GP, until there are
+// KVSP_DECODE_SPLIT_GROUPS groups: each group then merges its own partials,
+// at the price of reading the KV head once per group.
+#ifndef KVSP_DECODE_SPLIT_GROUPS
+#define KVSP_DECODE_SPLIT_GROUPS 8
+#endif
+#ifndef KVSP_DECODE_MIN_GP
+#define KVSP_DECODE_MIN_GP 4
+#endif
 constexpr int kScoreTargetWorkgroups = 512;
 constexpr int kDecodeMaxWorkgroups = KVSP_DECODE_MAX_WORKGROUPS;
 
@@ -70,7 +81,7 @@ struct DecodeGeometry {
 DecodeGeometry decode_geometry(const kvsp_layout& l) {
   DecodeGeometry d;
   const int G = l.num_q_heads / l.num_kv_heads;
-  d.gp = decode_group_pad(G);
+  d.gp = decode_group_pad(l);
   d.n_head_groups = (G + d.gp - 1) / d.gp;
   d.max_chunks = decode_max_chunks(l);
   d.total_items = l.batch * l.num_kv_heads * d.n_head_groups * d.max_chunks;
@@ -147,12 +158,12 @@ kvsp_status run_decode(const kvsp_layout* layout, const kvsp_select_params* para
 
 }  // namespace
 
-int decode_group_pad(int G) {
-  if (G <= 1) return 1;
-  if (G <= 2) return 2;
-  if (G <= 4) return 4;
-  if (G <= 8) return 8;
-  return 16;
+int decode_group_pad(const kvsp_layout& l) {
+  const int G = l.num_q_heads / l.num_kv_heads;
+  int gp = G <= 1 ? 1 : G <= 2 ? 2 : G <= 4 ? 4 : G <= 8 ? 8 : 16;
+  const int64_t pairs = static_cast<int64_t>(l.batch) * l.num_kv_heads;
+  while (gp > KVSP_DECODE_MIN_GP && pairs * ((G + gp - 1) / gp) < KVSP_DECODE_SPLIT_GROUPS) gp /= 2;
+  return gp;
 }
 
 // Chunks per (sequence, KV head, head group): enough workgroup items to
@@ -160,7 +171,7 @@ int decode_group_pad(int G) {
 // possible context has chunk quanta.
 int decode_max_chunks(const kvsp_layout& l) {
   const int G = l.num_q_heads / l.num_kv_heads;
-  const int gp = decode_group_pad(G);
+  const int gp = decode_group_pad(l);
   const int64_t groups = static_cast<int64_t>(l.batch) * l.num_kv_heads * ((G + gp - 1) / gp);
   const int quantum = decode_chunk_quantum(l.dtype, l.head_dim);
   const int64_t max_sub = (static_cast<int64_t>(l.max_blocks_per_seq) * l.block_size + quantum - 1) / quantum;

@@ -44,6 +44,11 @@ namespace kvsp {
 #ifndef KVSP_PIPELINE
 #define KVSP_PIPELINE 0
 #endif
+// Chunks per output whose accumulators the merging workgroup requests before
+// it has the merge weights.
+#ifndef KVSP_MERGE_PRE
+#define KVSP_MERGE_PRE 16
+#endif
 // 1: items are numbered chunk-major (see the item loop of attend_kernel).
 #ifndef KVSP_CHUNK_MAJOR
 #define KVSP_CHUNK_MAJOR 1
@@ -454,62 +459,91 @@ __global__ __launch_bounds__(256) void attend_kernel(DecodeArgs a) {
       if (last_flag) {
         // Every chunk of this group is published: merge by log-sum-exp,
         // reading the partials at the device coherence point.
-        //   1. (m, l) of every (chunk, head) into LDS in one round trip;
-        //   2. per head M = max m and Lsum = sum l 2^(m - M);
-        //   3. out = sum acc 2^(m - M) / Lsum, the chunks split over CG
-        //      thread groups (16-byte loads), folded through LDS.
+        //   1. the first MERGE_PRE chunks' accumulators of every output this
+        //      thread owns are requested at once (16-byte loads);
+        //   2. meanwhile each wave takes heads h = wave, wave + 4, ...: lane
+        //      cc reads (m, l) of chunk cc, and wave reductions give
+        //      M = max m, the weights 2^(m - M) (0 for empty chunks, kept in
+        //      LDS) and Lsum = sum l 2^(m - M);
+        //   3. out = sum weight * acc / Lsum, the chunks split over CG thread
+        //      groups, folded through LDS.
         // The merge reuses the LDS of the main loop (xacc and p_lds).
         const int64_t slot0 = static_cast<int64_t>(grp) * a.max_chunks;
-        float* ml_s = &xacc[0][0];                    // [nc][GP][2]
-        float* head_s = ml_s + 2 * a.max_chunks * GP;  // [GP][2]: M, Lsum
+        float* wt_s = &xacc[0][0];                   // [max_chunks][GP] weights
+        float* head_s = wt_s + a.max_chunks * GP;    // [GP][2]: M, Lsum
         float4* red_s = reinterpret_cast<float4*>(&p_lds[0][0]);
         constexpr int PAIRS = GP * D / 4;                     // (head, 4 channels) outputs
         constexpr int CG = PAIRS >= 256 ? 1 : 256 / PAIRS;    // chunk groups per output
         constexpr int PER = PAIRS >= 256 ? PAIRS / 256 : 1;   // outputs per thread
+        constexpr int PRE = KVSP_MERGE_PRE;
         const int cg = threadIdx.x / (PAIRS >= 256 ? 256 : PAIRS);
         const int pbase = threadIdx.x % (PAIRS >= 256 ? 256 : PAIRS);
-        for (int i = threadIdx.x; i < w.nc * GP; i += blockDim.x) {
-          ml_s[2 * i] = load_coherent(a.part_ml + (slot0 * GP + i) * 2);
-          ml_s[2 * i + 1] = load_coherent(a.part_ml + (slot0 * GP + i) * 2 + 1);
-        }
-        __syncthreads();
-        if (threadIdx.x < GP) {
-          const int h = threadIdx.x;
-          float M = NEG_INF;
-          for (int cc = 0; cc < w.nc; ++cc)
-            if (ml_s[2 * (cc * GP + h) + 1] > 0.f) M = fmaxf(M, ml_s[2 * (cc * GP + h)]);
-          float Ls = 0.f;
-          if (M != NEG_INF)
-            for (int cc = 0; cc < w.nc; ++cc) {
-              const float lc = ml_s[2 * (cc * GP + h) + 1];
-              if (lc > 0.f) Ls += lc * __builtin_amdgcn_exp2f(ml_s[2 * (cc * GP + h)] - M);
-            }
-          head_s[2 * h] = M;
-          head_s[2 * h + 1] = Ls;
-        }
-        __syncthreads();
-        auto weight = [&](int cc, int h, float M) {
-          const float lc = ml_s[2 * (cc * GP + h) + 1];
-          return lc > 0.f ? __builtin_amdgcn_exp2f(ml_s[2 * (cc * GP + h)] - M) : 0.f;
+        auto acc_off = [&](int cc, int pv) {
+          const int h = (4 * pv) / D;
+          const int d = (4 * pv) % D;
+          return static_cast<uint32_t>((((slot0 + cc) * GP + h) * D + d) * sizeof(float));
         };
+        float4 pre[PER][PRE];
+#pragma unroll
+        for (int q = 0; q < PER; ++q)
+#pragma unroll
+          for (int i = 0; i < PRE; ++i) {
+            const int cc = cg + i * CG;
+            pre[q][i] = cc < w.nc ? load_coherent4(part_rsrc, acc_off(cc, pbase + q * 256))
+                                  : make_float4(0.f, 0.f, 0.f, 0.f);
+          }
+        constexpr int HPW = (GP + kDecodeWaves - 1) / kDecodeWaves;  // heads per wave
+        float mv[HPW], lv[HPW];
+#pragma unroll
+        for (int i = 0; i < HPW; ++i) {
+          const int h = wave + i * kDecodeWaves;
+          mv[i] = NEG_INF;
+          lv[i] = 0.f;
+          if (h < GP && lane < w.nc) {
+            mv[i] = load_coherent(a.part_ml + ((slot0 + lane) * GP + h) * 2);
+            lv[i] = load_coherent(a.part_ml + ((slot0 + lane) * GP + h) * 2 + 1);
+          }
+        }
+#pragma unroll
+        for (int i = 0; i < HPW; ++i) {
+          const int h = wave + i * kDecodeWaves;
+          if (h < GP) {  // wave-uniform
+            const float M = group_max<kWave>(lv[i] > 0.f ? mv[i] : NEG_INF);
+            const float wt = (lv[i] > 0.f && M != NEG_INF) ? __builtin_amdgcn_exp2f(mv[i] - M) : 0.f;
+            const float Ls = group_sum<kWave>(lv[i] * wt);
+            if (lane < w.nc) wt_s[lane * GP + h] = wt;
+            if (lane == 0) {
+              head_s[2 * h] = M;
+              head_s[2 * h + 1] = Ls;
+            }
+          }
+        }
+        __syncthreads();
 #pragma unroll
         for (int q = 0; q < PER; ++q) {
           const int pv = pbase + q * 256;
           const int h = (4 * pv) / D;
           const int d = (4 * pv) % D;
-          const float M = head_s[2 * h];
           float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
-          if (M != NEG_INF) {
-#pragma unroll 8
-            for (int cc = cg; cc < w.nc; cc += CG) {
-              const float wgt = weight(cc, h, M);
-              const float4 pa = load_coherent4(
-                  part_rsrc, static_cast<uint32_t>((((slot0 + cc) * GP + h) * D + d) * sizeof(float)));
-              o.x += wgt * pa.x;
-              o.y += wgt * pa.y;
-              o.z += wgt * pa.z;
-              o.w += wgt * pa.w;
+#pragma unroll
+          for (int i = 0; i < PRE; ++i) {
+            const int cc = cg + i * CG;
+            if (cc < w.nc) {
+              const float wgt = wt_s[cc * GP + h];
+              o.x += wgt * pre[q][i].x;
+              o.y += wgt * pre[q][i].y;
+              o.z += wgt * pre[q][i].z;
+              o.w += wgt * pre[q][i].w;
             }
+          }
+#pragma unroll 8
+          for (int cc = cg + PRE * CG; cc < w.nc; cc += CG) {
+            const float wgt = wt_s[cc * GP + h];
+            const float4 pa = load_coherent4(part_rsrc, acc_off(cc, pv));
+            o.x += wgt * pa.x;
+            o.y += wgt * pa.y;
+            o.z += wgt * pa.z;
+            o.w += wgt * pa.w;
           }
           if constexpr (CG > 1) {
             red_s[threadIdx.x] = o;
@@ -525,6 +559,7 @@ __global__ __launch_bounds__(256) void attend_kernel(DecodeArgs a) {
                 o.w += r.w;
               }
             }
+            const float M = head_s[2 * h];
             const float Ls = head_s[2 * h + 1];
             const float inv = Ls > 0.f ? 1.f / Ls : 0.f;
             const int hq = g * G + hg * GP + h;

@@ -174,6 +174,18 @@ __device__ __forceinline__ F group_sum(F v) {
   return v;
 }
 
+// Maximum over aligned groups of LANES consecutive lanes (same butterfly).
+template <int LANES>
+__device__ __forceinline__ float group_max(float v) {
+  if constexpr (LANES >= 2) v = fmaxf(v, dpp_f<0xB1>(v));
+  if constexpr (LANES >= 4) v = fmaxf(v, dpp_f<0x4E>(v));
+  if constexpr (LANES >= 8) v = fmaxf(v, dpp_f<0x141>(v));
+  if constexpr (LANES >= 16) v = fmaxf(v, dpp_f<0x140>(v));
+  if constexpr (LANES >= 32) v = fmaxf(v, xor16(v));
+  if constexpr (LANES >= 64) v = fmaxf(v, xor32(v));
+  return v;
+}
+
 __device__ __forceinline__ double wave_sum(double v) { return group_sum<kWave>(v); }
 
 // Inclusive prefix sum over the wave (DPP row shifts and row broadcasts).

@@ -81,7 +81,7 @@ hipError_t launch_decode(const DecodeArgs& a, int dtype, int group_pad, int num_
                          hipStream_t stream);
 
 // Host-side sizing shared by the entry points and kvsp_workspace_bytes.
-int decode_group_pad(int G);        // GP: heads per work item (1, 2, 4, 8 or 16)
+int decode_group_pad(const kvsp_layout& l);  // GP: heads per work item (1, 2, 4, 8 or 16)
 int decode_max_chunks(const kvsp_layout& l);
 int decode_chunk_quantum(int dtype, int D);  // tokens per chunk unit
 int score_group_lanes(int Hkv, int D);       // lanes that share one summary row

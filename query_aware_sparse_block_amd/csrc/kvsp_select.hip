@@ -50,9 +50,11 @@ __device__ int score_blocks(const ScoreArgs& a, double* qbar, int b) {
     phys_lds[i] = first + i < a.max_blocks ? a.block_table[trow + first + i] : 0;
 
   // qbar[g][d] = sum over the group's query heads, ascending, in double
-  // (exact for 16-bit inputs). One 16-byte vector of q per head and thread.
+  // (exact for 16-bit inputs). One 16-byte vector of q per head and thread;
+  // the heads are loaded 16 at a time so a group costs one round trip.
   const int G = a.Hq / a.Hkv;
   constexpr int EPV = T::kPerVec;
+  constexpr int QB = 16;
   const char* qb = static_cast<const char*>(a.q) + static_cast<int64_t>(b) * a.Hq * a.D * T::kBytes;
   for (int v = threadIdx.x; v < row / EPV; v += blockDim.x) {
     const int g = (v * EPV) / a.D;
@@ -60,11 +62,21 @@ __device__ int score_blocks(const ScoreArgs& a, double* qbar, int b) {
     double s[EPV];
 #pragma unroll
     for (int e = 0; e < EPV; ++e) s[e] = 0.0;
-    for (int h = 0; h < G; ++h) {
-      float f[EPV];
-      T::widen(load16(qb + (static_cast<int64_t>(g * G + h) * a.D + d0) * T::kBytes), f);
+    for (int h0 = 0; h0 < G; h0 += QB) {
+      uint4 qv[QB];
 #pragma unroll
-      for (int e = 0; e < EPV; ++e) s[e] += static_cast<double>(f[e]);
+      for (int u = 0; u < QB; ++u)
+        qv[u] = h0 + u < G ? load16(qb + (static_cast<int64_t>(g * G + h0 + u) * a.D + d0) * T::kBytes)
+                           : make_uint4(0, 0, 0, 0);
+#pragma unroll
+      for (int u = 0; u < QB; ++u) {
+        if (h0 + u < G) {
+          float f[EPV];
+          T::widen(qv[u], f);
+#pragma unroll
+          for (int e = 0; e < EPV; ++e) s[e] += static_cast<double>(f[e]);
+        }
+      }
     }
 #pragma unroll
     for (int e = 0; e < EPV; ++e) qbar[v * EPV + e] = s[e];
@@ -215,41 +227,50 @@ __device__ uint32_t block_excl_scan(uint32_t v, uint32_t* tmp, uint32_t& total) 
 }
 
 struct TopkShared {
-  uint32_t hist[256];
+  uint32_t hist[4][256];  // one histogram per radix pass, cleared together
   uint32_t scan_tmp[2 * (16 + 1)];
-  uint32_t bcast[2];
 };
 
 // Top-k, spans and the dense flag of sequence b, by a workgroup of WAVES
-// wavefronts (every thread calls it). `kept` holds max_blocks bytes of LDS.
-// COHERENT reads scores written by other workgroups of the same launch.
+// wavefronts (every thread calls it). COHERENT reads scores written by other
+// workgroups of the same launch.
+//
+// Thread t owns the R consecutive candidates t*R .. t*R+R-1 and also reads
+// the scores of the candidate just before and just after them, so it can
+// decide on its own whether its first and last candidates open or close a
+// run. Each radix pass costs one barrier: the four histograms are cleared
+// up front and every wavefront finds the pass's digit by itself. When every
+// key equal to the threshold is kept (no tie is cut), one block-wide scan of
+// (kept, run starts) places the selected ids and the spans; a cut tie adds
+// one scan that ranks the equal keys by index.
 template <int WAVES, bool COHERENT>
-__device__ void select_sequence(const TopkArgs& a, int b, TopkShared& sh, uint8_t* kept) {
+__device__ void select_sequence(const TopkArgs& a, int b, TopkShared& sh) {
   constexpr int kTopkThreads = WAVES * kWave;
-  uint32_t* hist = sh.hist;
-  uint32_t* scan_tmp = sh.scan_tmp;
-  uint32_t* bcast = sh.bcast;
   const int t = threadIdx.x;
   const int lane = t % kWave;
   const SelectArgs sel{a.top_k, a.keep_num, a.keep_den, a.keep_floor, a.recent_window,
                        a.gamma_num, a.gamma_den};
   // Candidates are assigned from the row capacity, so the score loads do not
   // wait for the context length.
-  const int R = (a.max_blocks + kTopkThreads - 1) / kTopkThreads;  // consecutive per thread
+  const int R = (a.max_blocks + kTopkThreads - 1) / kTopkThreads;
   const int jbase = t * R;
   const int64_t row = static_cast<int64_t>(b) * a.max_blocks;
+  auto score_at = [&](int j) -> float {
+    if constexpr (COHERENT) {
+      return load_coherent(a.scores + row + j);
+    } else {
+      return a.scores[row + j];
+    }
+  };
   float raw[kTopkMaxPerThread];
 #pragma unroll
   for (int r = 0; r < kTopkMaxPerThread; ++r) {
     const int j = jbase + r;
-    if constexpr (COHERENT) {
-      raw[r] = (r < R && j < a.max_blocks) ? load_coherent(a.scores + row + j) : 0.f;
-    } else {
-      raw[r] = (r < R && j < a.max_blocks) ? a.scores[row + j] : 0.f;
-    }
+    raw[r] = (r < R && j < a.max_blocks) ? score_at(j) : 0.f;
   }
-  const int L = a.context_lens[b];
-  const SeqPlan p = plan_sequence(L, a.P, sel);
+  const float raw_prev = (jbase >= 1 && jbase - 1 < a.max_blocks) ? score_at(jbase - 1) : 0.f;
+  const float raw_next = jbase + R < a.max_blocks ? score_at(jbase + R) : 0.f;
+  const SeqPlan p = plan_sequence(a.context_lens[b], a.P, sel);
   const int C = p.C;
   const int k = p.k;
 
@@ -259,125 +280,128 @@ __device__ void select_sequence(const TopkArgs& a, int b, TopkShared& sh, uint8_
     const int j = jbase + r;
     key[r] = (r < R && j < C) ? order_key(raw[r]) : 0u;
   }
+  const bool has_prev = jbase >= 1 && jbase - 1 < C;
+  const bool has_next = jbase + R < C;
+  const uint32_t key_prev = has_prev ? order_key(raw_prev) : 0u;
+  const uint32_t key_next = has_next ? order_key(raw_next) : 0u;
 
-  // Radix select of the k-th largest key (only when 0 < k < C).
+  // Radix select of the k-th largest key T (only when 0 < k < C): after the
+  // last pass, `take_equal` of the `eq_total` keys equal to T are kept.
   uint32_t thresh = 0;
-  int take_equal = 0;
+  int take_equal = 0, eq_total = 0;
   const bool partial = k > 0 && k < C;
   if (partial) {
+    for (int i = t; i < 4 * 256; i += kTopkThreads) (&sh.hist[0][0])[i] = 0;
+    __syncthreads();
     uint32_t prefix = 0, mask = 0;
     int krem = k;
     for (int pass = 0; pass < 4; ++pass) {
       const int shift = 24 - 8 * pass;
-      for (int i = t; i < 256; i += kTopkThreads) hist[i] = 0;
-      __syncthreads();
+      uint32_t* hist = sh.hist[pass];
 #pragma unroll
       for (int r = 0; r < kTopkMaxPerThread; ++r) {
         const int j = jbase + r;
         if (r < R && j < C && (key[r] & mask) == prefix) atomicAdd(&hist[(key[r] >> shift) & 255u], 1u);
       }
       __syncthreads();
-      if (t < kWave) {
-        // lane owns digits 4*lane .. 4*lane+3; count keys in digits above
-        uint32_t h[4];
+      // Every wavefront: lane owns digits 4*lane .. 4*lane+3; the digit is
+      // the one where the count of keys in higher digits first reaches krem.
+      uint32_t h[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) h[i] = hist[4 * lane + i];
-        const uint32_t local = h[0] + h[1] + h[2] + h[3];
-        const uint32_t incl = wave_incl_scan(local);
-        const uint32_t total = __builtin_amdgcn_readlane(incl, kWave - 1);
-        uint32_t above = total - incl;  // keys in digits owned by higher lanes
-        for (int i = 3; i >= 0; --i) {
-          if (above < static_cast<uint32_t>(krem) && static_cast<uint32_t>(krem) <= above + h[i]) {
-            bcast[0] = 4u * lane + i;
-            bcast[1] = static_cast<uint32_t>(krem) - above;
-          }
-          above += h[i];
+      for (int i = 0; i < 4; ++i) h[i] = hist[4 * lane + i];
+      const uint32_t incl = wave_incl_scan(h[0] + h[1] + h[2] + h[3]);
+      uint32_t above = __builtin_amdgcn_readlane(incl, kWave - 1) - incl;
+      bool found = false;
+      uint32_t d_sel = 0, k_sel = 0, n_sel = 0;
+#pragma unroll
+      for (int i = 3; i >= 0; --i) {
+        if (above < static_cast<uint32_t>(krem) && static_cast<uint32_t>(krem) <= above + h[i]) {
+          found = true;
+          d_sel = 4u * lane + i;
+          k_sel = static_cast<uint32_t>(krem) - above;
+          n_sel = h[i];
         }
+        above += h[i];
       }
-      __syncthreads();
-      const uint32_t digit = bcast[0];
-      krem = static_cast<int>(bcast[1]);
+      // exactly one lane holds the digit (krem lies in (0, keys with this prefix])
+      const int src = __builtin_ctzll(__ballot(found) | (1ull << 63));
+      const uint32_t digit = __builtin_amdgcn_readlane(d_sel, src);
+      krem = static_cast<int>(__builtin_amdgcn_readlane(k_sel, src));
+      eq_total = static_cast<int>(__builtin_amdgcn_readlane(n_sel, src));
       prefix |= digit << shift;
       mask |= 0xFFu << shift;
-      __syncthreads();
     }
     thresh = prefix;
     take_equal = krem;
   }
 
-  // Kept flags in index order.
+  // Equal keys are kept in index order: rank them when a tie is cut.
+  const bool cut_tie = partial && take_equal < eq_total;  // uniform
   uint32_t n_eq = 0;
 #pragma unroll
   for (int r = 0; r < kTopkMaxPerThread; ++r) {
     const int j = jbase + r;
-    if (partial && r < R && j < C && key[r] == thresh) ++n_eq;
+    if (r < R && j < C && key[r] == thresh) ++n_eq;
   }
-  uint32_t eq_total;
-  uint32_t eq_before = block_excl_scan<WAVES>(n_eq, scan_tmp, eq_total);
-  uint32_t keep_bits = 0, n_keep = 0;
-#pragma unroll
-  for (int r = 0; r < kTopkMaxPerThread; ++r) {
-    const int j = jbase + r;
-    if (!(r < R && j < C)) continue;
-    bool keep;
-    if (k >= C) {
-      keep = true;
-    } else if (k == 0) {
-      keep = false;
-    } else if (key[r] > thresh) {
-      keep = true;
-    } else if (key[r] == thresh) {
-      keep = eq_before < static_cast<uint32_t>(take_equal);
-      ++eq_before;
-    } else {
-      keep = false;
-    }
-    if (keep) {
-      keep_bits |= 1u << r;
-      ++n_keep;
-    }
+  uint32_t eq_before = 0;
+  if (cut_tie) {
+    uint32_t eq_all;
+    eq_before = block_excl_scan<WAVES>(n_eq, sh.scan_tmp, eq_all);
   }
-  uint32_t keep_total;
-  const uint32_t pos0 = block_excl_scan<WAVES>(n_keep, scan_tmp, keep_total);
-  uint32_t pos = pos0;
-#pragma unroll
-  for (int r = 0; r < kTopkMaxPerThread; ++r) {
-    const int j = jbase + r;
-    if (r < R && j < C) {
-      const bool keep = (keep_bits >> r) & 1u;
-      kept[j] = keep ? 1 : 0;
-      if (keep) a.selected[row + pos++] = j;
-    }
-  }
-  __syncthreads();
+  // Kept? for a candidate with key `kk` whose rank among the equal keys is eq_rank.
+  auto kept = [&](uint32_t kk, uint32_t eq_rank) -> bool {
+    if (!partial) return k >= C;
+    if (kk != thresh) return kk > thresh;
+    return !cut_tie || eq_rank < static_cast<uint32_t>(take_equal);
+  };
+  const bool keep_prev = has_prev && kept(key_prev, eq_before - 1u);
+  const bool keep_next = has_next && kept(key_next, eq_before + n_eq);
 
-  // Span boundaries: a run starts where a kept block follows a dropped one
-  // and ends where a dropped one (or the candidate range end) follows.
-  const bool window = p.n > C;
-  uint32_t n_start = 0, n_end = 0;
+  uint32_t keep_bits = 0, n_keep = 0, n_start = 0;
+  {
+    uint32_t eq_rank = eq_before;
+    bool left = keep_prev;  // kept(j - 1)
 #pragma unroll
-  for (int r = 0; r < kTopkMaxPerThread; ++r) {
-    const int j = jbase + r;
-    if (r < R && j < C && ((keep_bits >> r) & 1u)) {
-      if (j == 0 || !kept[j - 1]) ++n_start;
-      if (j == C - 1 || !kept[j + 1]) ++n_end;
+    for (int r = 0; r < kTopkMaxPerThread; ++r) {
+      const int j = jbase + r;
+      if (!(r < R && j < C)) continue;
+      const bool kp = kept(key[r], eq_rank);
+      if (key[r] == thresh) ++eq_rank;
+      if (kp) {
+        keep_bits |= 1u << r;
+        ++n_keep;
+        if (!left) ++n_start;
+      }
+      left = kp;
     }
   }
-  uint32_t se_total;
-  const uint32_t se_before = block_excl_scan<WAVES>((n_start << 16) | n_end, scan_tmp, se_total);
-  uint32_t s_idx = se_before >> 16, e_idx = se_before & 0xFFFFu;
+  // One scan places both: kept ids before this thread (high half) and runs
+  // started before it (low half); C <= 16 * threads keeps each below 2^16.
+  uint32_t totals;
+  const uint32_t before = block_excl_scan<WAVES>((n_keep << 16) | n_start, sh.scan_tmp, totals);
+  uint32_t pos = before >> 16;
+  uint32_t s_idx = before & 0xFFFFu;
+  // A run still open at this thread's first candidate has its end counted here.
+  const bool first_kept = (keep_bits & 1u) != 0;
+  uint32_t e_idx = s_idx - ((keep_prev && first_kept) ? 1u : 0u);
+  const bool window = p.n > C;
   int32_t* sp = a.spans + row * 2 + static_cast<int64_t>(b) * 2;  // [B][max_blocks+1][2]
 #pragma unroll
   for (int r = 0; r < kTopkMaxPerThread; ++r) {
     const int j = jbase + r;
-    if (r < R && j < C && ((keep_bits >> r) & 1u)) {
-      if (j == 0 || !kept[j - 1]) sp[2 * s_idx++] = j;
-      if (j == C - 1 || !kept[j + 1]) sp[2 * e_idx++ + 1] = (j == C - 1 && window) ? p.n : j + 1;
-    }
+    if (!(r < R && j < C) || !((keep_bits >> r) & 1u)) continue;
+    const bool left = r == 0 ? keep_prev : ((keep_bits >> (r - 1)) & 1u) != 0;
+    const bool right = r == R - 1 ? keep_next : ((keep_bits >> (r + 1)) & 1u) != 0;
+    a.selected[row + pos++] = j;
+    if (!left) sp[2 * s_idx++] = j;
+    if (!right) sp[2 * e_idx++ + 1] = (j == C - 1 && window) ? p.n : j + 1;
   }
-  if (t == 0) {
-    const int sel_spans = static_cast<int>(se_total >> 16);
-    const bool joined = C > 0 && k > 0 && kept[C - 1];
+  // The thread holding candidate C - 1 knows whether the window joins the
+  // last selected span; it writes the counts.
+  const int writer = C > 0 ? (C - 1) / R : 0;
+  if (t == writer) {
+    const int sel_spans = static_cast<int>(totals & 0xFFFFu);
+    const bool joined = C > 0 && ((keep_bits >> (C - 1 - jbase)) & 1u) != 0;
     int nsp = sel_spans;
     if (window && !joined) {
       sp[2 * nsp] = C;
@@ -394,14 +418,12 @@ __device__ void select_sequence(const TopkArgs& a, int b, TopkShared& sh, uint8_
 template <int WAVES>
 __global__ __launch_bounds__(WAVES * kWave) void topk_kernel(TopkArgs a) {
   __shared__ TopkShared sh;
-  extern __shared__ uint8_t kept[];  // [max_blocks] 0/1 per candidate
-  select_sequence<WAVES, false>(a, blockIdx.x, sh, kept);
+  select_sequence<WAVES, false>(a, blockIdx.x, sh);
 }
 
 template <int WAVES>
 static hipError_t launch_topk_w(const TopkArgs& a, hipStream_t stream) {
-  const size_t lds = static_cast<size_t>((a.max_blocks + 3) / 4 * 4);
-  hipLaunchKernelGGL((topk_kernel<WAVES>), dim3(a.B), dim3(WAVES * kWave), lds, stream, a);
+  hipLaunchKernelGGL((topk_kernel<WAVES>), dim3(a.B), dim3(WAVES * kWave), 0, stream, a);
   return hipGetLastError();
 }
 
@@ -430,8 +452,7 @@ __global__ __launch_bounds__(256) void score_select_kernel(ScoreArgs sa, TopkArg
   __syncthreads();
   if (!is_last) return;
   TopkShared& sh = *reinterpret_cast<TopkShared*>(lds);
-  uint8_t* kept = reinterpret_cast<uint8_t*>(lds) + sizeof(TopkShared);
-  select_sequence<4, true>(ta, b, sh, kept);
+  select_sequence<4, true>(ta, b, sh);
   if (threadIdx.x == 0) store_coherent_i(counters + b, 0);
 }
 
@@ -443,7 +464,7 @@ static hipError_t launch_fused_v(const ScoreArgs& sa, const TopkArgs& ta, int32_
   const int per_wg = 4 * sa.blocks_per_wave;
   dim3 grid((sa.max_blocks + per_wg - 1) / per_wg, sa.B);
   const size_t score_lds = static_cast<size_t>(sa.Hkv) * sa.D * sizeof(double) + per_wg * sizeof(int32_t);
-  const size_t topk_lds = sizeof(TopkShared) + static_cast<size_t>(sa.max_blocks);
+  const size_t topk_lds = sizeof(TopkShared);
   const size_t lds = (score_lds > topk_lds ? score_lds : topk_lds + 7) / 8 * 8;
   hipLaunchKernelGGL((score_select_kernel<T, LG, VPL>), grid, dim3(256), lds, stream, sa, ta,
                      counters);

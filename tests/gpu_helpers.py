@@ -9,6 +9,8 @@ Bars (written here once, used by every parity test):
     choice is accepted; the GPU's set must hold every block above the band,
     none below it, and exactly k blocks. Where the sets differ, outputs are
     compared with the oracle recomputed on the GPU's set;
+  * selection against the GPU's own float32 scores: exactly their k largest,
+    equal scores (+0 and -0 alike) taken in ascending block order;
   * spans, counts and the dense flag: exact (spans of the GPU's own set);
   * outputs: max-abs error <= 2e-3 for fp16/bf16 caches and <= 1e-5 for fp32
     caches (float32 accumulation); lse within 1e-4.
@@ -77,6 +79,11 @@ def check_selection(case, r_or, gpu, b):
     sel_g = gpu["selected"][b, :k].astype(np.int64)
     sel_o = r_or["sel"][b, :k].astype(np.int64)
     assert np.all(np.diff(sel_g) > 0) and (k == 0 or (sel_g[0] >= 0 and sel_g[-1] < C))
+    # the Top-k rule on the GPU's own scores: a stable descending sort keeps
+    # equal scores in index order, so its first k are the lowest-index ties
+    own = gpu["scores"][b, :C].astype(np.float64)
+    expect = np.sort(np.argsort(-own, kind="stable")[:k])
+    assert np.array_equal(sel_g, expect), f"b={b}: not the k best of its own scores"
     if not np.array_equal(sel_g, sel_o):
         score = r_or["scores"][b, :C]
         s_k = np.sort(score)[::-1][k - 1]

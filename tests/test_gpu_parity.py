@@ -153,3 +153,52 @@ def test_long_block_table_uses_two_kernel_selection():
     case = wl.make_case("long-table", seed=66, B=1, Hq=2, Hkv=1, D=64, P=16, dtype="fp16",
                         ctx_lens=[70400], top_k=12, keep_floor=1, recent_window=40)
     H.full_parity(case)
+
+
+def _repeat_blocks(case, period):
+    """Every sequence's logical block j reads physical block table[j % period]:
+    blocks with equal j % period have bit-identical summaries and scores."""
+    bt = case.block_table.copy()
+    for b in range(case.B):
+        bt[b] = bt[b, np.arange(bt.shape[1]) % period]
+    return wl.Case(**{**case.__dict__, "name": case.name + "-repeat", "block_table": bt})
+
+
+@pytest.mark.parametrize("period,top_k", [(5, 7), (3, 1), (7, 30)])
+def test_exact_ties_cut_by_top_k(period, top_k):
+    # repeated summaries make groups of exactly equal scores; top_k cuts
+    # through one of them, which the lowest block indices must fill
+    base = wl.make_case("ties", seed=67, B=3, Hq=8, Hkv=2, D=64, P=16, dtype="bf16",
+                        ctx_lens=[1600, 1111, 700], shuffle=True, num_phys=400, top_k=top_k,
+                        keep_floor=1, recent_window=48)
+    case = _repeat_blocks(base, period)
+    gpu, r_or = H.full_parity(case)
+    for b in range(case.B):
+        C = int(r_or["plan"][b][1])
+        k = int(r_or["plan"][b][3])
+        assert np.array_equal(gpu["selected"][b, :k], r_or["sel"][b, :k])
+        vals = gpu["scores"][b, :C]
+        assert len(np.unique(vals)) <= period
+
+
+def test_exact_ties_on_the_two_kernel_path():
+    base = wl.make_case("ties-long", seed=68, B=1, Hq=2, Hkv=1, D=64, P=16, dtype="fp16",
+                        ctx_lens=[70400], top_k=700, keep_floor=1, recent_window=40)
+    case = _repeat_blocks(base, 11)
+    gpu, r_or = H.full_parity(case)
+    assert np.array_equal(gpu["selected"][0, :700], r_or["sel"][0, :700])
+
+
+@pytest.mark.parametrize("max_blocks_pad", [0, 5000])
+def test_zero_queries_tie_every_block(max_blocks_pad):
+    # q = 0: every score is +0 or -0, all equal; the k lowest blocks are kept
+    # and the output is the plain mean of the attended values
+    base = wl.make_case("zero-q", seed=69, B=2, Hq=4, Hkv=2, D=64, P=16, dtype="fp16",
+                        ctx_lens=[900, 333], keep_num=1, keep_den=3, keep_floor=1,
+                        recent_window=20,
+                        max_blocks=(max_blocks_pad or None), num_phys=(max_blocks_pad * 2 or None))
+    case = wl.Case(**{**base.__dict__, "q": np.zeros_like(base.q)})
+    gpu, r_or = H.full_parity(case)
+    for b in range(case.B):
+        k = int(r_or["plan"][b][3])
+        assert np.array_equal(gpu["selected"][b, :k], np.arange(k))
