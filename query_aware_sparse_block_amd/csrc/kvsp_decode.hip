@@ -40,9 +40,15 @@ namespace kvsp {
 #ifndef KVSP_SUB_TILE_BYTES
 #define KVSP_SUB_TILE_BYTES 4096
 #endif
-// 1: each wavefront loads sub-tile i+1 while it computes sub-tile i.
-#ifndef KVSP_PIPELINE
-#define KVSP_PIPELINE 0
+// Work items of at most this many heads load sub-tile i+1 while they compute
+// sub-tile i, and read K/V with non-temporal loads. Measured: both help
+// one-head items (little compute per byte, registers to spare) and cost
+// time on GQA items, whose head groups may share a KV head through the caches.
+#ifndef KVSP_PIPELINE_MAX_GP
+#define KVSP_PIPELINE_MAX_GP 1
+#endif
+#ifndef KVSP_STREAM_MAX_GP
+#define KVSP_STREAM_MAX_GP 1
 #endif
 // Chunks per output whose accumulators the merging workgroup requests before
 // it has the merge weights.
@@ -242,6 +248,13 @@ __global__ __launch_bounds__(256) void attend_kernel(DecodeArgs a) {
     const uint32_t k_lane_off = static_cast<uint32_t>(hl * D * E + (lane / 16) * 16);
     const uint32_t v_lane_off = static_cast<uint32_t>((rg * D + col) * E);
 
+    auto kv_load = [](const char* p) {
+      if constexpr (GP <= KVSP_STREAM_MAX_GP) {
+        return load16_stream(p);
+      } else {
+        return load16(p);
+      }
+    };
     // Enqueue the K and V loads of the sub-tile starting at attended token i0.
     // Tile bases are wave-uniform, so every load is base + lane offset.
     auto issue = [&](int i0, SubTile& st) {
@@ -266,13 +279,13 @@ __global__ __launch_bounds__(256) void attend_kernel(DecodeArgs a) {
       for (int t = 0; t < S::TILES; ++t) {
         const char* tk = kbase + tile_byte0[t];
 #pragma unroll
-        for (int s = 0; s < S::KLD; ++s) st.kv[t][s] = load16(tk + k_lane_off + 64 * s);
+        for (int s = 0; s < S::KLD; ++s) st.kv[t][s] = kv_load(tk + k_lane_off + 64 * s);
       }
 #pragma unroll
       for (int r = 0; r < S::VLD; ++r) {
         const int t = (r * S::RPL) / 16;
         const char* tv = vbase + tile_byte0[t] + (r * S::RPL - 16 * t) * D * E;
-        st.vv[r] = load16(tv + v_lane_off);
+        st.vv[r] = kv_load(tv + v_lane_off);
       }
     };
 
@@ -344,7 +357,7 @@ __global__ __launch_bounds__(256) void attend_kernel(DecodeArgs a) {
     SubTile buf0, buf1;
     int i0 = first_tok;
     if (i0 < end) issue(i0, buf0);
-    if constexpr (KVSP_PIPELINE) {
+    if constexpr (GP <= KVSP_PIPELINE_MAX_GP) {
       while (i0 < end) {
         int i1 = i0 + STRIDE;
         if (i1 < end) issue(i1, buf1);

@@ -70,6 +70,12 @@ __device__ __forceinline__ uint4 load16(const void* p) {
   return *reinterpret_cast<const uint4*>(p);
 }
 
+// 16-byte non-temporal load, for data read once per call.
+__device__ __forceinline__ uint4 load16_stream(const void* p) {
+  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
+
 // ---- cross-lane -----------------------------------------------------------------
 // DPP row permutations and the gfx950 permlane16/32 swaps move data between
 // lanes inside the VALU, without the LDS round trip of ds_bpermute.
