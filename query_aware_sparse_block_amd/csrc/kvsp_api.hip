@@ -249,7 +249,7 @@ kvsp_status kvsp_score_topk(const kvsp_layout* layout, const kvsp_select_params*
   // About kScoreTargetWorkgroups workgroups of four waves over all candidates.
   const int64_t total_blocks = static_cast<int64_t>(l.batch) * l.max_blocks_per_seq;
   int64_t bpw = (total_blocks + 4 * kScoreTargetWorkgroups - 1) / (4 * kScoreTargetWorkgroups);
-  const int per_pass = 64 / score_group_lanes(l.num_kv_heads, l.head_dim);  // blocks per wave pass
+  const int per_pass = 64 / score_shape(l.num_kv_heads, l.head_dim).lg;  // blocks per wave pass
   bpw = (bpw + per_pass - 1) / per_pass * per_pass;
   sa.blocks_per_wave = static_cast<int>(bpw > 256 ? 256 : bpw);
   sa.top_k = p.top_k;

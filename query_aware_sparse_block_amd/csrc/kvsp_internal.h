@@ -84,6 +84,9 @@ hipError_t launch_decode(const DecodeArgs& a, int dtype, int group_pad, int num_
 int decode_group_pad(const kvsp_layout& l);  // GP: heads per work item (1, 2, 4, 8 or 16)
 int decode_max_chunks(const kvsp_layout& l);
 int decode_chunk_quantum(int dtype, int D);  // tokens per chunk unit
-int score_group_lanes(int Hkv, int D);       // lanes that share one summary row
+struct ScoreShape {
+  int lg, vpl;  // lanes that share one summary row, 16-byte vectors per lane
+};
+ScoreShape score_shape(int Hkv, int D);
 
 }  // namespace kvsp

@@ -31,12 +31,12 @@ namespace kvsp {
 // scores 64 / LG blocks per pass, and one DPP butterfly over LG lanes reduces
 // all of them at once. The prologue issues its independent loads together
 // (context length, the workgroup's block-table entries, the queries); the
-// passes are double-buffered so one pass's loads fly while the previous one
-// is reduced. This scores the workgroup's block range of sequence b and
+// passes are double-buffered (up to 16 vectors per lane) so one pass's loads
+// fly while the previous one is reduced. This scores the workgroup's block range of sequence b and
 // returns C (the sequence's candidate count). COHERENT stores make the scores
 // visible to other workgroups of the same launch.
 template <typename T, int LG, int VPL, bool COHERENT>
-__device__ int score_blocks(const ScoreArgs& a, double* qbar, int b) {
+__device__ __forceinline__ int score_blocks(const ScoreArgs& a, double* qbar, int b) {
   const int lane = threadIdx.x % kWave;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int per_wg = 4 * a.blocks_per_wave;
@@ -93,23 +93,28 @@ __device__ int score_blocks(const ScoreArgs& a, double* qbar, int b) {
   const int w0 = wave * a.blocks_per_wave;  // offset of this wave's blocks in the range
   const int j1 = min(C, first + w0 + a.blocks_per_wave);
 
+  // The row's nvec vectors are spread as gl + LG * v; the group covers
+  // LG * VPL >= nvec of them and the lanes past the row's end contribute 0.
+  const int nvec = row / 4;
   auto issue = [&](int jb, float4 (&sv)[VPL]) {
     const int j = jb + slot;
     const int64_t phys = j < j1 ? phys_lds[j - first] : 0;
     const float4* srow = reinterpret_cast<const float4*>(a.summaries + phys * row);
 #pragma unroll
     for (int v = 0; v < VPL; ++v)
-      sv[v] = j < j1 ? srow[gl + LG * v] : make_float4(0.f, 0.f, 0.f, 0.f);
+      sv[v] = (j < j1 && gl + LG * v < nvec) ? srow[gl + LG * v] : make_float4(0.f, 0.f, 0.f, 0.f);
   };
   auto consume = [&](int jb, const float4 (&sv)[VPL]) {
     double acc = 0.0;
 #pragma unroll
     for (int v = 0; v < VPL; ++v) {
-      const double* qv = qbar + 4 * (gl + LG * v);
-      acc += qv[0] * static_cast<double>(sv[v].x);
-      acc += qv[1] * static_cast<double>(sv[v].y);
-      acc += qv[2] * static_cast<double>(sv[v].z);
-      acc += qv[3] * static_cast<double>(sv[v].w);
+      if (gl + LG * v < nvec) {
+        const double* qv = qbar + 4 * (gl + LG * v);
+        acc += qv[0] * static_cast<double>(sv[v].x);
+        acc += qv[1] * static_cast<double>(sv[v].y);
+        acc += qv[2] * static_cast<double>(sv[v].z);
+        acc += qv[3] * static_cast<double>(sv[v].w);
+      }
     }
     acc = group_sum<LG>(acc);
     const int j = jb + slot;
@@ -122,18 +127,27 @@ __device__ int score_blocks(const ScoreArgs& a, double* qbar, int b) {
     }
   };
 
-  float4 buf0[VPL], buf1[VPL];
   int jb = first + w0;
-  if (jb < j1) issue(jb, buf0);
-  while (jb < j1) {
-    const int jn = jb + BPP;
-    if (jn < j1) issue(jn, buf1);
-    consume(jb, buf0);
-    if (jn >= j1) break;
-    const int jn2 = jn + BPP;
-    if (jn2 < j1) issue(jn2, buf0);
-    consume(jn, buf1);
-    jb = jn2;
+  if constexpr (VPL <= 16) {
+    float4 buf0[VPL], buf1[VPL];
+    if (jb < j1) issue(jb, buf0);
+    while (jb < j1) {
+      const int jn = jb + BPP;
+      if (jn < j1) issue(jn, buf1);
+      consume(jb, buf0);
+      if (jn >= j1) break;
+      const int jn2 = jn + BPP;
+      if (jn2 < j1) issue(jn2, buf0);
+      consume(jn, buf1);
+      jb = jn2;
+    }
+  } else {
+    // The longest rows: one buffer already holds 32 vectors per lane.
+    float4 buf[VPL];
+    for (; jb < j1; jb += BPP) {
+      issue(jb, buf);
+      consume(jb, buf);
+    }
   }
   return C;
 }
@@ -153,31 +167,47 @@ static hipError_t launch_score_v(const ScoreArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
-// Group width from the summary row length: 8 vectors per lane (more for the
-// longest rows), at most one wave per block.
+// Group shape from the summary row length nvec = Hkv * D / 4 vectors (at
+// least 16): LG, the largest power of two <= 64 with 8 * LG <= nvec lanes
+// per block, and VPL, the fewest of 8, 16 or 32 vectors per lane that cover
+// the row (16 at most below 64 lanes).
 constexpr int kScoreVecPerLane = 8;
-int score_group_lanes(int Hkv, int D) {
+ScoreShape score_shape(int Hkv, int D) {
   const int nvec = Hkv * D / 4;
-  const int lg = nvec / kScoreVecPerLane;
-  return lg < 1 ? 1 : (lg > kWave ? kWave : lg);
+  ScoreShape sh{2, kScoreVecPerLane};
+  while (sh.lg < kWave && 2 * sh.lg * kScoreVecPerLane <= nvec) sh.lg *= 2;
+  while (sh.lg * sh.vpl < nvec) sh.vpl *= 2;
+  return sh;
+}
+
+// Calls F::template run<LG, VPL>() for the shape of (Hkv, D).
+template <typename F>
+static hipError_t with_score_shape(int Hkv, int D, F&& f) {
+  const ScoreShape sh = score_shape(Hkv, D);
+  const bool wide = sh.vpl > kScoreVecPerLane;
+  switch (sh.lg) {
+    case 2: return wide ? f.template run<2, 16>() : f.template run<2, 8>();
+    case 4: return wide ? f.template run<4, 16>() : f.template run<4, 8>();
+    case 8: return wide ? f.template run<8, 16>() : f.template run<8, 8>();
+    case 16: return wide ? f.template run<16, 16>() : f.template run<16, 8>();
+    case 32: return wide ? f.template run<32, 16>() : f.template run<32, 8>();
+    default:
+      if (sh.vpl == 32) return f.template run<64, 32>();
+      return wide ? f.template run<64, 16>() : f.template run<64, 8>();
+  }
 }
 
 template <typename T>
+struct ScoreLauncher {
+  const ScoreArgs& a;
+  hipStream_t stream;
+  template <int LG, int VPL>
+  hipError_t run() const { return launch_score_v<T, LG, VPL>(a, stream); }
+};
+
+template <typename T>
 static hipError_t launch_score_t(const ScoreArgs& a, hipStream_t stream) {
-  constexpr int V = kScoreVecPerLane;
-  const int nvec = a.Hkv * a.D / 4;
-  switch (score_group_lanes(a.Hkv, a.D)) {
-    case 1: return launch_score_v<T, 1, V>(a, stream);   // nvec >= 16 always: not reached
-    case 2: return launch_score_v<T, 2, V>(a, stream);
-    case 4: return launch_score_v<T, 4, V>(a, stream);
-    case 8: return launch_score_v<T, 8, V>(a, stream);
-    case 16: return launch_score_v<T, 16, V>(a, stream);
-    case 32: return launch_score_v<T, 32, V>(a, stream);
-    default:
-      if (nvec > kWave * 2 * V) return launch_score_v<T, 64, 4 * V>(a, stream);
-      if (nvec > kWave * V) return launch_score_v<T, 64, 2 * V>(a, stream);
-      return launch_score_v<T, 64, V>(a, stream);
-  }
+  return with_score_shape(a.Hkv, a.D, ScoreLauncher<T>{a, stream});
 }
 
 hipError_t launch_score(const ScoreArgs& a, int dtype, hipStream_t stream) {
@@ -243,8 +273,8 @@ struct TopkShared {
 // key equal to the threshold is kept (no tie is cut), one block-wide scan of
 // (kept, run starts) places the selected ids and the spans; a cut tie adds
 // one scan that ranks the equal keys by index.
-template <int WAVES, bool COHERENT>
-__device__ void select_sequence(const TopkArgs& a, int b, TopkShared& sh) {
+template <int WAVES, bool COHERENT, int RMAX>
+__device__ __forceinline__ void select_sequence_r(const TopkArgs& a, int b, TopkShared& sh) {
   constexpr int kTopkThreads = WAVES * kWave;
   const int t = threadIdx.x;
   const int lane = t % kWave;
@@ -262,9 +292,9 @@ __device__ void select_sequence(const TopkArgs& a, int b, TopkShared& sh) {
       return a.scores[row + j];
     }
   };
-  float raw[kTopkMaxPerThread];
+  float raw[RMAX];
 #pragma unroll
-  for (int r = 0; r < kTopkMaxPerThread; ++r) {
+  for (int r = 0; r < RMAX; ++r) {
     const int j = jbase + r;
     raw[r] = (r < R && j < a.max_blocks) ? score_at(j) : 0.f;
   }
@@ -274,9 +304,9 @@ __device__ void select_sequence(const TopkArgs& a, int b, TopkShared& sh) {
   const int C = p.C;
   const int k = p.k;
 
-  uint32_t key[kTopkMaxPerThread];
+  uint32_t key[RMAX];
 #pragma unroll
-  for (int r = 0; r < kTopkMaxPerThread; ++r) {
+  for (int r = 0; r < RMAX; ++r) {
     const int j = jbase + r;
     key[r] = (r < R && j < C) ? order_key(raw[r]) : 0u;
   }
@@ -299,7 +329,7 @@ __device__ void select_sequence(const TopkArgs& a, int b, TopkShared& sh) {
       const int shift = 24 - 8 * pass;
       uint32_t* hist = sh.hist[pass];
 #pragma unroll
-      for (int r = 0; r < kTopkMaxPerThread; ++r) {
+      for (int r = 0; r < RMAX; ++r) {
         const int j = jbase + r;
         if (r < R && j < C && (key[r] & mask) == prefix) atomicAdd(&hist[(key[r] >> shift) & 255u], 1u);
       }
@@ -339,7 +369,7 @@ __device__ void select_sequence(const TopkArgs& a, int b, TopkShared& sh) {
   const bool cut_tie = partial && take_equal < eq_total;  // uniform
   uint32_t n_eq = 0;
 #pragma unroll
-  for (int r = 0; r < kTopkMaxPerThread; ++r) {
+  for (int r = 0; r < RMAX; ++r) {
     const int j = jbase + r;
     if (r < R && j < C && key[r] == thresh) ++n_eq;
   }
@@ -362,7 +392,7 @@ __device__ void select_sequence(const TopkArgs& a, int b, TopkShared& sh) {
     uint32_t eq_rank = eq_before;
     bool left = keep_prev;  // kept(j - 1)
 #pragma unroll
-    for (int r = 0; r < kTopkMaxPerThread; ++r) {
+    for (int r = 0; r < RMAX; ++r) {
       const int j = jbase + r;
       if (!(r < R && j < C)) continue;
       const bool kp = kept(key[r], eq_rank);
@@ -387,7 +417,7 @@ __device__ void select_sequence(const TopkArgs& a, int b, TopkShared& sh) {
   const bool window = p.n > C;
   int32_t* sp = a.spans + row * 2 + static_cast<int64_t>(b) * 2;  // [B][max_blocks+1][2]
 #pragma unroll
-  for (int r = 0; r < kTopkMaxPerThread; ++r) {
+  for (int r = 0; r < RMAX; ++r) {
     const int j = jbase + r;
     if (!(r < R && j < C) || !((keep_bits >> r) & 1u)) continue;
     const bool left = r == 0 ? keep_prev : ((keep_bits >> (r - 1)) & 1u) != 0;
@@ -413,6 +443,24 @@ __device__ void select_sequence(const TopkArgs& a, int b, TopkShared& sh) {
     a.use_dense[b] = p.dense;
   }
   (void)lane;
+}
+
+// Candidates per thread are bounded by RMAX at compile time, so the loops over
+// a thread's candidates unroll to the bound the table actually needs.
+template <int WAVES, bool COHERENT>
+__device__ __forceinline__ void select_sequence(const TopkArgs& a, int b, TopkShared& sh) {
+  const int R = (a.max_blocks + WAVES * kWave - 1) / (WAVES * kWave);
+  if (R <= 1) {
+    select_sequence_r<WAVES, COHERENT, 1>(a, b, sh);
+  } else if (R <= 2) {
+    select_sequence_r<WAVES, COHERENT, 2>(a, b, sh);
+  } else if (R <= 4) {
+    select_sequence_r<WAVES, COHERENT, 4>(a, b, sh);
+  } else if (R <= 8) {
+    select_sequence_r<WAVES, COHERENT, 8>(a, b, sh);
+  } else {
+    select_sequence_r<WAVES, COHERENT, kTopkMaxPerThread>(a, b, sh);
+  }
 }
 
 template <int WAVES>
@@ -472,22 +520,19 @@ static hipError_t launch_fused_v(const ScoreArgs& sa, const TopkArgs& ta, int32_
 }
 
 template <typename T>
+struct FusedLauncher {
+  const ScoreArgs& sa;
+  const TopkArgs& ta;
+  int32_t* counters;
+  hipStream_t stream;
+  template <int LG, int VPL>
+  hipError_t run() const { return launch_fused_v<T, LG, VPL>(sa, ta, counters, stream); }
+};
+
+template <typename T>
 static hipError_t launch_fused_t(const ScoreArgs& sa, const TopkArgs& ta, int32_t* counters,
                                  hipStream_t stream) {
-  constexpr int V = kScoreVecPerLane;
-  const int nvec = sa.Hkv * sa.D / 4;
-  switch (score_group_lanes(sa.Hkv, sa.D)) {
-    case 1: return launch_fused_v<T, 1, V>(sa, ta, counters, stream);
-    case 2: return launch_fused_v<T, 2, V>(sa, ta, counters, stream);
-    case 4: return launch_fused_v<T, 4, V>(sa, ta, counters, stream);
-    case 8: return launch_fused_v<T, 8, V>(sa, ta, counters, stream);
-    case 16: return launch_fused_v<T, 16, V>(sa, ta, counters, stream);
-    case 32: return launch_fused_v<T, 32, V>(sa, ta, counters, stream);
-    default:
-      if (nvec > kWave * 2 * V) return launch_fused_v<T, 64, 4 * V>(sa, ta, counters, stream);
-      if (nvec > kWave * V) return launch_fused_v<T, 64, 2 * V>(sa, ta, counters, stream);
-      return launch_fused_v<T, 64, V>(sa, ta, counters, stream);
-  }
+  return with_score_shape(sa.Hkv, sa.D, FusedLauncher<T>{sa, ta, counters, stream});
 }
 
 bool fused_select_supported(int max_blocks) { return max_blocks <= kFusedSelectMaxBlocks; }

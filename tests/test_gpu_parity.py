@@ -202,3 +202,21 @@ def test_zero_queries_tie_every_block(max_blocks_pad):
     for b in range(case.B):
         k = int(r_or["plan"][b][3])
         assert np.array_equal(gpu["selected"][b, :k], np.arange(k))
+
+
+@pytest.mark.parametrize("Hkv,D,G", [(6, 128, 2), (12, 64, 1), (24, 128, 1), (40, 128, 1)])
+def test_summary_rows_of_any_head_count(Hkv, D, G):
+    # summary rows of Hkv * D / 4 = 192, 192, 768 and 1280 16-byte vectors: none
+    # is a whole number of lane groups, so the last vectors of a row are
+    # partial; 40 heads also take the longest-row variant (32 vectors per lane)
+    case = wl.make_case(f"hkv{Hkv}", seed=70 + Hkv, B=2, Hq=Hkv * G, Hkv=Hkv, D=D, P=16,
+                        dtype="bf16", ctx_lens=[1024, 700], shuffle=True, num_phys=140, top_k=6,
+                        keep_floor=1, recent_window=32)
+    H.full_parity(case)
+
+
+def test_long_table_with_three_kv_heads():
+    # the two-kernel selection with a partial last lane group (48 vectors a row)
+    case = wl.make_case("long-table-hkv3", seed=71, B=1, Hq=3, Hkv=3, D=64, P=16, dtype="bf16",
+                        ctx_lens=[70000], top_k=9, keep_floor=1, recent_window=40)
+    H.full_parity(case)
