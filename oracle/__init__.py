@@ -53,6 +53,8 @@ def _bind(path: str):
                                             i32, f64, P, P]
     L.kvsp_oracle_attended_tokens.argtypes = [i32, i32, i32, P, i32, i32, P]
     L.kvsp_oracle_attended_tokens.restype = i32
+    L.kvsp_oracle_append.argtypes = [ctypes.c_int, P, P, i32, i32, i32, P, P, P, i32, P, i32, P,
+                                     P]
     L.kvsp_oracle_decode_step.argtypes = ([ctypes.c_int] + [i32] * 6 + [P] * 6 + [i32] * 7
                                           + [f64] + [P] * 8)
     return L
@@ -127,6 +129,24 @@ def summaries(dtype, k_pool, block_table, ctx_lens, Hkv, P, D):
     lib().kvsp_oracle_summaries(_code(dtype), _p(k_pool), B, Hkv, P, D, _p(block_table),
                                 max_blocks, _p(ctx_lens), _p(out))
     return out
+
+
+def append(dtype, k_pool, v_pool, k_new, v_new, block_table, positions, *, Hkv, P, D):
+    """Decode-time append [SparPR opening paragraphs; ¶Query-Aware key-block
+    selection]: writes each sequence's new K/V row at token positions[b]
+    (skipped when negative) into k_pool / v_pool IN PLACE; returns
+    (filled [B][Hkv][D] double, flags [B]) where flags[b] = 1 marks that the
+    token completed its block and filled[b] is that block's mean key."""
+    B = len(positions)
+    assert k_pool.flags["C_CONTIGUOUS"] and v_pool.flags["C_CONTIGUOUS"]
+    filled = np.full((B, Hkv, D), np.nan, np.float64)
+    flags = np.zeros(B, np.int32)
+    lib().kvsp_oracle_append(_code(dtype), _p(k_pool), _p(v_pool), Hkv, P, D,
+                             _p(np.ascontiguousarray(k_new)), _p(np.ascontiguousarray(v_new)),
+                             _p(np.ascontiguousarray(block_table, np.int32)),
+                             block_table.shape[1], _p(np.ascontiguousarray(positions, np.int32)),
+                             B, _p(filled), _p(flags))
+    return filled, flags
 
 
 def scores(dtype, q_b, summ_b, Hq, Hkv, D, C):

@@ -20,6 +20,8 @@
 //                 window, flash-style log-sum-exp merge of partial attentions).
 //   [KVO-WHY]     "KV cache offloading" (aiwiki), section "Why the cache leaves
 //                 the GPU" (dense decode reads every stored key and value).
+//   [SparPR-INTRO] the SparPR page's opening paragraphs (the KV cache gains
+//                 one token per decoded token).
 //
 // Arithmetic: every stored element (fp32, fp16 or bf16) is widened exactly to
 // double, and everything after that is double. Loops run in the plain order
@@ -174,6 +176,22 @@ void kvsp_oracle_summaries(int dtype, const void* k_pool, int32_t B, int32_t Hkv
     }
   }
 }
+
+// ---- decode-time append [SparPR-INTRO, SparPR-QA] ----------------------------
+//
+// One decode step adds one token per sequence [SparPR-INTRO]. For sequence b
+// with positions[b] = p >= 0, the new key and value rows (k_new/v_new
+// [B][Hkv][D], element type `dtype`) are copied into token p % P of physical
+// block block_table[b][p / P], for every KV head. If p % P == P - 1 the token
+// completes its block, which therefore now has a summary [SparPR-QA]: the
+// mean key of its P tokens, computed with kvsp_oracle_block_summary on the
+// updated pool, goes to filled[b][g][d] and flags[b] = 1. Otherwise (or when
+// p < 0: no token this step) nothing is written for b and flags[b] = 0.
+// Pools are modified in place.
+void kvsp_oracle_append(int dtype, void* k_pool, void* v_pool, int32_t Hkv, int32_t P,
+                        int32_t D, const void* k_new, const void* v_new,
+                        const int32_t* block_table, int32_t max_blocks,
+                        const int32_t* positions, int32_t B, double* filled, int32_t* flags);
 
 // ---- step 2: block relevance score [SparPR-QA] -------------------------------
 //
@@ -377,6 +395,35 @@ void kvsp_oracle_decode_step(int dtype, int32_t B, int32_t Hq, int32_t Hkv, int3
                                 Hkv, P, D, h / G, bt_row, tokens.data(), ntok, scale,
                                 out + (static_cast<int64_t>(b) * Hq + h) * D,
                                 lse + static_cast<int64_t>(b) * Hq + h);
+    }
+  }
+}
+
+void kvsp_oracle_append(int dtype, void* k_pool, void* v_pool, int32_t Hkv, int32_t P,
+                        int32_t D, const void* k_new, const void* v_new,
+                        const int32_t* block_table, int32_t max_blocks,
+                        const int32_t* positions, int32_t B, double* filled, int32_t* flags) {
+  const int64_t elem = dtype == 0 ? 4 : 2;
+  for (int32_t b = 0; b < B; ++b) {
+    flags[b] = 0;
+    const int32_t p = positions[b];
+    if (p < 0) continue;
+    const int32_t j = p / P;
+    const int32_t t = p % P;
+    const int32_t phys = block_table[static_cast<int64_t>(b) * max_blocks + j];
+    for (int32_t g = 0; g < Hkv; ++g) {
+      const int64_t src = (static_cast<int64_t>(b) * Hkv + g) * D;
+      const int64_t dst = pool_index(phys, g, t, 0, Hkv, P, D);
+      std::memcpy(static_cast<char*>(k_pool) + dst * elem,
+                  static_cast<const char*>(k_new) + src * elem, D * elem);
+      std::memcpy(static_cast<char*>(v_pool) + dst * elem,
+                  static_cast<const char*>(v_new) + src * elem, D * elem);
+    }
+    if (t == P - 1) {
+      flags[b] = 1;
+      for (int32_t g = 0; g < Hkv; ++g)
+        kvsp_oracle_block_summary(dtype, k_pool, Hkv, P, D, phys, g,
+                                  filled + (static_cast<int64_t>(b) * Hkv + g) * D);
     }
   }
 }

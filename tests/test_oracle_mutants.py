@@ -14,6 +14,7 @@ import sys
 import pytest
 
 import oracle
+from tests import test_oracle_append as Ap
 from tests import test_oracle_attention as A
 from tests import test_oracle_selection as S
 from tests import test_oracle_widen as Wd
@@ -47,6 +48,14 @@ MUTANTS = {
                              "std::ldexp(static_cast<double>(frac), -25)"),
     "default scale 1/D": ("scale = 1.0 / std::sqrt(static_cast<double>(D));",
                           "scale = 1.0 / static_cast<double>(D);"),
+    "append one token late": ("const int64_t dst = pool_index(phys, g, t, 0, Hkv, P, D);",
+                              "const int64_t dst = pool_index(phys, g, (t + 1) % P, 0, Hkv, P, D);"),
+    "append value into K": ("std::memcpy(static_cast<char*>(v_pool) + dst * elem,\n                  static_cast<const char*>(v_new)",
+                             "std::memcpy(static_cast<char*>(k_pool) + dst * elem,\n                  static_cast<const char*>(v_new)"),
+    "append summary one token early": ("    if (t == P - 1) {\n      flags[b] = 1;",
+                                       "    if (t == P - 2) {\n      flags[b] = 1;"),
+    "append ignores table": ("const int32_t phys = block_table[static_cast<int64_t>(b) * max_blocks + j];\n    for (int32_t g = 0; g < Hkv; ++g) {\n      const int64_t src",
+                             "const int32_t phys = j;\n    for (int32_t g = 0; g < Hkv; ++g) {\n      const int64_t src"),
 }
 
 
@@ -80,6 +89,10 @@ def _pins():
         out.append((f"lse merge {seed}", lambda s=seed: A.test_lse_merge_partition_invariance(s)))
     out.append(("single token", A.test_single_token_gives_value_exactly))
     out.append(("equal logits", A.test_equal_logits_give_mean_of_values))
+    out.append(("append fill", Ap.test_filling_a_block_token_by_token))
+    out.append(("append fp16/fp32", Ap.test_filling_a_block_fp16_and_fp32))
+    out.append(("append skip", Ap.test_negative_position_writes_nothing))
+    out.append(("append batch", Ap.test_batch_append_lands_in_each_sequences_block_and_matches_summaries))
     return out
 
 
