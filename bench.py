@@ -213,6 +213,21 @@ def main():
     attn_s = timed(capture(lambda i: dev.sparse_decode(reps[i % R], bufs[i % R])))
     sel_s = timed(capture(lambda i: dev.score_topk(reps[i % R], bufs[i % R])))
 
+    # Decode-time append, timed on its own (it precedes scoring in a decode
+    # loop): each sequence's newest token is written again with its own K/V
+    # rows, so the pools and summaries keep their contents; when the contexts
+    # end on a block boundary every call also re-derives that block's summary.
+    ctx0 = dc0.ctx_lens.long()
+    bt0 = dc0.block_table.long()
+    last_phys = bt0[torch.arange(case.B, device=bt0.device), (ctx0 - 1) // case.P]
+    last_t = (ctx0 - 1) % case.P
+    k_last = dc0.k_pool[last_phys, :, last_t].contiguous()
+    v_last = dc0.v_pool[last_phys, :, last_t].contiguous()
+    pos_last = (ctx0 - 1).to(torch.int32)
+    append_s = timed(capture(lambda i: dev.append_kv(reps[i % R], bufs[i % R], k_last, v_last,
+                                                     pos_last)))
+    completes = bool(((ctx0 % case.P) == 0).all().item())
+
     nsel = bufs[0].num_selected.cpu().numpy()
     dense = bufs[0].use_dense.cpu().numpy()
     tokens = attended_tokens_per_seq(case, nsel, dense)
@@ -258,7 +273,13 @@ def main():
         "selected_kv_hbm_frac": achieved / HBM_PEAK_GBPS,
         "kernels_us": {"score_topk": sel_s / args.steps * 1e6,
                        "sparse_decode": attn_avg * 1e6,
-                       "step": ms_per_step * 1e3},
+                       "step": ms_per_step * 1e3,
+                       "append_kv": append_s / args.steps * 1e6},
+        "append": {"completes_block": completes,
+                   "bytes_written_per_launch": 2 * case.B * case.Hkv * case.D * E
+                   + (case.B * case.Hkv * case.D * 4 if completes else 0),
+                   "bytes_read_per_launch": case.B * case.Hkv * case.P * case.D * E
+                   if completes else 0},
         "roofline": {
             "bound": "hbm",
             "kernel": "attend_kernel (the whole kvsp_sparse_decode call)",

@@ -133,6 +133,28 @@ kvsp_status kvsp_build_summaries(const kvsp_layout* layout, const void* k_pool,
                                  const int32_t* block_table, const int32_t* context_lens,
                                  float* summaries, hipStream_t stream);
 
+/* Decode-time append (SparPR, opening paragraphs: the cache gains one token
+ * per decoded token; "Query-Aware key-block selection": full blocks carry a
+ * summary). For every sequence b with 0 <= p = positions[b] <
+ * max_blocks_per_seq * P, and phys = block_table[b][p / P] in
+ * [0, num_phys_blocks):
+ *   K[phys][g][p % P][:] = k_new[b][g][:],  V[phys][g][p % P][:] = v_new[b][g][:]
+ * for all KV heads g; and when p % P == P - 1 (the token completes its block)
+ *   summaries[phys][g][d] = (1/P) * sum_t K[phys][g][t][d]
+ * with the same exact-rounded arithmetic as kvsp_build_summaries (the result
+ * is bit-identical to it). Sequences whose position or block is out of range
+ * are skipped on the device (no token this step); nothing else is written.
+ *   k_new, v_new  [B][Hkv][D] device, layout->dtype; read only
+ *   positions     [B] int32 device: the token index the new token takes (the
+ *                 context length before this step); the caller advances its
+ *                 context lengths afterwards
+ *   k_pool, v_pool, summaries: as in the calls around it, updated in place
+ * Needs no workspace. Calls on one stream run in order; a call must not
+ * overlap another that reads or writes the same pool rows. */
+kvsp_status kvsp_append_kv(const kvsp_layout* layout, const void* k_new, const void* v_new,
+                           const int32_t* block_table, const int32_t* positions, void* k_pool,
+                           void* v_pool, float* summaries, hipStream_t stream);
+
 /* Steps 2-3 and the step-5 decision (SparPR, "Query-Aware key-block
  * selection", "Dynamic budget control", "On-demand local recomputation with
  * cost-aware fallback"). For every sequence b:

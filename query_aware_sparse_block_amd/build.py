@@ -16,7 +16,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 OBJDIR = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libkvsp.so")
-SOURCES = ["kvsp_api.hip", "kvsp_summaries.hip", "kvsp_select.hip", "kvsp_decode.hip"]
+SOURCES = ["kvsp_api.hip", "kvsp_summaries.hip", "kvsp_append.hip", "kvsp_select.hip",
+           "kvsp_decode.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 

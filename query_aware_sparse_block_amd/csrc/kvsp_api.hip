@@ -205,6 +205,19 @@ size_t kvsp_workspace_bytes(const kvsp_layout* layout, const kvsp_select_params*
   return workspace_layout(*layout).total;
 }
 
+kvsp_status kvsp_append_kv(const kvsp_layout* layout, const void* k_new, const void* v_new,
+                           const int32_t* block_table, const int32_t* positions, void* k_pool,
+                           void* v_pool, float* summaries, hipStream_t stream) {
+  kvsp_status st = check_layout(layout);
+  if (st != KVSP_OK) return st;
+  if (!k_new || !v_new || !block_table || !positions || !k_pool || !v_pool || !summaries)
+    return KVSP_ERR_INVALID_ARG;
+  const kvsp_layout& l = *layout;
+  AppendArgs a{k_new, v_new, block_table, positions, k_pool, v_pool, summaries, l.batch,
+               l.num_kv_heads, l.block_size, l.max_blocks_per_seq, l.num_phys_blocks};
+  return from_hip(launch_append(a, l.dtype, l.head_dim, stream));
+}
+
 kvsp_status kvsp_build_summaries(const kvsp_layout* layout, const void* k_pool,
                                  const int32_t* block_table, const int32_t* context_lens,
                                  float* summaries, hipStream_t stream) {

@@ -70,6 +70,8 @@ __device__ __forceinline__ uint4 load16(const void* p) {
   return *reinterpret_cast<const uint4*>(p);
 }
 
+__device__ __forceinline__ void store16(void* p, uint4 v) { *reinterpret_cast<uint4*>(p) = v; }
+
 // 16-byte non-temporal load, for data read once per call.
 __device__ __forceinline__ uint4 load16_stream(const void* p) {
   const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));

@@ -17,6 +17,17 @@ struct SummaryArgs {
   int32_t B, Hkv, P, max_blocks;
 };
 
+struct AppendArgs {
+  const void* k_new;
+  const void* v_new;
+  const int32_t* block_table;
+  const int32_t* positions;
+  void* k_pool;
+  void* v_pool;
+  float* summaries;
+  int32_t B, Hkv, P, max_blocks, num_phys;
+};
+
 struct ScoreArgs {
   const void* q;
   const float* summaries;
@@ -69,6 +80,7 @@ struct DecodeArgs {
   float scale_log2;             // softmax scale * log2(e)
 };
 
+hipError_t launch_append(const AppendArgs& a, int dtype, int D, hipStream_t stream);
 hipError_t launch_build_summaries(const SummaryArgs& a, int dtype, int D, hipStream_t stream);
 hipError_t launch_score(const ScoreArgs& a, int dtype, hipStream_t stream);
 hipError_t launch_topk(const TopkArgs& a, hipStream_t stream);

@@ -85,6 +85,13 @@ def build_summaries(dc: DeviceCase, buf: StepBuffers, stream=None):
                               stream)
 
 
+def append_kv(dc: DeviceCase, buf: StepBuffers, k_new, v_new, positions, stream=None):
+    """Writes each sequence's new K/V row at positions[b] (device int32, -1 =
+    none) and the summary of every block a new token completes."""
+    kvsp.kvsp_append_kv(dc.layout, k_new, v_new, dc.block_table, positions, dc.k_pool, dc.v_pool,
+                        buf.summaries, stream)
+
+
 def score_topk(dc: DeviceCase, buf: StepBuffers, params=None, stream=None):
     kvsp.kvsp_score_topk(dc.layout, params or dc.params, dc.q, buf.summaries, dc.block_table,
                          dc.ctx_lens, buf.scores, buf.selected, buf.num_selected, buf.spans,

@@ -66,6 +66,8 @@ def library() -> ctypes.CDLL:
         L.kvsp_status_string.argtypes = [ctypes.c_int]
         L.kvsp_workspace_bytes.restype = sz
         L.kvsp_workspace_bytes.argtypes = [LP, SP]
+        L.kvsp_append_kv.restype = ctypes.c_int
+        L.kvsp_append_kv.argtypes = [LP, P, P, P, P, P, P, P, P]
         L.kvsp_build_summaries.restype = ctypes.c_int
         L.kvsp_build_summaries.argtypes = [LP, P, P, P, P, P]
         L.kvsp_score_topk.restype = ctypes.c_int
@@ -142,6 +144,13 @@ def alloc_workspace(layout: kvsp_layout, params: SelectParams | None = None,
                     device="cuda") -> torch.Tensor:
     n = kvsp_workspace_bytes(layout, params)
     return torch.zeros(max(n, 1), dtype=torch.uint8, device=device)  # counters start at zero
+
+
+def kvsp_append_kv(layout, k_new, v_new, block_table, positions, k_pool, v_pool, summaries,
+                   stream=None):
+    _check("kvsp_append_kv", library().kvsp_append_kv(
+        ctypes.byref(layout), _ptr(k_new), _ptr(v_new), _ptr(block_table), _ptr(positions),
+        _ptr(k_pool), _ptr(v_pool), _ptr(summaries), _stream(stream)))
 
 
 def kvsp_build_summaries(layout, k_pool, block_table, context_lens, summaries, stream=None):

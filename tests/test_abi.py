@@ -35,7 +35,7 @@ def test_library_exports_every_declared_entry_point():
     lib = kvsp.library()
     names = kvsp.declared_entry_points()
     assert {"kvsp_build_summaries", "kvsp_score_topk", "kvsp_sparse_decode",
-            "kvsp_dense_decode", "kvsp_workspace_bytes", "kvsp_status_string",
+            "kvsp_dense_decode", "kvsp_append_kv", "kvsp_workspace_bytes", "kvsp_status_string",
             "kvsp_abi_version"} <= set(names)
     for name in names:
         assert hasattr(lib, name), name
@@ -74,6 +74,7 @@ def test_bad_layout_rejected(over, code):
     par = _params()
     nul = [None] * 10
     assert lib.kvsp_build_summaries(ctypes.byref(lay), None, None, None, None, None) == code
+    assert lib.kvsp_append_kv(ctypes.byref(lay), *([None] * 7), None) == code
     assert lib.kvsp_score_topk(ctypes.byref(lay), ctypes.byref(par), *nul, None, 0, None) == code
     assert lib.kvsp_sparse_decode(ctypes.byref(lay), ctypes.byref(par), *([None] * 8),
                                   ctypes.c_float(0), None, None, None, 0, None) == code
@@ -98,6 +99,10 @@ def test_null_pointers_rejected():
     lib = kvsp.library()
     lay, par = _layout(), _params()
     assert lib.kvsp_build_summaries(ctypes.byref(lay), None, FAKE, FAKE, FAKE, None) == -1
+    for i in range(7):
+        args = [FAKE] * 7
+        args[i] = None
+        assert lib.kvsp_append_kv(ctypes.byref(lay), *args, None) == -1
     args = [FAKE] * 10
     args[7] = None  # num_spans
     assert lib.kvsp_score_topk(ctypes.byref(lay), ctypes.byref(par), *args, FAKE, 1 << 30,
