@@ -23,6 +23,7 @@ import sys
 import time
 
 HBM_PEAK_GBPS = 8000.0
+PCIE_PEAK_GBPS = 64.0  # PCIe 5.0 x16 host link, one direction
 METRIC = "decode-attn steps/sec + selected-KV GB/s (% of HBM peak) on 1 MI355X"
 
 
@@ -140,6 +141,8 @@ def main():
     ap.add_argument("--replicas", type=int, default=0,
                     help="device copies of the pool rotated per step (0: enough for 2 GiB)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-host-pool", action="store_true",
+                    help="skip the decode over a host-resident (pinned, mapped) pool")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the library has "
@@ -228,6 +231,26 @@ def main():
                                                      pos_last)))
     completes = bool(((ctx0 % case.P) == 0).all().item())
 
+    # The pool in host RAM (mapped pinned memory, the SparPR setting): the
+    # decode then reads its attended tiles across PCIe. A few eager calls on
+    # replica 0's selection; skipped for pools above 4 GiB.
+    host_pool = None
+    if not args.no_host_pool and pool_bytes <= (4 << 30):
+        print("[bench] decode over a host-resident pool", file=sys.stderr, flush=True)
+        hdc = dev.with_host_pool(dc0)
+        dev.sparse_decode(hdc, bufs[0])  # warm
+        torch.cuda.synchronize()
+        n_host = 5
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        t0.record()
+        for _ in range(n_host):
+            dev.sparse_decode(hdc, bufs[0])
+        t1.record()
+        torch.cuda.synchronize()
+        host_pool = {"calls": n_host, "decode_us": t0.elapsed_time(t1) / n_host * 1e3}
+        del hdc
+
     nsel = bufs[0].num_selected.cpu().numpy()
     dense = bufs[0].use_dense.cpu().numpy()
     tokens = attended_tokens_per_seq(case, nsel, dense)
@@ -293,6 +316,13 @@ def main():
             "traffic": profiling.recorded_traffic(args.workload),
             "traffic_source": "profiles/attend_traffic.txt (rocprofv3 FETCH_SIZE*2 + "
                               "WRITE_SIZE*1 per launch; null if the decode sources changed)",
+        },
+        "host_pool": None if host_pool is None else {
+            **host_pool,
+            "pcie_gbps": attn_bytes / (host_pool["decode_us"] * 1e-6) / 1e9,
+            "pcie_peak_gbps": PCIE_PEAK_GBPS,
+            "frac": attn_bytes / (host_pool["decode_us"] * 1e-6) / 1e9 / PCIE_PEAK_GBPS,
+            "note": "kvsp_sparse_decode with K/V in mapped pinned host memory; bytes as roofline",
         },
         "scoring": {"bytes_per_launch": scoring_bytes(case, Cs),
                     "gbps": scoring_bytes(case, Cs) / (sel_s / args.steps) / 1e9},

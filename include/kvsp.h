@@ -33,6 +33,12 @@
  *
  * Conventions for every entry point
  *   - Tensor pointers are DEVICE pointers; struct pointers are HOST pointers.
+ *     k_pool and v_pool may also be host memory the device can read: pinned
+ *     with hipHostMalloc(hipHostMallocMapped), passed as the address
+ *     hipHostGetDevicePointer returns. The kernels then read, across PCIe,
+ *     only the tiles they touch (for kvsp_sparse_decode: the kept blocks and
+ *     the window), which is the offloaded-cache setting of the SparPR page;
+ *     results are bit-identical to a device-resident pool.
  *   - Work is enqueued on `stream` (0 = the null stream) and returns without
  *     waiting for it. No entry point allocates memory, synchronises the host
  *     or copies device data to the host. The library keeps no pointer after

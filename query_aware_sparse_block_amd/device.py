@@ -46,6 +46,16 @@ def upload(case: Case, device="cuda") -> DeviceCase:
     return DeviceCase(case, q, k, v, bt, cl, layout, params)
 
 
+def with_host_pool(dc: DeviceCase) -> DeviceCase:
+    """The same case with its K/V pool in mapped pinned host memory (queries,
+    block table and lengths stay on the device). The kernels then read the
+    pool across PCIe, and only the tiles they attend."""
+    from . import hostmem
+    return DeviceCase(dc.case, dc.q, hostmem.host_copy(dc.case.k_pool),
+                      hostmem.host_copy(dc.case.v_pool), dc.block_table, dc.ctx_lens, dc.layout,
+                      dc.params)
+
+
 @dataclass
 class StepBuffers:
     summaries: torch.Tensor

@@ -118,9 +118,13 @@ def make_layout(q: torch.Tensor, k_pool: torch.Tensor, block_table: torch.Tensor
     return kvsp_layout(B, Hq, Hkv, D, P, num_phys, block_table.shape[1], DTYPE_CODES[q.dtype])
 
 
-def _ptr(t: torch.Tensor | None):
+def _ptr(t):
+    """Device address of a contiguous device tensor, or of a mapped pinned
+    host buffer (an object with `device_ptr`)."""
     if t is None:
         return None
+    if hasattr(t, "device_ptr"):
+        return ctypes.c_void_p(t.device_ptr)
     assert t.is_cuda and t.is_contiguous(), "device tensors must be contiguous"
     return ctypes.c_void_p(t.data_ptr())
 
