@@ -220,3 +220,36 @@ def test_long_table_with_three_kv_heads():
     case = wl.make_case("long-table-hkv3", seed=71, B=1, Hq=3, Hkv=3, D=64, P=16, dtype="bf16",
                         ctx_lens=[70000], top_k=9, keep_floor=1, recent_window=40)
     H.full_parity(case)
+
+
+def test_more_items_than_workgroups_grid_stride():
+    # 300 sequences x 8 KV heads = 2400 one-chunk items > 2048 launched
+    # workgroups: later items are taken in grid-stride order
+    ctx = [256 + 16 * (b % 13) for b in range(300)]
+    case = wl.make_case("grid-stride", seed=72, B=300, Hq=16, Hkv=8, D=64, P=16, dtype="bf16",
+                        ctx_lens=ctx, shuffle=True, num_phys=300 * 28 + 10, top_k=4,
+                        keep_floor=1, recent_window=32)
+    H.full_parity(case, head_mask=_sample_heads(case, 200, 3))
+
+
+def _sample_heads(case, n, seed):
+    rng = np.random.default_rng(seed)
+    mask = np.zeros((case.B, case.Hq), np.uint8)
+    while int(mask.sum()) < n:
+        mask[rng.integers(case.B), rng.integers(case.Hq)] = 1
+    mask[0, 0] = mask[case.B - 1, case.Hq - 1] = 1
+    return mask
+
+
+@pytest.mark.parametrize("dtype,Hq,Hkv,D,P,ctx", [
+    ("fp32", 8, 2, 128, 256, [5000, 2300]),   # 128 KiB fp32 tiles
+    ("bf16", 15, 5, 128, 64, [3000, 999]),    # G = 3 padded to 4, five KV heads
+    ("fp16", 7, 7, 64, 32, [2048, 31]),       # odd MHA head count, a context inside the window
+    ("bf16", 64, 4, 64, 16, [1500, 800]),     # G = 16 at D = 64
+])
+def test_uncommon_shapes(dtype, Hq, Hkv, D, P, ctx):
+    case = wl.make_case(f"shape-{dtype}-{Hq}-{Hkv}-{D}-{P}", seed=73 + Hq + P, B=len(ctx), Hq=Hq,
+                        Hkv=Hkv, D=D, P=P, dtype=dtype, ctx_lens=ctx, shuffle=True,
+                        num_phys=len(ctx) * -(-max(ctx) // P) + 40, keep_num=1, keep_den=5,
+                        keep_floor=2, recent_window=P + 7)
+    H.full_parity(case)
