@@ -84,8 +84,6 @@ __device__ __forceinline__ int score_blocks(const ScoreArgs& a, double* qbar, in
   const SelectArgs sel{a.top_k, a.keep_num, a.keep_den, a.keep_floor, a.recent_window,
                        a.gamma_num, a.gamma_den};
   const int C = plan_sequence(a.context_lens[b], a.P, sel).C;
-  __syncthreads();
-  if (first >= C) return C;  // uniform over the workgroup
 
   constexpr int BPP = kWave / LG;  // blocks per wave pass
   const int gl = lane % LG;
@@ -95,10 +93,13 @@ __device__ __forceinline__ int score_blocks(const ScoreArgs& a, double* qbar, in
 
   // The row's nvec vectors are spread as gl + LG * v; the group covers
   // LG * VPL >= nvec of them and the lanes past the row's end contribute 0.
+  // The first pass reads its block-table entries itself (`direct`), so its
+  // summary loads leave before the workgroup barrier that publishes qbar.
   const int nvec = row / 4;
-  auto issue = [&](int jb, float4 (&sv)[VPL]) {
+  auto issue = [&](int jb, float4 (&sv)[VPL], bool direct) {
     const int j = jb + slot;
-    const int64_t phys = j < j1 ? phys_lds[j - first] : 0;
+    int64_t phys = 0;
+    if (j < j1) phys = direct ? a.block_table[trow + j] : phys_lds[j - first];
     const float4* srow = reinterpret_cast<const float4*>(a.summaries + phys * row);
 #pragma unroll
     for (int v = 0; v < VPL; ++v)
@@ -130,22 +131,27 @@ __device__ __forceinline__ int score_blocks(const ScoreArgs& a, double* qbar, in
   int jb = first + w0;
   if constexpr (VPL <= 16) {
     float4 buf0[VPL], buf1[VPL];
-    if (jb < j1) issue(jb, buf0);
+    if (jb < j1) issue(jb, buf0, true);
+    __syncthreads();  // qbar and the staged table entries
+    if (first >= C) return C;  // uniform over the workgroup
     while (jb < j1) {
       const int jn = jb + BPP;
-      if (jn < j1) issue(jn, buf1);
+      if (jn < j1) issue(jn, buf1, false);
       consume(jb, buf0);
       if (jn >= j1) break;
       const int jn2 = jn + BPP;
-      if (jn2 < j1) issue(jn2, buf0);
+      if (jn2 < j1) issue(jn2, buf0, false);
       consume(jn, buf1);
       jb = jn2;
     }
   } else {
     // The longest rows: one buffer already holds 32 vectors per lane.
     float4 buf[VPL];
+    if (jb < j1) issue(jb, buf, true);
+    __syncthreads();
+    if (first >= C) return C;
     for (; jb < j1; jb += BPP) {
-      issue(jb, buf);
+      if (jb != first + w0) issue(jb, buf, false);
       consume(jb, buf);
     }
   }
