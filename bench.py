@@ -141,8 +141,8 @@ def main():
     ap.add_argument("--replicas", type=int, default=0,
                     help="device copies of the pool rotated per step (0: enough for 2 GiB)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-host-pool", action="store_true",
-                    help="skip the decode over a host-resident (pinned, mapped) pool")
+    ap.add_argument("--host-pool", action="store_true",
+                    help="also time the decode over a host-resident (pinned, mapped) pool")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the library has "
@@ -231,11 +231,11 @@ def main():
                                                      pos_last)))
     completes = bool(((ctx0 % case.P) == 0).all().item())
 
-    # The pool in host RAM (mapped pinned memory, the SparPR setting): the
-    # decode then reads its attended tiles across PCIe. A few eager calls on
-    # replica 0's selection; skipped for pools above 4 GiB.
+    # With --host-pool: the pool in host RAM (mapped pinned memory, the SparPR
+    # setting), where the decode reads its attended tiles across PCIe. A few
+    # eager calls on replica 0's selection; pools above 4 GiB are skipped.
     host_pool = None
-    if not args.no_host_pool and pool_bytes <= (4 << 30):
+    if args.host_pool and pool_bytes <= (4 << 30):
         print("[bench] decode over a host-resident pool", file=sys.stderr, flush=True)
         hdc = dev.with_host_pool(dc0)
         dev.sparse_decode(hdc, bufs[0])  # warm
