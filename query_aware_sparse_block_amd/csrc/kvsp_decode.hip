@@ -11,8 +11,10 @@
 // i / P at offset i % P, because every attended block but the last is full.
 // That sequence is cut into at most max_chunks chunks of whole sub-tiles.
 // One workgroup handles one (sequence, KV head, head group, chunk) item: its
-// four wavefronts take the chunk's sub-tiles (SUB tokens, 8 KiB of keys) in
-// turn, each with its own online softmax, and merge through LDS at the end.
+// four wavefronts take the chunk's sub-tiles (SUB tokens: 4 KiB of keys and
+// as much of values, at least 16 tokens) in turn, each with its own online softmax, and merge
+// through LDS at the end. One-head items keep two sub-tiles in flight per
+// wavefront and read them non-temporally; GQA items keep one.
 // Workgroups walk the items with a grid stride, so any mix of sparse and
 // dense sequences fills the chip.
 //
