@@ -52,6 +52,8 @@ namespace kvsp {
 #ifndef KVSP_STREAM_MAX_GP
 #define KVSP_STREAM_MAX_GP 1
 #endif
+// Groups of at most this many chunks are merged by wave 0 alone, in registers.
+constexpr int kFastMergeChunks = 8;
 // Chunks per output whose accumulators the merging workgroup requests before
 // it has the merge weights.
 #ifndef KVSP_MERGE_PRE
@@ -472,119 +474,181 @@ __global__ __launch_bounds__(256) void attend_kernel(DecodeArgs a) {
       }
       __syncthreads();
       if (last_flag) {
-        // Every chunk of this group is published: merge by log-sum-exp,
-        // reading the partials at the device coherence point.
-        //   1. the first MERGE_PRE chunks' accumulators of every output this
-        //      thread owns are requested at once (16-byte loads);
-        //   2. meanwhile each wave takes heads h = wave, wave + 4, ...: lane
-        //      cc reads (m, l) of chunk cc, and wave reductions give
-        //      M = max m, the weights 2^(m - M) (0 for empty chunks, kept in
-        //      LDS) and Lsum = sum l 2^(m - M);
-        //   3. out = sum weight * acc / Lsum, the chunks split over CG thread
-        //      groups, folded through LDS.
-        // The merge reuses the LDS of the main loop (xacc and p_lds).
-        const int64_t slot0 = static_cast<int64_t>(grp) * a.max_chunks;
-        float* wt_s = &xacc[0][0];                   // [max_chunks][GP] weights
-        float* head_s = wt_s + a.max_chunks * GP;    // [GP][2]: M, Lsum
-        float4* red_s = reinterpret_cast<float4*>(&p_lds[0][0]);
-        constexpr int PAIRS = GP * D / 4;                     // (head, 4 channels) outputs
-        constexpr int CG = PAIRS >= 256 ? 1 : 256 / PAIRS;    // chunk groups per output
-        constexpr int PER = PAIRS >= 256 ? PAIRS / 256 : 1;   // outputs per thread
-        constexpr int PRE = KVSP_MERGE_PRE;
-        const int cg = threadIdx.x / (PAIRS >= 256 ? 256 : PAIRS);
-        const int pbase = threadIdx.x % (PAIRS >= 256 ? 256 : PAIRS);
-        auto acc_off = [&](int cc, int pv) {
-          const int h = (4 * pv) / D;
-          const int d = (4 * pv) % D;
-          return static_cast<uint32_t>((((slot0 + cc) * GP + h) * D + d) * sizeof(float));
-        };
-        float4 pre[PER][PRE];
+        if (GP <= S::NRG && w.nc <= kFastMergeChunks) {
+          // Few chunks and at most one head per row group: each output lane
+          // of wave 0 (row group = head, EPV channels) loads every chunk's
+          // (m, l) and its channels in one round trip and merges them in
+          // registers; no LDS, no barrier.
+          const int h = rg;
+          if (wave == 0 && h < GP && hg * GP + h < G) {
+            const int64_t slot0 = static_cast<int64_t>(grp) * a.max_chunks;
+            float4 pa[kFastMergeChunks][S::EPV / 4];
+            float pm[kFastMergeChunks], pl[kFastMergeChunks];
 #pragma unroll
-        for (int q = 0; q < PER; ++q)
+            for (int cc = 0; cc < kFastMergeChunks; ++cc) {
+              pm[cc] = NEG_INF;
+              pl[cc] = 0.f;
 #pragma unroll
-          for (int i = 0; i < PRE; ++i) {
-            const int cc = cg + i * CG;
-            pre[q][i] = cc < w.nc ? load_coherent4(part_rsrc, acc_off(cc, pbase + q * 256))
-                                  : make_float4(0.f, 0.f, 0.f, 0.f);
-          }
-        constexpr int HPW = (GP + kDecodeWaves - 1) / kDecodeWaves;  // heads per wave
-        float mv[HPW], lv[HPW];
+              for (int q = 0; q < S::EPV / 4; ++q) pa[cc][q] = make_float4(0.f, 0.f, 0.f, 0.f);
+              if (cc < w.nc) {
+                const int64_t ps = (slot0 + cc) * GP + h;
 #pragma unroll
-        for (int i = 0; i < HPW; ++i) {
-          const int h = wave + i * kDecodeWaves;
-          mv[i] = NEG_INF;
-          lv[i] = 0.f;
-          if (h < GP && lane < w.nc) {
-            mv[i] = load_coherent(a.part_ml + ((slot0 + lane) * GP + h) * 2);
-            lv[i] = load_coherent(a.part_ml + ((slot0 + lane) * GP + h) * 2 + 1);
-          }
-        }
-#pragma unroll
-        for (int i = 0; i < HPW; ++i) {
-          const int h = wave + i * kDecodeWaves;
-          if (h < GP) {  // wave-uniform
-            const float M = group_max<kWave>(lv[i] > 0.f ? mv[i] : NEG_INF);
-            const float wt = (lv[i] > 0.f && M != NEG_INF) ? __builtin_amdgcn_exp2f(mv[i] - M) : 0.f;
-            const float Ls = group_sum<kWave>(lv[i] * wt);
-            if (lane < w.nc) wt_s[lane * GP + h] = wt;
-            if (lane == 0) {
-              head_s[2 * h] = M;
-              head_s[2 * h + 1] = Ls;
-            }
-          }
-        }
-        __syncthreads();
-#pragma unroll
-        for (int q = 0; q < PER; ++q) {
-          const int pv = pbase + q * 256;
-          const int h = (4 * pv) / D;
-          const int d = (4 * pv) % D;
-          float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
-#pragma unroll
-          for (int i = 0; i < PRE; ++i) {
-            const int cc = cg + i * CG;
-            if (cc < w.nc) {
-              const float wgt = wt_s[cc * GP + h];
-              o.x += wgt * pre[q][i].x;
-              o.y += wgt * pre[q][i].y;
-              o.z += wgt * pre[q][i].z;
-              o.w += wgt * pre[q][i].w;
-            }
-          }
-#pragma unroll 8
-          for (int cc = cg + PRE * CG; cc < w.nc; cc += CG) {
-            const float wgt = wt_s[cc * GP + h];
-            const float4 pa = load_coherent4(part_rsrc, acc_off(cc, pv));
-            o.x += wgt * pa.x;
-            o.y += wgt * pa.y;
-            o.z += wgt * pa.z;
-            o.w += wgt * pa.w;
-          }
-          if constexpr (CG > 1) {
-            red_s[threadIdx.x] = o;
-          }
-          __syncthreads();
-          if (cg == 0 && hg * GP + h < G) {
-            if constexpr (CG > 1) {
-              for (int k = 1; k < CG; ++k) {
-                const float4 r = red_s[k * PAIRS + pbase];
-                o.x += r.x;
-                o.y += r.y;
-                o.z += r.z;
-                o.w += r.w;
+                for (int q = 0; q < S::EPV / 4; ++q)
+                  pa[cc][q] = load_coherent4(part_rsrc, static_cast<uint32_t>((ps * D + col + 4 * q) * sizeof(float)));
+                pm[cc] = load_coherent(a.part_ml + ps * 2);
+                pl[cc] = load_coherent(a.part_ml + ps * 2 + 1);
               }
             }
-            const float M = head_s[2 * h];
-            const float Ls = head_s[2 * h + 1];
+            float M = NEG_INF;
+#pragma unroll
+            for (int cc = 0; cc < kFastMergeChunks; ++cc)
+              if (pl[cc] > 0.f) M = fmaxf(M, pm[cc]);
+            float Ls = 0.f;
+            float o[S::EPV];
+#pragma unroll
+            for (int e = 0; e < S::EPV; ++e) o[e] = 0.f;
+            if (M != NEG_INF) {
+#pragma unroll
+              for (int cc = 0; cc < kFastMergeChunks; ++cc) {
+                if (pl[cc] > 0.f) {
+                  const float wgt = __builtin_amdgcn_exp2f(pm[cc] - M);
+                  Ls += pl[cc] * wgt;
+#pragma unroll
+                  for (int q = 0; q < S::EPV / 4; ++q) {
+                    o[4 * q + 0] += wgt * pa[cc][q].x;
+                    o[4 * q + 1] += wgt * pa[cc][q].y;
+                    o[4 * q + 2] += wgt * pa[cc][q].z;
+                    o[4 * q + 3] += wgt * pa[cc][q].w;
+                  }
+                }
+              }
+            }
             const float inv = Ls > 0.f ? 1.f / Ls : 0.f;
             const int hq = g * G + hg * GP + h;
-            *reinterpret_cast<float4*>(a.out + (static_cast<int64_t>(b) * a.Hq + hq) * D + d) =
-                make_float4(o.x * inv, o.y * inv, o.z * inv, o.w * inv);
-            if (d == 0 && a.lse != nullptr)
+            float* dst = a.out + (static_cast<int64_t>(b) * a.Hq + hq) * D + col;
+#pragma unroll
+            for (int q = 0; q < S::EPV / 4; ++q)
+              *reinterpret_cast<float4*>(dst + 4 * q) =
+                  make_float4(o[4 * q] * inv, o[4 * q + 1] * inv, o[4 * q + 2] * inv, o[4 * q + 3] * inv);
+            if (col == 0 && a.lse != nullptr)
               a.lse[static_cast<int64_t>(b) * a.Hq + hq] =
                   Ls > 0.f ? (M + __builtin_log2f(Ls)) * 0.69314718055994531f : NEG_INF;
           }
+        } else {
+          // Every chunk of this group is published: merge by log-sum-exp,
+          // reading the partials at the device coherence point.
+          //   1. the first MERGE_PRE chunks' accumulators of every output this
+          //      thread owns are requested at once (16-byte loads);
+          //   2. meanwhile each wave takes heads h = wave, wave + 4, ...: lane
+          //      cc reads (m, l) of chunk cc, and wave reductions give
+          //      M = max m, the weights 2^(m - M) (0 for empty chunks, kept in
+          //      LDS) and Lsum = sum l 2^(m - M);
+          //   3. out = sum weight * acc / Lsum, the chunks split over CG thread
+          //      groups, folded through LDS.
+          // The merge reuses the LDS of the main loop (xacc and p_lds).
+          const int64_t slot0 = static_cast<int64_t>(grp) * a.max_chunks;
+          float* wt_s = &xacc[0][0];                   // [max_chunks][GP] weights
+          float* head_s = wt_s + a.max_chunks * GP;    // [GP][2]: M, Lsum
+          float4* red_s = reinterpret_cast<float4*>(&p_lds[0][0]);
+          constexpr int PAIRS = GP * D / 4;                     // (head, 4 channels) outputs
+          constexpr int CG = PAIRS >= 256 ? 1 : 256 / PAIRS;    // chunk groups per output
+          constexpr int PER = PAIRS >= 256 ? PAIRS / 256 : 1;   // outputs per thread
+          constexpr int PRE = KVSP_MERGE_PRE;
+          const int cg = threadIdx.x / (PAIRS >= 256 ? 256 : PAIRS);
+          const int pbase = threadIdx.x % (PAIRS >= 256 ? 256 : PAIRS);
+          auto acc_off = [&](int cc, int pv) {
+            const int h = (4 * pv) / D;
+            const int d = (4 * pv) % D;
+            return static_cast<uint32_t>((((slot0 + cc) * GP + h) * D + d) * sizeof(float));
+          };
+          float4 pre[PER][PRE];
+  #pragma unroll
+          for (int q = 0; q < PER; ++q)
+  #pragma unroll
+            for (int i = 0; i < PRE; ++i) {
+              const int cc = cg + i * CG;
+              pre[q][i] = cc < w.nc ? load_coherent4(part_rsrc, acc_off(cc, pbase + q * 256))
+                                    : make_float4(0.f, 0.f, 0.f, 0.f);
+            }
+          constexpr int HPW = (GP + kDecodeWaves - 1) / kDecodeWaves;  // heads per wave
+          float mv[HPW], lv[HPW];
+  #pragma unroll
+          for (int i = 0; i < HPW; ++i) {
+            const int h = wave + i * kDecodeWaves;
+            mv[i] = NEG_INF;
+            lv[i] = 0.f;
+            if (h < GP && lane < w.nc) {
+              mv[i] = load_coherent(a.part_ml + ((slot0 + lane) * GP + h) * 2);
+              lv[i] = load_coherent(a.part_ml + ((slot0 + lane) * GP + h) * 2 + 1);
+            }
+          }
+  #pragma unroll
+          for (int i = 0; i < HPW; ++i) {
+            const int h = wave + i * kDecodeWaves;
+            if (h < GP) {  // wave-uniform
+              const float M = group_max<kWave>(lv[i] > 0.f ? mv[i] : NEG_INF);
+              const float wt = (lv[i] > 0.f && M != NEG_INF) ? __builtin_amdgcn_exp2f(mv[i] - M) : 0.f;
+              const float Ls = group_sum<kWave>(lv[i] * wt);
+              if (lane < w.nc) wt_s[lane * GP + h] = wt;
+              if (lane == 0) {
+                head_s[2 * h] = M;
+                head_s[2 * h + 1] = Ls;
+              }
+            }
+          }
           __syncthreads();
+  #pragma unroll
+          for (int q = 0; q < PER; ++q) {
+            const int pv = pbase + q * 256;
+            const int h = (4 * pv) / D;
+            const int d = (4 * pv) % D;
+            float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
+  #pragma unroll
+            for (int i = 0; i < PRE; ++i) {
+              const int cc = cg + i * CG;
+              if (cc < w.nc) {
+                const float wgt = wt_s[cc * GP + h];
+                o.x += wgt * pre[q][i].x;
+                o.y += wgt * pre[q][i].y;
+                o.z += wgt * pre[q][i].z;
+                o.w += wgt * pre[q][i].w;
+              }
+            }
+  #pragma unroll 8
+            for (int cc = cg + PRE * CG; cc < w.nc; cc += CG) {
+              const float wgt = wt_s[cc * GP + h];
+              const float4 pa = load_coherent4(part_rsrc, acc_off(cc, pv));
+              o.x += wgt * pa.x;
+              o.y += wgt * pa.y;
+              o.z += wgt * pa.z;
+              o.w += wgt * pa.w;
+            }
+            if constexpr (CG > 1) {
+              red_s[threadIdx.x] = o;
+            }
+            __syncthreads();
+            if (cg == 0 && hg * GP + h < G) {
+              if constexpr (CG > 1) {
+                for (int k = 1; k < CG; ++k) {
+                  const float4 r = red_s[k * PAIRS + pbase];
+                  o.x += r.x;
+                  o.y += r.y;
+                  o.z += r.z;
+                  o.w += r.w;
+                }
+              }
+              const float M = head_s[2 * h];
+              const float Ls = head_s[2 * h + 1];
+              const float inv = Ls > 0.f ? 1.f / Ls : 0.f;
+              const int hq = g * G + hg * GP + h;
+              *reinterpret_cast<float4*>(a.out + (static_cast<int64_t>(b) * a.Hq + hq) * D + d) =
+                  make_float4(o.x * inv, o.y * inv, o.z * inv, o.w * inv);
+              if (d == 0 && a.lse != nullptr)
+                a.lse[static_cast<int64_t>(b) * a.Hq + hq] =
+                    Ls > 0.f ? (M + __builtin_log2f(Ls)) * 0.69314718055994531f : NEG_INF;
+            }
+            __syncthreads();
+          }
         }
         if (threadIdx.x == 0) store_coherent_i(a.counters + grp, 0);  // ready for the next call
       }
