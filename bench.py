@@ -139,7 +139,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--replicas", type=int, default=0,
-                    help="device copies of the pool rotated per step (0: enough for 2 GiB)")
+                    help="device copies of the pool rotated per step (0: at least 3 and "
+                         "enough for 2 GiB)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--host-pool", action="store_true",
                     help="also time the decode over a host-resident (pinned, mapped) pool")
@@ -164,9 +165,11 @@ def main():
     case = wls[args.workload]()
     dc0 = dev.upload(case)
     pool_bytes = dc0.k_pool.numel() * dc0.k_pool.element_size() * 2
-    R = args.replicas or max(1, -(-(2 << 30) // pool_bytes))
-    # Distinct device copies (different addresses) so successive steps do not
-    # hit data a previous step left in the 256 MB Infinity Cache.
+    R = args.replicas or max(3, -(-(2 << 30) // pool_bytes))
+    # Distinct device copies (different addresses), taken in turn, so a step
+    # never finds in the 256 MB Infinity Cache what an earlier step read: at
+    # least 3, so two other replicas' traffic separates two uses of one, and
+    # enough for 2 GiB of pools.
     reps = [dc0]
     for _ in range(R - 1):
         reps.append(dev.DeviceCase(case, dc0.q.clone(), dc0.k_pool.clone(), dc0.v_pool.clone(),
