@@ -53,7 +53,7 @@
  *     recent_window == 0, or a workspace smaller than kvsp_workspace_bytes.
  *     A failed kernel launch returns KVSP_ERR_HIP.
  *   - Device data is trusted: block-table entries must lie in
- *     [0, num_phys_blocks), context_lens in [1, max_blocks_per_seq *
+ *     [0, num_phys_blocks), context_lens in [0, max_blocks_per_seq *
  *     block_size], values finite. Violations are undefined behaviour.
  *
  * Memory layouts (row-major, innermost last)
@@ -197,7 +197,9 @@ kvsp_status kvsp_score_topk(const kvsp_layout* layout, const kvsp_select_params*
  * [0, L), with logits scale * <q, K> (scale <= 0 means 1/sqrt(head_dim)),
  * accumulating in float32, and writes the normalised output and its
  * log-sum-exp. `selected` holds ascending candidate ids < C as written by
- * kvsp_score_topk; params supplies recent_window (C depends on it). */
+ * kvsp_score_topk; params supplies recent_window (C depends on it). A
+ * sequence with no cached token attends nothing: its out is 0 and its lse
+ * -inf. */
 kvsp_status kvsp_sparse_decode(const kvsp_layout* layout, const kvsp_select_params* params,
                                const void* q, const void* k_pool, const void* v_pool,
                                const int32_t* block_table, const int32_t* context_lens,

@@ -142,7 +142,11 @@ def check_outputs(case, r_or, gpu, b, sel_g, heads=None):
     for h in hs:
         err = float(np.max(np.abs(gpu["out"][b, h].astype(np.float64) - ref_out[h])))
         assert err <= tol, f"b={b} h={h}: max-abs {err:.3e} > {tol}"
-        lerr = abs(float(gpu["lse"][b, h]) - ref_lse[h])
+        g_lse, r_lse = float(gpu["lse"][b, h]), float(ref_lse[h])
+        if np.isneginf(r_lse):  # nothing attended (an empty sequence): out = 0, lse = -inf
+            assert np.isneginf(g_lse), f"b={b} h={h}: lse {g_lse} for an empty sequence"
+            continue
+        lerr = abs(g_lse - r_lse)
         assert lerr <= LSE_TOL, f"b={b} h={h}: lse off by {lerr:.3e}"
 
 

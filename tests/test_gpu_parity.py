@@ -253,3 +253,25 @@ def test_uncommon_shapes(dtype, Hq, Hkv, D, P, ctx):
                         num_phys=len(ctx) * -(-max(ctx) // P) + 40, keep_num=1, keep_den=5,
                         keep_floor=2, recent_window=P + 7)
     H.full_parity(case)
+
+
+def test_empty_sequences_in_a_batch():
+    # sequences with no cached token attend nothing: out = 0 and lse = -inf
+    # (the oracle's definition), no block is selected and no span emitted;
+    # their neighbours in the batch are unaffected
+    case = wl.make_case("empty", seed=74, B=4, Hq=8, Hkv=2, D=128, P=16, dtype="bf16",
+                        ctx_lens=[0, 700, 0, 37], shuffle=True, num_phys=4 * 44 + 8, top_k=3,
+                        keep_floor=1, recent_window=32)
+    gpu, r_or = H.full_parity(case)
+    for b in (0, 2):
+        assert not gpu["out"][b].any() and np.isneginf(gpu["lse"][b]).all()
+        assert gpu["num_selected"][b] == 0 and gpu["num_spans"][b] == 0
+
+
+def test_largest_block_table():
+    # 16384 blocks of 16 tokens (262144 tokens), the table-size limit: the
+    # two-kernel selection at 16 candidates per thread of 16 wavefronts
+    case = wl.make_case("max-table", seed=75, B=1, Hq=2, Hkv=1, D=64, P=16, dtype="fp16",
+                        ctx_lens=[16384 * 16], top_k=40, keep_floor=1, recent_window=100)
+    assert case.max_blocks == 16384
+    H.full_parity(case)

@@ -160,3 +160,18 @@ def test_head_mask_limits_work():
     full = _run(case)
     assert np.array_equal(r["out"][0, 3], full["out"][0, 3])
     assert np.isnan(r["out"][0, 2]).all()
+
+
+def test_empty_sequence_step():
+    # a sequence with no cached token: no candidate, nothing selected, no
+    # span, and attention over the empty set gives out = 0, lse = -inf
+    # (the empty-merge convention pinned above)
+    case = wl.make_case("empty-oracle", seed=11, B=2, Hq=2, Hkv=1, D=64, P=16, dtype="fp32",
+                        ctx_lens=[0, 40], max_blocks=3, top_k=1, keep_floor=1, recent_window=8)
+    summ = oracle.summaries(case.dtype, case.k_pool, case.block_table, case.ctx_lens, 1, 16, 64)
+    r = oracle.decode_step(case.dtype, case.q, case.k_pool, case.v_pool, case.block_table,
+                           case.ctx_lens, summ, Hkv=1, P=16, **case.select_params)
+    assert r["plan"][0].tolist() == [0, 0, 1, 0, 0]
+    assert r["nspans"][0] == 0
+    assert not r["out"][0].any() and np.isneginf(r["lse"][0]).all()
+    assert np.isfinite(r["lse"][1]).all()
