@@ -39,7 +39,12 @@ constexpr int kDecodeMaxChunks = 64;
 #ifndef KVSP_DECODE_MIN_GP
 #define KVSP_DECODE_MIN_GP 4
 #endif
-constexpr int kScoreTargetWorkgroups = 512;
+// Scoring workgroups a launch aims for (a sequence's candidates are split
+// into whole waves' worth of blocks).
+#ifndef KVSP_SCORE_TARGET_WORKGROUPS
+#define KVSP_SCORE_TARGET_WORKGROUPS 512
+#endif
+constexpr int kScoreTargetWorkgroups = KVSP_SCORE_TARGET_WORKGROUPS;
 constexpr int kDecodeMaxWorkgroups = KVSP_DECODE_MAX_WORKGROUPS;
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }

@@ -82,12 +82,6 @@ __device__ __forceinline__ uint4 load16_stream(const void* p) {
 // DPP row permutations and the gfx950 permlane16/32 swaps move data between
 // lanes inside the VALU, without the LDS round trip of ds_bpermute.
 
-__device__ __forceinline__ float lane_xor(float v, int mask) { return __shfl_xor(v, mask, kWave); }
-
-__device__ __forceinline__ double lane_xor(double v, int mask) {
-  return __shfl_xor(v, mask, kWave);
-}
-
 template <int CTRL, int ROW_MASK = 0xf, int BANK_MASK = 0xf, bool BOUND_ZERO = true>
 __device__ __forceinline__ uint32_t dpp_u32(uint32_t x) {
   return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(x), CTRL, ROW_MASK,
@@ -194,7 +188,6 @@ __device__ __forceinline__ float group_max(float v) {
   return v;
 }
 
-__device__ __forceinline__ double wave_sum(double v) { return group_sum<kWave>(v); }
 
 // Inclusive prefix sum over the wave (DPP row shifts and row broadcasts).
 __device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x) {
