@@ -112,15 +112,15 @@ void kvsp_oracle_widen(int dtype, const void* src, int64_t n, double* dst) {
 //   n   = ceil(L / P) logical blocks.
 //   The exact recency window [DKV] is the token range [C*P, L) with
 //   C = floor(max(0, L - W) / P): the last W tokens, widened down to a block
-//   boundary so that the blocks before it are whole. Those C blocks are the
-//   "historical" candidate blocks that [SparPR-QA] scores.
+//   boundary so that the blocks before it are whole. Those C older blocks
+//   are the candidates that [SparPR-QA] scores.
 //   k_req = top_k if top_k > 0, else ceil(C * keep_num / keep_den) (a keep
 //           ratio given as an exact fraction; integer arithmetic).
 //   k_eff = min(max(k_req, keep_floor), C)   — the Minimum Keep Floor bounds
 //           the budget from below [SparPR-BUD]; there are only C candidates.
-//   use_dense = C > 0 and k_eff / C > gamma_num / gamma_den: the sparse path
-//           is no longer clearly cheaper once the kept fraction exceeds the
-//           Dense Fallback Threshold γ [SparPR-REC].
+//   use_dense = C > 0 and k_eff / C > gamma_num / gamma_den: above the Dense
+//           Fallback Threshold γ the kept fraction is too large for the
+//           sparse path to pay off, and the step goes dense [SparPR-REC].
 // out = {n, C, k_req, k_eff, use_dense}.
 void kvsp_oracle_plan(int32_t L, int32_t P, int32_t W, int32_t top_k, int32_t keep_num,
                       int32_t keep_den, int32_t keep_floor, int32_t gamma_num,

@@ -1,7 +1,7 @@
 // Step 1: per-block mean-key summaries (SparPR news page, "Three decisions
 // rather than one compression ratio", paragraph "Query-Aware key-block
-// selection": every historical block keeps a compact precomputed summary, the
-// mean key vector, resident on the GPU).
+// selection": each older block carries a small summary made ahead of time,
+// its mean key, kept in GPU memory).
 //
 // One workgroup per (sequence, logical block); its four waves split the KV
 // heads. A (block, KV head) tile is P rows of D elements, contiguous in the
