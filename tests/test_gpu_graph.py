@@ -64,3 +64,54 @@ def test_graph_replays_match_eager(name, make):
         for k in KEYS:
             assert np.array_equal(got[k], eager[k]), f"replay {rep}: {k} differs"
     assert np.array_equal(_snapshot(other)["out"], eager["out"])
+
+
+def test_graph_of_append_score_decode_replays():
+    # a whole decode-loop step in one graph: append each sequence's token at
+    # its last position (completing the block), then score, select and
+    # attend. The appended rows are the rows already there, so every replay
+    # must reproduce the eager step exactly, pools and summaries included.
+    case = wl.c5(keep="1/32", B=8, L=4096)
+    H.note("[graph] append + step, serving-small")
+    dc = dev.upload(case)
+    buf = dev.alloc_buffers(dc)
+    dev.build_summaries(dc, buf)
+    ctx = dc.ctx_lens.long()
+    bt = dc.block_table.long()
+    phys = bt[torch.arange(case.B, device=bt.device), (ctx - 1) // case.P]
+    t = (ctx - 1) % case.P
+    k_new = dc.k_pool[phys, :, t].contiguous()
+    v_new = dc.v_pool[phys, :, t].contiguous()
+    pos = (ctx - 1).to(torch.int32)
+
+    def step():
+        dev.append_kv(dc, buf, k_new, v_new, pos)
+        dev.decode_step(dc, buf)
+
+    step()
+    torch.cuda.synchronize()
+    eager = _snapshot(buf)
+    summ0 = buf.summaries.clone()
+    k0 = dc.k_pool.clone()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    torch.cuda.synchronize()
+    for rep in range(3):
+        buf.selected.fill_(-1)
+        buf.spans.fill_(-1)
+        for k in ("out", "lse", "scores", "num_selected", "num_spans", "use_dense"):
+            getattr(buf, k).zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        got = _snapshot(buf)
+        for k in KEYS:
+            assert np.array_equal(got[k], eager[k]), f"replay {rep}: {k} differs"
+        assert torch.equal(buf.summaries, summ0) and torch.equal(dc.k_pool, k0)
