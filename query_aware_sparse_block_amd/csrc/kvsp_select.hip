@@ -299,10 +299,25 @@ __device__ __forceinline__ void select_sequence_r(const TopkArgs& a, int b, Topk
     }
   };
   float raw[RMAX];
+  if constexpr (COHERENT && RMAX >= 4) {
+    // RMAX consecutive scores as 16-byte loads (a range-checked buffer: past
+    // the row's end they read 0; slots r >= R are never used).
+    const __amdgpu_buffer_rsrc_t rs =
+        coherent_rsrc(a.scores + row, static_cast<uint32_t>(a.max_blocks) * sizeof(float));
 #pragma unroll
-  for (int r = 0; r < RMAX; ++r) {
-    const int j = jbase + r;
-    raw[r] = (r < R && j < a.max_blocks) ? score_at(j) : 0.f;
+    for (int q = 0; q < RMAX / 4; ++q) {
+      const float4 v = load_coherent4(rs, static_cast<uint32_t>(jbase + 4 * q) * sizeof(float));
+      raw[4 * q + 0] = v.x;
+      raw[4 * q + 1] = v.y;
+      raw[4 * q + 2] = v.z;
+      raw[4 * q + 3] = v.w;
+    }
+  } else {
+#pragma unroll
+    for (int r = 0; r < RMAX; ++r) {
+      const int j = jbase + r;
+      raw[r] = (r < R && j < a.max_blocks) ? score_at(j) : 0.f;
+    }
   }
   const float raw_prev = (jbase >= 1 && jbase - 1 < a.max_blocks) ? score_at(jbase - 1) : 0.f;
   const float raw_next = jbase + R < a.max_blocks ? score_at(jbase + R) : 0.f;
