@@ -178,10 +178,13 @@ static hipError_t launch_score_v(const ScoreArgs& a, hipStream_t stream) {
 // per block, and VPL, the fewest of 8, 16 or 32 vectors per lane that cover
 // the row (16 at most below 64 lanes).
 constexpr int kScoreVecPerLane = 8;
+#ifndef KVSP_SCORE_MIN_VPL
+#define KVSP_SCORE_MIN_VPL 8
+#endif
 ScoreShape score_shape(int Hkv, int D) {
   const int nvec = Hkv * D / 4;
-  ScoreShape sh{2, kScoreVecPerLane};
-  while (sh.lg < kWave && 2 * sh.lg * kScoreVecPerLane <= nvec) sh.lg *= 2;
+  ScoreShape sh{2, KVSP_SCORE_MIN_VPL};
+  while (sh.lg < kWave && 2 * sh.lg * KVSP_SCORE_MIN_VPL <= nvec) sh.lg *= 2;
   while (sh.lg * sh.vpl < nvec) sh.vpl *= 2;
   return sh;
 }
@@ -190,7 +193,7 @@ ScoreShape score_shape(int Hkv, int D) {
 template <typename F>
 static hipError_t with_score_shape(int Hkv, int D, F&& f) {
   const ScoreShape sh = score_shape(Hkv, D);
-  const bool wide = sh.vpl > kScoreVecPerLane;
+  const bool wide = sh.vpl >= 16;
   switch (sh.lg) {
     case 2: return wide ? f.template run<2, 16>() : f.template run<2, 8>();
     case 4: return wide ? f.template run<4, 16>() : f.template run<4, 8>();
