@@ -14,7 +14,8 @@
 // four wavefronts take the chunk's sub-tiles (SUB tokens: 4 KiB of keys and
 // as much of values, at least 16 tokens) in turn, each with its own online softmax, and merge
 // through LDS at the end. One-head items keep two sub-tiles in flight per
-// wavefront and read them non-temporally; GQA items keep one.
+// wavefront, GQA items one; K/V are read non-temporally unless several head
+// groups share a KV head.
 // Workgroups walk the items with a grid stride, so any mix of sparse and
 // dense sequences fills the chip.
 //
@@ -43,14 +44,10 @@ namespace kvsp {
 #define KVSP_SUB_TILE_BYTES 4096
 #endif
 // Work items of at most this many heads load sub-tile i+1 while they compute
-// sub-tile i, and read K/V with non-temporal loads. Measured: both help
-// one-head items (little compute per byte, registers to spare) and cost
-// time on GQA items, whose head groups may share a KV head through the caches.
+// sub-tile i. Measured: it helps one-head items (little compute per byte,
+// registers to spare) and costs GQA items occupancy.
 #ifndef KVSP_PIPELINE_MAX_GP
 #define KVSP_PIPELINE_MAX_GP 1
-#endif
-#ifndef KVSP_STREAM_MAX_GP
-#define KVSP_STREAM_MAX_GP 1
 #endif
 // Groups of at most this many chunks are merged by wave 0 alone, in registers.
 constexpr int kFastMergeChunks = 8;
@@ -162,7 +159,10 @@ __device__ __forceinline__ int k_elem_offset(int lane, int s) {
   }
 }
 
-template <typename T, int D, int GP>
+// STREAM: read K/V with non-temporal loads. The launch picks it when every KV
+// head is read by one head group only (nothing to reuse from the caches);
+// when split head groups share a KV head, default loads let them reuse it.
+template <typename T, int D, int GP, bool STREAM>
 __global__ __launch_bounds__(256) void attend_kernel(DecodeArgs a) {
   using S = DecodeShape<T, D>;
   constexpr int E = S::E;
@@ -253,7 +253,7 @@ __global__ __launch_bounds__(256) void attend_kernel(DecodeArgs a) {
     const uint32_t v_lane_off = static_cast<uint32_t>((rg * D + col) * E);
 
     auto kv_load = [](const char* p) {
-      if constexpr (GP <= KVSP_STREAM_MAX_GP) {
+      if constexpr (STREAM) {
         return load16_stream(p);
       } else {
         return load16(p);
@@ -659,8 +659,13 @@ __global__ __launch_bounds__(256) void attend_kernel(DecodeArgs a) {
 
 template <typename T, int D, int GP>
 static hipError_t launch_decode_t(const DecodeArgs& a, int num_wgs, hipStream_t stream) {
-  hipLaunchKernelGGL((attend_kernel<T, D, GP>), dim3(num_wgs), dim3(kDecodeWaves * kWave), 0,
-                     stream, a);
+  if (a.n_head_groups == 1) {
+    hipLaunchKernelGGL((attend_kernel<T, D, GP, true>), dim3(num_wgs), dim3(kDecodeWaves * kWave),
+                       0, stream, a);
+  } else {
+    hipLaunchKernelGGL((attend_kernel<T, D, GP, false>), dim3(num_wgs), dim3(kDecodeWaves * kWave),
+                       0, stream, a);
+  }
   return hipGetLastError();
 }
 
