@@ -45,6 +45,10 @@ constexpr int kDecodeMaxChunks = 64;
 #define KVSP_SCORE_TARGET_WORKGROUPS 512
 #endif
 constexpr int kScoreTargetWorkgroups = KVSP_SCORE_TARGET_WORKGROUPS;
+// Calls reading more summary bytes than this use non-temporal loads for them:
+// measured faster for the 128 MiB of the serving shape, slower for the 8 MiB
+// of the OPT-like batch, which can stay in the 256 MB Infinity Cache.
+constexpr int64_t kScoreStreamBytes = int64_t(64) << 20;
 constexpr int kDecodeMaxWorkgroups = KVSP_DECODE_MAX_WORKGROUPS;
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
@@ -270,6 +274,9 @@ kvsp_status kvsp_score_topk(const kvsp_layout* layout, const kvsp_select_params*
   const int per_pass = 64 / score_shape(l.num_kv_heads, l.head_dim).lg;  // blocks per wave pass
   bpw = (bpw + per_pass - 1) / per_pass * per_pass;
   sa.blocks_per_wave = static_cast<int>(bpw > 256 ? 256 : bpw);
+  // Summary sets beyond this size are streamed (read once, not worth caching).
+  const int64_t summary_bytes = total_blocks * l.num_kv_heads * l.head_dim * 4;
+  sa.stream_rows = summary_bytes > kScoreStreamBytes ? 1 : 0;
   sa.top_k = p.top_k;
   sa.keep_num = p.keep_num;
   sa.keep_den = p.keep_den;

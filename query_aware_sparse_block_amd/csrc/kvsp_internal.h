@@ -36,6 +36,7 @@ struct ScoreArgs {
   float* scores;  // [B][max_blocks]
   int32_t B, Hq, Hkv, D, P, max_blocks;
   int32_t blocks_per_wave;
+  int32_t stream_rows;  // 1: read summary rows with non-temporal loads
   int32_t top_k, keep_num, keep_den, keep_floor, recent_window, gamma_num, gamma_den;
 };
 

@@ -35,6 +35,7 @@ namespace kvsp {
 // fly while the previous one is reduced. This scores the workgroup's block range of sequence b and
 // returns C (the sequence's candidate count). COHERENT stores make the scores
 // visible to other workgroups of the same launch.
+
 template <typename T, int LG, int VPL, bool COHERENT>
 __device__ __forceinline__ int score_blocks(const ScoreArgs& a, double* qbar, int b) {
   const int lane = threadIdx.x % kWave;
@@ -96,14 +97,23 @@ __device__ __forceinline__ int score_blocks(const ScoreArgs& a, double* qbar, in
   // The first pass reads its block-table entries itself (`direct`), so its
   // summary loads leave before the workgroup barrier that publishes qbar.
   const int nvec = row / 4;
+  // Large summary sets are read once per call with non-temporal loads
+  // (a.stream_rows, uniform); small ones may stay cached between calls.
   auto issue = [&](int jb, float4 (&sv)[VPL], bool direct) {
     const int j = jb + slot;
     int64_t phys = 0;
     if (j < j1) phys = direct ? a.block_table[trow + j] : phys_lds[j - first];
     const float4* srow = reinterpret_cast<const float4*>(a.summaries + phys * row);
+    if (a.stream_rows) {
 #pragma unroll
-    for (int v = 0; v < VPL; ++v)
-      sv[v] = (j < j1 && gl + LG * v < nvec) ? srow[gl + LG * v] : make_float4(0.f, 0.f, 0.f, 0.f);
+      for (int v = 0; v < VPL; ++v)
+        sv[v] = (j < j1 && gl + LG * v < nvec) ? __builtin_bit_cast(float4, load16_stream(srow + gl + LG * v))
+                                              : make_float4(0.f, 0.f, 0.f, 0.f);
+    } else {
+#pragma unroll
+      for (int v = 0; v < VPL; ++v)
+        sv[v] = (j < j1 && gl + LG * v < nvec) ? srow[gl + LG * v] : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
   };
   auto consume = [&](int jb, const float4 (&sv)[VPL]) {
     double acc = 0.0;
