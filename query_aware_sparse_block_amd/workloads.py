@@ -183,6 +183,8 @@ def make_case(name, *, seed, B, Hq, Hkv, D, P, dtype, ctx_lens, values="iid", sh
                  older than the recent window, has keys 0.8*u_g + 0.6*z with a
                  per-head direction u_g ~ N(0, I); every query head h reads
                  0.8*u_g(h) + 0.6*z_h. All values stay N(0,1) marginally.
+      "lowrank"  every (block, KV head) is jointly low-rank in K|V (see
+                 ``_lowrank_transforms``), the premise of the DKV codec.
     """
     ctx_lens = np.asarray(ctx_lens, np.int32).reshape(B)
     if max_blocks is None:
@@ -250,6 +252,9 @@ def make_case(name, *, seed, B, Hq, Hkv, D, P, dtype, ctx_lens, values="iid", sh
             for phys, b in phys_of.items():
                 if b0 <= phys < b0 + x.shape[0]:
                     x[phys - b0] = rho * u[b][:, None, :] + rest * x[phys - b0]
+    elif values == "lowrank":
+        meta["n_spikes"] = int(params.get("n_spikes", 8))
+        k_transform, v_transform = _lowrank_transforms(seed, Hkv, P, D, params)
     elif values != "iid":
         raise ValueError(values)
 
@@ -258,6 +263,54 @@ def make_case(name, *, seed, B, Hq, Hkv, D, P, dtype, ctx_lens, values="iid", sh
     return Case(name=name, dtype=dtype, B=B, Hq=Hq, Hkv=Hkv, D=D, P=P, q=encode(q32, dtype),
                 k_pool=k_pool, v_pool=v_pool, block_table=bt, ctx_lens=ctx_lens, meta=meta,
                 **params)
+
+
+LOWRANK_RANK = 32        # planted joint K|V rank per (block, KV head)
+LOWRANK_NOISE = 0.05     # iid noise standard deviation
+LOWRANK_SPIKE = 6.0      # norm of each planted distinctive token's K|V offset
+
+
+def _lowrank_block(seed: int, phys: int, Hkv: int, P: int, D: int, n_spikes: int):
+    """Per-physical-block draws shared by the K and V transforms:
+    coefficients A [Hkv][P][32], bases B [Hkv][2D][32], means mu [Hkv][2D]
+    and spike offsets [Hkv][P][2D] (zero except n_spikes rows per head,
+    never token 0)."""
+    rng = _rng(seed, 8, phys)
+    r = LOWRANK_RANK
+    A = rng.standard_normal((Hkv, P, r))
+    Bm = rng.standard_normal((Hkv, 2 * D, r))
+    mu = rng.standard_normal((Hkv, 2 * D))
+    spikes = np.zeros((Hkv, P, 2 * D))
+    for g in range(Hkv):
+        rows = rng.choice(np.arange(1, P), size=min(n_spikes, P - 1), replace=False)
+        for t in rows:
+            u = rng.standard_normal(2 * D)
+            spikes[g, t] = LOWRANK_SPIKE * u / np.linalg.norm(u)
+    return A, Bm, mu, spikes
+
+
+def _lowrank_transforms(seed, Hkv, P, D, params):
+    """K|V rows of (block p, head g): mu + amp * A diag(s) B^T + noise + spikes,
+    with s_j falling geometrically from 1 to 1/2 over the 32 planted
+    directions and amp setting the signal's per-entry variance to 1. The
+    iid N(0,1) pool draw, scaled by LOWRANK_NOISE, is the noise. The spikes
+    are the distinctive tokens; their count is ``n_spikes`` (default 8)."""
+    n_spikes = int(params.pop("n_spikes", 8))
+    s = 0.5 ** (np.arange(LOWRANK_RANK) / (LOWRANK_RANK - 1))
+    amp = 1.0 / np.sqrt(np.sum(s * s))
+
+    def make(part):
+        lo, hi = (0, D) if part == 0 else (D, 2 * D)
+
+        def tf(b0, x):
+            for i in range(x.shape[0]):
+                A, Bm, mu, spikes = _lowrank_block(seed, b0 + i, Hkv, P, D, n_spikes)
+                sig = amp * np.einsum("gtr,gdr->gtd", A * s, Bm[:, lo:hi])
+                x[i] = (mu[:, None, lo:hi] + sig + spikes[:, :, lo:hi]
+                        + LOWRANK_NOISE * x[i]).astype(np.float32)
+        return tf
+
+    return make(0), make(1)
 
 
 def _ratio(keep) -> tuple[int, int]:
@@ -331,6 +384,106 @@ def c5(keep="1/32", B=64, L=32768, seed=None, workers=None) -> Case:
                      P=64, dtype="bf16", ctx_lens=[L] * B, shuffle=True,
                      num_phys=B * max_blocks, workers=workers, keep_num=num, keep_den=den,
                      recent_window=0, gamma_num=3, gamma_den=5)
+
+
+def c4_dkv(L=65536, n_resid=16, seed=None) -> Case:
+    """The c4 shape (Qwen2.5-1.5B-like, 256-token blocks, top-16 + 1024-token
+    window) with jointly low-rank K|V blocks holding ``n_resid`` distinctive
+    tokens each: the workload of the DKV codec (DKV abstract)."""
+    vid = {4096: 0, 8192: 1, 16384: 2, 32768: 3, 65536: 4}.get(L, 9)
+    case = make_case(f"c4dkv-L{L}-R{n_resid}", seed=4500 + 10 * vid if seed is None else seed,
+                     B=1, Hq=12, Hkv=2, D=128, P=256, dtype="bf16", ctx_lens=[L],
+                     values="lowrank", n_spikes=n_resid, top_k=16, recent_window=1024)
+    case.meta["n_resid"] = n_resid
+    return case
+
+
+# ---- DKV compressed-block records (byte layout of the C ABI) ---------------
+
+DKV_RANK = 32
+
+
+def dkv_record_layout(D: int, P: int, elem_bytes: int, n_resid: int, rank: int = DKV_RANK):
+    """Byte offsets of one (block, KV head) record and its padded size:
+    anchor K and V rows (cache dtype), basis [rank][2D] fp32, coefficients
+    [P][rank] fp32, residual K rows and V rows [n_resid][D] (cache dtype),
+    residual token offsets [n_resid] int32; the record is padded to 256 B."""
+    def up(x, a):
+        return (x + a - 1) // a * a
+    off = {"anchor": 0}
+    off["basis"] = up(2 * D * elem_bytes, 16)
+    off["coef"] = off["basis"] + rank * 2 * D * 4
+    off["resid_k"] = off["coef"] + P * rank * 4
+    off["resid_v"] = off["resid_k"] + n_resid * D * elem_bytes
+    off["resid"] = off["resid_v"] + n_resid * D * elem_bytes
+    off["bytes"] = up(off["resid"] + 4 * n_resid, 256)
+    return off
+
+
+def dkv_pack(fields: dict, dtype: str, P: int, n_resid: int) -> np.ndarray:
+    """One record as uint8 bytes. ``fields`` hold stored values: anchor_k,
+    anchor_v, resid_k, resid_v as the cache dtype's raw patterns (uint16 or
+    float32), basis and coef as float32, resid as int."""
+    D = fields["anchor_k"].shape[0]
+    E = ELEM_BYTES[dtype]
+    lay = dkv_record_layout(D, P, E, n_resid)
+    buf = np.zeros(lay["bytes"], np.uint8)
+
+    def put(off, arr):
+        b = np.ascontiguousarray(arr).view(np.uint8).reshape(-1)
+        buf[off:off + b.size] = b
+
+    put(lay["anchor"], fields["anchor_k"])
+    put(lay["anchor"] + D * E, fields["anchor_v"])
+    put(lay["basis"], np.asarray(fields["basis"], np.float32))
+    put(lay["coef"], np.asarray(fields["coef"], np.float32))
+    put(lay["resid_k"], fields["resid_k"])
+    put(lay["resid_v"], fields["resid_v"])
+    put(lay["resid"], np.asarray(fields["resid"], np.int32))
+    return buf
+
+
+def dkv_unpack(buf: np.ndarray, dtype: str, D: int, P: int, n_resid: int) -> dict:
+    """Inverse of ``dkv_pack`` (raw stored values, no arithmetic)."""
+    E = ELEM_BYTES[dtype]
+    lay = dkv_record_layout(D, P, E, n_resid)
+    raw_t = np.float32 if dtype == "fp32" else np.uint16
+    b = np.asarray(buf, np.uint8)
+
+    def get(off, count, t):
+        return b[off:off + count * np.dtype(t).itemsize].view(t).copy()
+
+    return dict(
+        anchor_k=get(lay["anchor"], D, raw_t),
+        anchor_v=get(lay["anchor"] + D * E, D, raw_t),
+        basis=get(lay["basis"], DKV_RANK * 2 * D, np.float32).reshape(DKV_RANK, 2 * D),
+        coef=get(lay["coef"], P * DKV_RANK, np.float32).reshape(P, DKV_RANK),
+        resid_k=get(lay["resid_k"], n_resid * D, raw_t).reshape(n_resid, D),
+        resid_v=get(lay["resid_v"], n_resid * D, raw_t).reshape(n_resid, D),
+        resid=get(lay["resid"], n_resid, np.int32),
+    )
+
+
+def dkv_random_records(case: Case, n_resid: int, seed: int, blocks=None) -> dict:
+    """Synthetic records for decode tests, keyed by (phys, g): random
+    anchors, bases, coefficients and residual rows (stored values), residual
+    offsets a sorted random subset of the block. ``blocks`` limits the
+    physical blocks (default: all)."""
+    rng = _rng(seed, 9)
+    D, P = case.D, case.P
+    recs = {}
+    phys_list = range(case.num_phys) if blocks is None else blocks
+    for phys in phys_list:
+        for g in range(case.Hkv):
+            def draw(shape):
+                return encode(rng.standard_normal(shape).astype(np.float32), case.dtype)
+            recs[(int(phys), g)] = dict(
+                anchor_k=draw(D), anchor_v=draw(D),
+                basis=(rng.standard_normal((DKV_RANK, 2 * D)) / np.sqrt(2 * D)).astype(np.float32),
+                coef=rng.standard_normal((P, DKV_RANK)).astype(np.float32),
+                resid_k=draw((n_resid, D)), resid_v=draw((n_resid, D)),
+                resid=np.sort(rng.choice(P, size=n_resid, replace=False)).astype(np.int32))
+    return recs
 
 
 def kv_bytes_per_token(layers: int, kv_heads: int, head_dim: int, elem_bytes: int) -> int:

@@ -1,0 +1,251 @@
+"""Pins for the DKV codec and decode oracle (DKV abstract: anchor token,
+rank-32 joint K|V truncated SVD of the deltas, worst-reconstructed tokens kept
+exactly, low-rank scoring, exact residual and recency tokens, log-sum-exp
+merge of the halves).
+
+Every pin checks the numpy oracle against something other than itself:
+1. Eckart-Young: the discarded energy equals the sum of the smallest
+   eigenvalues of X^T X (a symmetric eigensolver, not the SVD);
+2. blocks whose deltas have rank <= 32 decompress exactly, so the decode
+   equals exact attention computed by the C++ oracle;
+3. with every token residual the decode equals exact attention (C++ oracle)
+   over the selected blocks and the window, for any data;
+4. the residual set equals a brute-force top-R by errors from an eigenvector
+   projector, and equals the planted distinctive tokens of the low-rank
+   workload;
+5. a hand-built record decompresses to closed-form rows;
+6. with no block selected only the window is attended.
+A mutant copy of the module must fail at least one pin
+(``test_dkv_mutant_is_caught``)."""
+
+import importlib.util
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle import dkv as DKV
+from query_aware_sparse_block_amd import workloads as wl
+
+SRC = DKV.__file__
+
+
+def _eig_projector(X, r):
+    w, vecs = np.linalg.eigh(X.T @ X)
+    top = vecs[:, np.argsort(w)[::-1][:r]]
+    return top @ top.T, np.sort(w)[::-1]
+
+
+def pin_eckart_young(mod=DKV):
+    rng = np.random.default_rng(11)
+    P, D, r = 64, 16, 8
+    K = rng.standard_normal((P, D))
+    V = rng.standard_normal((P, D))
+    rec = mod.compress_block(K, V, r, 0)
+    X = np.concatenate([K - K[0], V - V[0]], axis=1)
+    lam = np.sort(np.linalg.eigvalsh(X.T @ X))[::-1]
+    X_hat = rec["coef"] @ rec["basis"]
+    assert np.isclose(np.sum((X - X_hat) ** 2), lam[r:].sum(), rtol=1e-9)
+    assert np.isclose(np.sum(rec["coef"] ** 2), lam[:r].sum(), rtol=1e-9)
+    assert np.allclose(rec["basis"] @ rec["basis"].T, np.eye(r), atol=1e-12)
+    assert np.all(rec["coef"][0] == 0.0)
+
+
+def pin_residual_brute_force(mod=DKV):
+    rng = np.random.default_rng(12)
+    P, D, r, R = 12, 3, 2, 3
+    for _ in range(5):
+        K = rng.standard_normal((P, D))
+        V = rng.standard_normal((P, D))
+        rec = mod.compress_block(K, V, r, R)
+        X = np.concatenate([K - K[0], V - V[0]], axis=1)
+        proj, _ = _eig_projector(X, r)
+        err = np.linalg.norm(X - X @ proj, axis=1)
+        best = sorted(range(P), key=lambda t: (-round(err[t], 9), t))[:R]
+        assert sorted(best) == list(rec["resid"])
+        assert np.array_equal(rec["resid_k"], K[sorted(best)])
+        assert np.array_equal(rec["resid_v"], V[sorted(best)])
+
+
+def pin_planted_spikes(mod=DKV):
+    case = wl.c4_dkv(L=2048, n_resid=8)
+    P, D = case.P, case.D
+    for phys in range(0, 4):
+        for g in range(case.Hkv):
+            K = wl.decode_f32(case.k_pool[phys, g], case.dtype)
+            V = wl.decode_f32(case.v_pool[phys, g], case.dtype)
+            rec = mod.compress_block(K, V, 32, 8)
+            _, _, _, spikes = wl._lowrank_block(case_seed(case), phys, case.Hkv, P, D, 8)
+            planted = np.nonzero(np.abs(spikes[g]).sum(axis=1))[0]
+            assert list(rec["resid"]) == sorted(planted.tolist())
+
+
+def case_seed(case):
+    return 4500 + 10 * {4096: 0, 8192: 1, 16384: 2, 32768: 3, 65536: 4}.get(
+        int(case.ctx_lens[0]), 9)
+
+
+def pin_hand_record(mod=DKV):
+    P, D, r = 8, 2, 3
+    basis = np.arange(r * 2 * D, dtype=np.float64).reshape(r, 2 * D) / 7.0
+    coef = np.zeros((P, r))
+    for t in range(1, P):
+        coef[t, t % r] = 1.0
+    rec = dict(anchor_k=np.array([1.0, -2.0]), anchor_v=np.array([0.5, 3.0]), basis=basis,
+               coef=coef, resid=np.array([5]), resid_k=np.array([[9.0, 9.0]]),
+               resid_v=np.array([[-9.0, 8.0]]))
+    K, V = mod.reconstruct_block(rec, P)
+    for t in range(P):
+        if t == 5:
+            assert np.array_equal(K[t], [9.0, 9.0]) and np.array_equal(V[t], [-9.0, 8.0])
+            continue
+        ek = rec["anchor_k"] + (basis[t % r, :D] if t else 0.0)
+        ev = rec["anchor_v"] + (basis[t % r, D:] if t else 0.0)
+        assert np.allclose(K[t], ek, rtol=0, atol=1e-15)
+        assert np.allclose(V[t], ev, rtol=0, atol=1e-15)
+
+
+def _small_case(dtype="fp32", L=(700, 513), seed=21):
+    return wl.make_case("dkv-small", seed=seed, B=len(L), Hq=4, Hkv=2, D=16, P=64, dtype=dtype,
+                        ctx_lens=list(L), shuffle=True, num_phys=2 * 12, max_blocks=12,
+                        recent_window=96, top_k=3)
+
+
+def _exact_reference(case, selected, nsel, scale):
+    """Exact attention over the selected blocks' tokens and the window, by the
+    C++ oracle."""
+    out = np.zeros((case.B, case.Hq, case.D))
+    lse = np.zeros((case.B, case.Hq))
+    G = case.Hq // case.Hkv
+    for b in range(case.B):
+        L = int(case.ctx_lens[b])
+        C = max(0, L - case.recent_window) // case.P
+        toks = [j * case.P + t for j in selected[b][: nsel[b]] for t in range(case.P)]
+        toks += list(range(C * case.P, L))
+        for h in range(case.Hq):
+            out[b, h], lse[b, h] = oracle.attend_tokens(
+                case.dtype, case.q[b, h], case.k_pool, case.v_pool, case.Hkv, case.P, case.D, h // G,
+                case.block_table[b], np.array(toks), scale)
+    return out, lse
+
+
+def _selection(case, seed):
+    rng = np.random.default_rng(seed)
+    sel, nsel = [], []
+    for b in range(case.B):
+        C = max(0, int(case.ctx_lens[b]) - case.recent_window) // case.P
+        k = min(3, C)
+        sel.append(sorted(rng.choice(C, size=k, replace=False).tolist()))
+        nsel.append(k)
+    return sel, nsel
+
+
+def _pools_f64(case):
+    return (wl.decode_f32(case.k_pool, case.dtype).astype(np.float64),
+            wl.decode_f32(case.v_pool, case.dtype).astype(np.float64))
+
+
+def pin_low_rank_blocks_decode_exactly(mod=DKV):
+    case = _small_case("fp32")
+    rng = np.random.default_rng(5)
+    P, D = case.P, case.D
+    for phys in range(case.num_phys):
+        for g in range(case.Hkv):
+            A = rng.standard_normal((P, 12))
+            A[0] = 0.0
+            base = rng.standard_normal(2 * D)
+            X = base + A @ rng.standard_normal((12, 2 * D))
+            case.k_pool[phys, g] = X[:, :D].astype(np.float32)
+            case.v_pool[phys, g] = X[:, D:].astype(np.float32)
+    kp, vp = _pools_f64(case)
+    recs = mod.compress_case(kp, vp, case.block_table, case.ctx_lens, Hkv=case.Hkv, P=P,
+                             recent_window=case.recent_window, rank=32, n_resid=0)
+    sel, nsel = _selection(case, 1)
+    scale = 1.0 / np.sqrt(D)
+    out, lse = mod.decode(wl.decode_f32(case.q, case.dtype), kp, vp, recs, case.block_table,
+                          case.ctx_lens, sel, nsel, Hkv=case.Hkv, P=P,
+                          recent_window=case.recent_window, scale=scale)
+    ref, ref_lse = _exact_reference(case, sel, nsel, scale)
+    assert np.allclose(out, ref, rtol=0, atol=1e-5)
+    assert np.allclose(lse, ref_lse, rtol=0, atol=1e-5)
+
+
+def pin_all_residual_equals_exact(mod=DKV):
+    for dtype in ("bf16", "fp16"):
+        case = _small_case(dtype, L=(640, 300), seed=22)
+        kp, vp = _pools_f64(case)
+        recs = mod.compress_case(kp, vp, case.block_table, case.ctx_lens, Hkv=case.Hkv,
+                                 P=case.P, recent_window=case.recent_window, rank=32,
+                                 n_resid=case.P)
+        sel, nsel = _selection(case, 2)
+        scale = 0.3
+        out, lse = mod.decode(wl.decode_f32(case.q, case.dtype), kp, vp, recs,
+                              case.block_table, case.ctx_lens, sel, nsel, Hkv=case.Hkv,
+                              P=case.P, recent_window=case.recent_window, scale=scale)
+        ref, ref_lse = _exact_reference(case, sel, nsel, scale)
+        assert np.allclose(out, ref, rtol=0, atol=1e-12)
+        assert np.allclose(lse, ref_lse, rtol=0, atol=1e-12)
+
+
+def pin_empty_selection_is_window_only(mod=DKV):
+    case = _small_case("bf16", L=(700, 64), seed=23)
+    kp, vp = _pools_f64(case)
+    sel = [[], []]
+    nsel = [0, 0]
+    out, lse = mod.decode(wl.decode_f32(case.q, case.dtype), kp, vp, {}, case.block_table,
+                          case.ctx_lens, sel, nsel, Hkv=case.Hkv, P=case.P,
+                          recent_window=case.recent_window, scale=0.25)
+    ref, ref_lse = _exact_reference(case, sel, nsel, 0.25)
+    assert np.allclose(out, ref, rtol=0, atol=1e-12)
+    assert np.allclose(lse, ref_lse, rtol=0, atol=1e-12)
+
+
+PINS = [pin_eckart_young, pin_residual_brute_force, pin_planted_spikes, pin_hand_record,
+        pin_low_rank_blocks_decode_exactly, pin_all_residual_equals_exact,
+        pin_empty_selection_is_window_only]
+
+
+@pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
+def test_dkv_pin(pin):
+    pin()
+
+
+MUTANTS = {
+    "V delta from K anchor": ("V - V[0]], axis=1)\n\n\ndef compress_block",
+                              "V - K[0]], axis=1)\n\n\ndef compress_block"),
+    "smallest singular vectors": ("basis[:r_eff] = vt[:r_eff]", "basis[:r_eff] = vt[-r_eff:]"),
+    "residuals best-reconstructed": ("key=lambda t: (-err[t], t)", "key=lambda t: (err[t], t)"),
+    "residual K not substituted": ('K[resid] = rec["resid_k"]', "K[resid] = K[resid]"),
+    "anchor not added back": ('K = rec["anchor_k"][None, :] + X_hat[:, :D]', "K = X_hat[:, :D]"),
+    "V from the K half": ('V = rec["anchor_v"][None, :] + X_hat[:, D:]',
+                          'V = rec["anchor_v"][None, :] + X_hat[:, :D]'),
+    "window skips a block": ("for j in range(C, n):", "for j in range(C + 1, n):"),
+    "window start rounded up": ("return max(0, L - W) // P", "return -(-max(0, L - W) // P)"),
+    "lse drops the max": ("return (e @ V) / l, m + np.log(l)", "return (e @ V) / l, np.log(l)"),
+    "coefficients from K only": ("coef = X @ basis.T",
+                                 "coef = np.concatenate([X[:, :D], 0 * X[:, D:]], axis=1) @ basis.T"),
+}
+
+
+def _load_mutant(tmp_path, name):
+    before, after = MUTANTS[name]
+    text = open(SRC).read()
+    assert text.count(before) == 1, f"mutation site for {name!r} not unique"
+    path = tmp_path / "dkv_mutant.py"
+    path.write_text(text.replace(before, after))
+    spec = importlib.util.spec_from_file_location(f"dkv_mutant_{abs(hash(name))}", path)
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    return mod
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_dkv_mutant_is_caught(name, tmp_path):
+    mod = _load_mutant(tmp_path, name)
+    failed = []
+    for pin in PINS:
+        try:
+            pin(mod)
+        except (AssertionError, ValueError, IndexError):
+            failed.append(pin.__name__)
+    assert failed, f"no pin catches mutant {name!r}"
