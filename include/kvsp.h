@@ -217,6 +217,82 @@ kvsp_status kvsp_dense_decode(const kvsp_layout* layout, const void* q, const vo
                               const int32_t* context_lens, float scale, float* out, float* lse,
                               void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* ---- DKV variant: compressed older blocks -----------------------------------
+ * DKV abstract ("DKV: Anchor + Low-Rank Differential KV-Cache Compression for
+ * Scalable Long-Context Inference"): every block older than the recency window
+ * is stored as one exact anchor token, a rank-32 truncated SVD of the joint
+ * key|value difference of its tokens from the anchor, and a budget of exact
+ * residual tokens (the rows the low-rank basis reconstructs worst). Decoding
+ * attends the routed blocks through the low-rank factors (keys are never
+ * decompressed), the residual tokens and the recency window exactly, and merges
+ * the halves by log-sum-exp. Routing uses kvsp_build_summaries (run before the
+ * blocks are compressed) and kvsp_score_topk as for the exact cache.
+ *
+ * Readings where the abstract is silent: the anchor is the block's first token;
+ * the SVD is of X = [K - k_anchor | V - v_anchor] (block_size x 2*head_dim);
+ * residual tokens are the n_resid rows of largest ||X_t - X_hat_t||.
+ *
+ * Record of one (physical block p, KV head g), at byte offset
+ * (p * num_kv_heads + g) * kvsp_dkv_record_bytes() of `records`:
+ *   anchor   [2][head_dim]            layout dtype: anchor K row, anchor V row
+ *   basis    [32][2*head_dim] float32 at offset align16(2*D*E): row j is the
+ *                                     j-th basis vector (K half, then V half)
+ *   coef     [block_size][32] float32 right after basis: X_t projected on the
+ *                                     basis (rows of residual tokens unused)
+ *   resid_k  [n_resid][head_dim]      layout dtype, right after coef
+ *   resid_v  [n_resid][head_dim]      layout dtype, right after resid_k
+ *   resid    [n_resid] int32          ascending token offsets within the block
+ *   padding to a multiple of 256 bytes.
+ * E is the element size of the layout dtype. A compressed token t of the block
+ * stands for the rows k_anchor + coef[t] . basis[:, :D] and
+ * v_anchor + coef[t] . basis[:, D:]; a residual token stands for its exact rows.
+ * Supported: block_size 64, 128 or 256; num_q_heads / num_kv_heads <= 16;
+ * 0 <= n_resid <= min(64, block_size). */
+typedef struct {
+  int32_t rank;        /* must be 32 */
+  int32_t n_resid;     /* exact residual tokens per block */
+  int32_t power_iters; /* kvsp_dkv_compress subspace iterations; 0 = default (10) */
+} kvsp_dkv_params;
+
+/* Bytes of one record (see above); 0 for unsupported arguments. */
+size_t kvsp_dkv_record_bytes(const kvsp_layout* layout, const kvsp_dkv_params* dkv);
+
+/* Bytes of device workspace kvsp_dkv_decode needs. Same rules as
+ * kvsp_workspace_bytes: zero-fill once before first use; calls that return
+ * KVSP_OK leave it reusable; calls sharing one workspace must not overlap. */
+size_t kvsp_dkv_workspace_bytes(const kvsp_layout* layout, const kvsp_dkv_params* dkv);
+
+/* DKV codec: for every sequence b and every logical block j < C (C = floor(max(0,
+ * L - recent_window) / P), the blocks wholly older than the window) writes the
+ * record of (block_table[b][j], g) for every KV head g from the exact K/V rows
+ * in the pools. The basis is computed in float32 by subspace iteration
+ * (power_iters rounds of X^T X applied to the basis, each followed by a
+ * re-orthonormalisation), started from a fixed pseudo-random basis; with a
+ * gap between the 32nd and 33rd singular values of X it converges to the
+ * truncated SVD's subspace. coef = X basis^T; residual tokens are the n_resid
+ * rows with the largest float32 reconstruction error (ties to the lower
+ * offset); anchor and residual rows are bit-exact copies. Records of other
+ * blocks are not touched. Needs no workspace. */
+kvsp_status kvsp_dkv_compress(const kvsp_layout* layout, const kvsp_dkv_params* dkv,
+                              int32_t recent_window, const void* k_pool, const void* v_pool,
+                              const int32_t* block_table, const int32_t* context_lens,
+                              void* records, hipStream_t stream);
+
+/* DKV decode: for every sequence b and query head h, attention over the tokens of
+ * the compressed blocks selected[b][0..num_selected[b]) (ascending ids < C, as
+ * from kvsp_score_topk) read through their records, followed by the exact
+ * window tokens [C*P, L) from the pools; logits scale * <q, k> (scale <= 0
+ * means 1/sqrt(head_dim)); float32 accumulation; normalised out and natural-log
+ * lse as for kvsp_sparse_decode. params supplies recent_window (the other
+ * selection fields are ignored; there is no dense fallback: older blocks exist
+ * only as records). An empty attended set gives out 0 and lse -inf. */
+kvsp_status kvsp_dkv_decode(const kvsp_layout* layout, const kvsp_select_params* params,
+                            const kvsp_dkv_params* dkv, const void* q, const void* k_pool,
+                            const void* v_pool, const void* records, const int32_t* block_table,
+                            const int32_t* context_lens, const int32_t* selected,
+                            const int32_t* num_selected, float scale, float* out, float* lse,
+                            void* workspace, size_t workspace_bytes, hipStream_t stream);
+
 /* Static description of a status code (never NULL). */
 const char* kvsp_status_string(kvsp_status status);
 

@@ -119,8 +119,10 @@ WorkspaceLayout workspace_layout(const kvsp_layout& l) {
 
 kvsp_status from_hip(hipError_t e) { return e == hipSuccess ? KVSP_OK : KVSP_ERR_HIP; }
 
+// window_only: attend only the exact window [C*P, L) of every sequence (the
+// exact half of the DKV decode); selected, num_selected and use_dense unused.
 kvsp_status run_decode(const kvsp_layout* layout, const kvsp_select_params* params, bool all_dense,
-                       const void* q, const void* k_pool, const void* v_pool,
+                       bool window_only, const void* q, const void* k_pool, const void* v_pool,
                        const int32_t* block_table, const int32_t* context_lens,
                        const int32_t* selected, const int32_t* num_selected,
                        const int32_t* use_dense, float scale, float* out, float* lse,
@@ -130,7 +132,7 @@ kvsp_status run_decode(const kvsp_layout* layout, const kvsp_select_params* para
   if (!all_dense && (st = check_params(params)) != KVSP_OK) return st;
   if (!q || !k_pool || !v_pool || !block_table || !context_lens || !out)
     return KVSP_ERR_INVALID_ARG;
-  if (!all_dense && (!selected || !num_selected)) return KVSP_ERR_INVALID_ARG;
+  if (!all_dense && !window_only && (!selected || !num_selected)) return KVSP_ERR_INVALID_ARG;
   const kvsp_layout& l = *layout;
   const WorkspaceLayout wl = workspace_layout(l);
   if (workspace == nullptr || workspace_bytes < wl.total) return KVSP_ERR_WORKSPACE;
@@ -141,9 +143,10 @@ kvsp_status run_decode(const kvsp_layout* layout, const kvsp_select_params* para
   a.v_pool = v_pool;
   a.block_table = block_table;
   a.context_lens = context_lens;
-  a.selected = all_dense ? nullptr : selected;
-  a.num_selected = all_dense ? nullptr : num_selected;
-  a.use_dense = all_dense ? nullptr : use_dense;
+  const bool no_sel = all_dense || window_only;
+  a.selected = no_sel ? nullptr : selected;
+  a.num_selected = no_sel ? nullptr : num_selected;
+  a.use_dense = no_sel ? nullptr : use_dense;
   a.out = out;
   a.lse = lse;
   a.part_acc = reinterpret_cast<float*>(static_cast<char*>(workspace) + wl.part_acc);
@@ -163,6 +166,86 @@ kvsp_status run_decode(const kvsp_layout* layout, const kvsp_select_params* para
   const float s = scale > 0.f ? scale : 1.0f / __builtin_sqrtf(static_cast<float>(l.head_dim));
   a.scale_log2 = s * 1.4426950408889634f;
   return from_hip(launch_decode(a, l.dtype, g.gp, g.num_wgs, stream));
+}
+
+// ---- DKV variant ------------------------------------------------------------------
+
+constexpr int kDkvRank = 32;
+constexpr int kDkvMaxResid = 64;
+constexpr int kDkvMaxHeads = 16;      // query heads per KV head (MFMA columns)
+constexpr int kDkvTargetItems = 256;  // decode work items a launch aims for
+constexpr int kDkvMaxChunks = 64;
+constexpr int kDkvDefaultIters = 10;
+
+struct DkvRecordLayout {
+  int32_t off_basis, off_coef, off_rk, off_rv, off_ridx;
+  size_t bytes;
+};
+
+size_t align_to(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+int elem_bytes(int dtype) { return dtype == KVSP_F32 ? 4 : 2; }
+
+DkvRecordLayout dkv_record_layout(const kvsp_layout& l, int n_resid) {
+  const size_t D = static_cast<size_t>(l.head_dim), P = static_cast<size_t>(l.block_size);
+  const size_t E = static_cast<size_t>(elem_bytes(l.dtype));
+  DkvRecordLayout r;
+  size_t off = align_to(2 * D * E, 16);
+  r.off_basis = static_cast<int32_t>(off);
+  off += kDkvRank * 2 * D * 4;
+  r.off_coef = static_cast<int32_t>(off);
+  off += P * kDkvRank * 4;
+  r.off_rk = static_cast<int32_t>(off);
+  off += static_cast<size_t>(n_resid) * D * E;
+  r.off_rv = static_cast<int32_t>(off);
+  off += static_cast<size_t>(n_resid) * D * E;
+  r.off_ridx = static_cast<int32_t>(off);
+  off += static_cast<size_t>(n_resid) * 4;
+  r.bytes = align_to(off, 256);
+  return r;
+}
+
+kvsp_status check_dkv(const kvsp_layout* l, const kvsp_dkv_params* p) {
+  kvsp_status st = check_layout(l);
+  if (st != KVSP_OK) return st;
+  if (p == nullptr) return KVSP_ERR_INVALID_ARG;
+  if (p->rank != kDkvRank) return KVSP_ERR_UNSUPPORTED;
+  if (p->n_resid < 0 || p->power_iters < 0 || p->power_iters > 1000) return KVSP_ERR_INVALID_ARG;
+  if (l->block_size < 64) return KVSP_ERR_UNSUPPORTED;
+  if (p->n_resid > kDkvMaxResid || p->n_resid > l->block_size) return KVSP_ERR_UNSUPPORTED;
+  if (l->num_q_heads / l->num_kv_heads > kDkvMaxHeads) return KVSP_ERR_UNSUPPORTED;
+  return KVSP_OK;
+}
+
+int dkv_chunks(const kvsp_layout& l) {
+  const int64_t pairs = static_cast<int64_t>(l.batch) * l.num_kv_heads;
+  int nc = 1;
+  while (pairs * nc < kDkvTargetItems && nc < kDkvMaxChunks && nc < l.max_blocks_per_seq) nc *= 2;
+  return nc;
+}
+
+struct DkvWorkspace {
+  size_t decode, out_w, lse_w, counters, part_acc, part_ml, total;
+};
+
+DkvWorkspace dkv_workspace(const kvsp_layout& l) {
+  DkvWorkspace w;
+  const size_t slots = static_cast<size_t>(l.batch) * l.num_kv_heads * dkv_chunks(l);
+  size_t off = 0;
+  w.decode = off;
+  off += workspace_layout(l).total;
+  w.out_w = off;
+  off += align_up(static_cast<size_t>(l.batch) * l.num_q_heads * l.head_dim * sizeof(float));
+  w.lse_w = off;
+  off += align_up(static_cast<size_t>(l.batch) * l.num_q_heads * sizeof(float));
+  w.counters = off;
+  off += align_up(static_cast<size_t>(l.batch) * l.num_kv_heads * sizeof(int32_t));
+  w.part_acc = off;
+  off += align_up(slots * kDkvMaxHeads * l.head_dim * sizeof(float));
+  w.part_ml = off;
+  off += align_up(slots * kDkvMaxHeads * 2 * sizeof(float));
+  w.total = off;
+  return w;
 }
 
 }  // namespace
@@ -317,7 +400,7 @@ kvsp_status kvsp_sparse_decode(const kvsp_layout* layout, const kvsp_select_para
                                const int32_t* selected, const int32_t* num_selected,
                                const int32_t* use_dense, float scale, float* out, float* lse,
                                void* workspace, size_t workspace_bytes, hipStream_t stream) {
-  return run_decode(layout, params, false, q, k_pool, v_pool, block_table, context_lens, selected,
+  return run_decode(layout, params, false, false, q, k_pool, v_pool, block_table, context_lens, selected,
                     num_selected, use_dense, scale, out, lse, workspace, workspace_bytes, stream);
 }
 
@@ -325,8 +408,117 @@ kvsp_status kvsp_dense_decode(const kvsp_layout* layout, const void* q, const vo
                               const void* v_pool, const int32_t* block_table,
                               const int32_t* context_lens, float scale, float* out, float* lse,
                               void* workspace, size_t workspace_bytes, hipStream_t stream) {
-  return run_decode(layout, nullptr, true, q, k_pool, v_pool, block_table, context_lens, nullptr,
+  return run_decode(layout, nullptr, true, false, q, k_pool, v_pool, block_table, context_lens, nullptr,
                     nullptr, nullptr, scale, out, lse, workspace, workspace_bytes, stream);
+}
+
+size_t kvsp_dkv_record_bytes(const kvsp_layout* layout, const kvsp_dkv_params* dkv) {
+  if (check_dkv(layout, dkv) != KVSP_OK) return 0;
+  return dkv_record_layout(*layout, dkv->n_resid).bytes;
+}
+
+size_t kvsp_dkv_workspace_bytes(const kvsp_layout* layout, const kvsp_dkv_params* dkv) {
+  if (check_dkv(layout, dkv) != KVSP_OK) return 0;
+  return dkv_workspace(*layout).total;
+}
+
+kvsp_status kvsp_dkv_compress(const kvsp_layout* layout, const kvsp_dkv_params* dkv,
+                              int32_t recent_window, const void* k_pool, const void* v_pool,
+                              const int32_t* block_table, const int32_t* context_lens,
+                              void* records, hipStream_t stream) {
+  kvsp_status st = check_dkv(layout, dkv);
+  if (st != KVSP_OK) return st;
+  if (recent_window < 0) return KVSP_ERR_INVALID_ARG;
+  if (!k_pool || !v_pool || !block_table || !context_lens || !records) return KVSP_ERR_INVALID_ARG;
+  const kvsp_layout& l = *layout;
+  const DkvRecordLayout r = dkv_record_layout(l, dkv->n_resid);
+  DkvCompressArgs a;
+  a.k_pool = k_pool;
+  a.v_pool = v_pool;
+  a.block_table = block_table;
+  a.context_lens = context_lens;
+  a.records = static_cast<char*>(records);
+  a.rec_bytes = static_cast<int64_t>(r.bytes);
+  a.off_basis = r.off_basis;
+  a.off_coef = r.off_coef;
+  a.off_rk = r.off_rk;
+  a.off_rv = r.off_rv;
+  a.off_ridx = r.off_ridx;
+  a.B = l.batch;
+  a.Hkv = l.num_kv_heads;
+  a.P = l.block_size;
+  a.max_blocks = l.max_blocks_per_seq;
+  a.recent_window = recent_window;
+  a.n_resid = dkv->n_resid;
+  a.power_iters = dkv->power_iters > 0 ? dkv->power_iters : kDkvDefaultIters;
+  const hipError_t e = launch_dkv_compress(a, l.dtype, l.head_dim, stream);
+  if (e == hipErrorNotSupported) return KVSP_ERR_UNSUPPORTED;
+  return from_hip(e);
+}
+
+kvsp_status kvsp_dkv_decode(const kvsp_layout* layout, const kvsp_select_params* params,
+                            const kvsp_dkv_params* dkv, const void* q, const void* k_pool,
+                            const void* v_pool, const void* records, const int32_t* block_table,
+                            const int32_t* context_lens, const int32_t* selected,
+                            const int32_t* num_selected, float scale, float* out, float* lse,
+                            void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  kvsp_status st = check_dkv(layout, dkv);
+  if (st != KVSP_OK) return st;
+  if (params == nullptr || params->recent_window < 0) return KVSP_ERR_INVALID_ARG;
+  if (!q || !k_pool || !v_pool || !records || !block_table || !context_lens || !selected ||
+      !num_selected || !out)
+    return KVSP_ERR_INVALID_ARG;
+  const kvsp_layout& l = *layout;
+  const DkvWorkspace ws = dkv_workspace(l);
+  if (workspace == nullptr || workspace_bytes < ws.total) return KVSP_ERR_WORKSPACE;
+  char* wsb = static_cast<char*>(workspace);
+  float* out_w = reinterpret_cast<float*>(wsb + ws.out_w);
+  float* lse_w = reinterpret_cast<float*>(wsb + ws.lse_w);
+  // The exact half: the window of every sequence, on the split-KV kernel.
+  kvsp_select_params wp = *params;
+  if (wp.keep_floor == 0 && wp.recent_window == 0) wp.keep_floor = 1;  // only the window is read
+  if (wp.keep_den <= 0) wp.keep_den = 1;
+  if (wp.gamma_den <= 0) wp.gamma_den = 1;
+  if (wp.top_k < 0) wp.top_k = 0;
+  if (wp.keep_num < 0) wp.keep_num = 0;
+  if (wp.keep_floor < 0) wp.keep_floor = 0;
+  if (wp.gamma_num < 0) wp.gamma_num = 0;
+  st = run_decode(layout, &wp, false, true, q, k_pool, v_pool, block_table, context_lens, nullptr,
+                  nullptr, nullptr, scale, out_w, lse_w, wsb + ws.decode, ws.out_w - ws.decode,
+                  stream);
+  if (st != KVSP_OK) return st;
+  const DkvRecordLayout r = dkv_record_layout(l, dkv->n_resid);
+  DkvDecodeArgs a;
+  a.q = q;
+  a.records = static_cast<const char*>(records);
+  a.block_table = block_table;
+  a.context_lens = context_lens;
+  a.selected = selected;
+  a.num_selected = num_selected;
+  a.out_w = out_w;
+  a.lse_w = lse_w;
+  a.out = out;
+  a.lse = lse;
+  a.part_acc = reinterpret_cast<float*>(wsb + ws.part_acc);
+  a.part_ml = reinterpret_cast<float*>(wsb + ws.part_ml);
+  a.counters = reinterpret_cast<int32_t*>(wsb + ws.counters);
+  a.rec_bytes = static_cast<int64_t>(r.bytes);
+  a.off_basis = r.off_basis;
+  a.off_coef = r.off_coef;
+  a.off_rk = r.off_rk;
+  a.off_rv = r.off_rv;
+  a.off_ridx = r.off_ridx;
+  a.B = l.batch;
+  a.Hq = l.num_q_heads;
+  a.Hkv = l.num_kv_heads;
+  a.P = l.block_size;
+  a.max_blocks = l.max_blocks_per_seq;
+  a.recent_window = params->recent_window;
+  a.n_resid = dkv->n_resid;
+  a.n_chunks = dkv_chunks(l);
+  const float s = scale > 0.f ? scale : 1.0f / __builtin_sqrtf(static_cast<float>(l.head_dim));
+  a.scale_log2 = s * 1.4426950408889634f;
+  return from_hip(launch_dkv_decode(a, l.dtype, l.head_dim, stream));
 }
 
 }  // extern "C"

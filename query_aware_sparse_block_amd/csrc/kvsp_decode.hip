@@ -89,7 +89,7 @@ __device__ __forceinline__ SeqWork seq_work(const DecodeArgs& a, int b, int quan
   const int n = (w.L + a.P - 1) / a.P;
   w.Cw = window_start_block(w.L, a.P, a.recent_window);
   w.dense = a.all_dense || (a.use_dense != nullptr && a.use_dense[b] != 0);
-  w.k = w.dense ? 0 : a.num_selected[b];
+  w.k = (w.dense || a.num_selected == nullptr) ? 0 : a.num_selected[b];
   w.A = w.dense ? n : w.k + (n - w.Cw);
   w.T = w.dense ? w.L : w.k * a.P + (w.L - w.Cw * a.P);
   if (w.T > 0) {
@@ -115,48 +115,6 @@ __device__ __forceinline__ int32_t attended_phys(const DecodeArgs& a, int b, con
     logical = w.Cw + (ab - w.k);
   }
   return a.block_table[static_cast<int64_t>(b) * a.max_blocks + logical];
-}
-
-template <typename T>
-struct QkMfma;
-
-template <>
-struct QkMfma<BF16> {
-  __device__ static inline floatx4 step(const uint4& k, const uint4& q, floatx4 acc) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, k),
-                                                   __builtin_bit_cast(bf16x8, q), acc, 0, 0, 0);
-  }
-};
-
-template <>
-struct QkMfma<F16> {
-  __device__ static inline floatx4 step(const uint4& k, const uint4& q, floatx4 acc) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, k),
-                                                  __builtin_bit_cast(f16x8, q), acc, 0, 0, 0);
-  }
-};
-
-template <>
-struct QkMfma<F32> {
-  // Four k=4 steps, one per float of the 16-byte vector.
-  __device__ static inline floatx4 step(const uint4& k, const uint4& q, floatx4 acc) {
-    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(k.x), __uint_as_float(q.x), acc, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(k.y), __uint_as_float(q.y), acc, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(k.z), __uint_as_float(q.z), acc, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(k.w), __uint_as_float(q.w), acc, 0, 0, 0);
-    return acc;
-  }
-};
-
-// Element offset, within a K row, of the 16-byte vector lane `lane` feeds to
-// contraction step s of a 16x16 MFMA tile.
-template <typename T>
-__device__ __forceinline__ int k_elem_offset(int lane, int s) {
-  if constexpr (T::kBytes == 2) {
-    return (lane / 16) * 8 + 32 * s;
-  } else {
-    return (lane / 16) * 4 + 16 * s;
-  }
 }
 
 // STREAM: read K/V with non-temporal loads. The launch picks it when every KV

@@ -252,6 +252,52 @@ __device__ __forceinline__ void wait_stores_done() {
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
+// ---- QK^T on MFMA --------------------------------------------------------------
+// One 16x16 tile of logits: rows are 16 key rows (A operand, one 16-byte vector
+// per lane and contraction step), columns 16 query heads (B operand).
+
+template <typename T>
+struct QkMfma;
+
+template <>
+struct QkMfma<BF16> {
+  __device__ static inline floatx4 step(const uint4& k, const uint4& q, floatx4 acc) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, k),
+                                                   __builtin_bit_cast(bf16x8, q), acc, 0, 0, 0);
+  }
+};
+
+template <>
+struct QkMfma<F16> {
+  __device__ static inline floatx4 step(const uint4& k, const uint4& q, floatx4 acc) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, k),
+                                                  __builtin_bit_cast(f16x8, q), acc, 0, 0, 0);
+  }
+};
+
+template <>
+struct QkMfma<F32> {
+  // Four k=4 steps, one per float of the 16-byte vector.
+  __device__ static inline floatx4 step(const uint4& k, const uint4& q, floatx4 acc) {
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(k.x), __uint_as_float(q.x), acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(k.y), __uint_as_float(q.y), acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(k.z), __uint_as_float(q.z), acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(k.w), __uint_as_float(q.w), acc, 0, 0, 0);
+    return acc;
+  }
+};
+
+// Element offset, within a K row, of the 16-byte vector lane `lane` feeds to
+// contraction step s of a 16x16 MFMA tile.
+template <typename T>
+__device__ __forceinline__ int k_elem_offset(int lane, int s) {
+  if constexpr (T::kBytes == 2) {
+    return (lane / 16) * 8 + 32 * s;
+  } else {
+    return (lane / 16) * 4 + 16 * s;
+  }
+}
+
 // ---- per-sequence integer plan ----------------------------------------------------
 // n blocks, C candidate blocks before the exact window [C*P, L), k kept blocks
 // and the dense-fallback decision; see kvsp_select_params in kvsp.h.

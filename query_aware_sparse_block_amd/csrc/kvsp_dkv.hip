@@ -1,0 +1,425 @@
+// DKV variant ("DKV: Anchor + Low-Rank Differential KV-Cache Compression for
+// Scalable Long-Context Inference", abstract): attention over compressed
+// blocks without decompressing their keys, and the block codec.
+//
+// A compressed (block, KV head) record holds the anchor rows k_a, v_a, a
+// basis W = [W_K | W_V] (32 x 2D, fp32), coefficients C (P x 32, fp32) and R
+// exact residual rows. Token t (not residual) stands for
+//   k_t = k_a + C_t W_K,   v_t = v_a + C_t W_V.
+// For a query q the logit is therefore <q, k_a> + C_t . (W_K q), and the
+// softmax-weighted value sum over the block is
+//   (sum_t p_t) v_a + (sum_t p_t C_t) W_V + sum_residual p_r v_r,
+// so a block costs one pass over C, W and the residual rows.
+//
+// Decode work split. The exact window is attended first by the split-KV
+// kernel of kvsp_decode.hip (window only) into the workspace. Here a
+// workgroup of 4 waves takes a (chunk, sequence, KV head) item: a run of the
+// sequence's selected blocks, folded into one online softmax; each of the
+// group's query heads (at most 16) is one MFMA column. Per block:
+//   A. every wave stages its quarter of C in LDS, computes a partial
+//      W_K q over a quarter of the channels (fp32 MFMA 16x16x4), the anchor
+//      term, and the exact logits of one tile of 16 residual rows (the
+//      QK^T MFMA of the exact path);
+//   B. low-rank logits of the wave's tokens: C (16 tokens x 32) times
+//      (W_K q) (32 x heads) on fp32 MFMA; residual tokens masked;
+//   C. probabilities against the block maximum, and the wave's share of
+//      p^T C (heads x 32), again fp32 MFMA, with p taken from the logit
+//      registers as the A operand;
+//   D. each wave owns D/4 output channels: (p^T C) W_V, the anchor term and
+//      the residual PV on fp32 MFMA, then the online-softmax rescale.
+// Chunks of one (sequence, KV head) merge through the workspace (device-scope
+// stores, a completion counter, the last chunk merges) together with the
+// window result.
+#include <stddef.h>
+#include <stdint.h>
+
+#include "kvsp_device.h"
+#include "kvsp_internal.h"
+
+namespace kvsp {
+namespace {
+
+constexpr int kRank = 32;
+constexpr int kMaxResid = 64;
+constexpr int kCRow = 36;  // LDS row stride (floats) of staged coefficient rows
+constexpr int kQRow = 33;  // LDS row stride of per-head rank vectors
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.69314718055994531f;
+
+__device__ __forceinline__ floatx4 mfma4(float a, float b, floatx4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+template <typename T, int D, int TPW>
+__global__ __launch_bounds__(256) void dkv_attend_kernel(DkvDecodeArgs a) {
+  constexpr int E = T::kBytes;
+  constexpr int DQ = D / 4;          // channels per wave for W_K q
+  constexpr int QS = DQ / 4;         // per lane group: QS consecutive channels
+  constexpr int NDT = D / 64;        // 16-channel output tiles per wave
+  constexpr int TOKW = 16 * TPW;     // tokens per wave
+  constexpr int KLD = D * E / 64;    // exact-row MFMA steps over D
+  constexpr int RS = kMaxResid / 4;  // residual PV steps (4 rows each)
+
+  __shared__ __align__(16) float c_lds[4][TOKW * kCRow];
+  __shared__ float qt_part[4][16][kQRow];
+  __shared__ float qa_part[4][4][16];
+  __shared__ float cb_part[4][16][kQRow];
+  __shared__ float p_res[kMaxResid][16];
+  __shared__ float wmax[4][16];
+  __shared__ float wsum[4][16];
+  __shared__ float rsum[4][16];
+  __shared__ uint32_t res_mask[8];
+  __shared__ int last_flag;
+
+  const int lane = threadIdx.x % kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int hl = lane % 16;  // MFMA column: query head (or rank / channel)
+  const int gi = lane / 16;  // lane group: MFMA k-slot, and row quad of outputs
+  const int G = a.Hq / a.Hkv;
+  const int R = a.n_resid;
+  const int n_pairs = a.B * a.Hkv;
+  const int total = n_pairs * a.n_chunks;
+  const float NEG_INF = -__builtin_huge_valf();
+  const int dbase = wave * 16 * NDT;  // this wave's output channels
+
+  if (wave == 0 && lane < 8) res_mask[lane] = 0;
+
+  for (int item = blockIdx.x; item < total; item += gridDim.x) {
+    const int c = item / n_pairs;
+    const int pair = item - c * n_pairs;
+    const int b = pair / a.Hkv;
+    const int g = pair - b * a.Hkv;
+    const int L = a.context_lens[b];
+    const int C = window_start_block(L, a.P, a.recent_window);
+    int k = a.num_selected[b];
+    k = k < 0 ? 0 : (k > C ? C : k);
+    const int per = k > 0 ? (k + a.n_chunks - 1) / a.n_chunks : 1;
+    const int n_act = k > 0 ? (k + per - 1) / per : 1;
+    if (c >= n_act) continue;  // uniform over the workgroup
+    const int j0 = c * per;
+    const int j1 = min(k, j0 + per);
+
+    // Query operands (fixed for the item). Heads past G are zero columns.
+    const bool head_ok = hl < G;
+    const int64_t qrow = static_cast<int64_t>(b) * a.Hq + g * G + hl;
+    float qreg[QS];
+#pragma unroll
+    for (int s = 0; s < QS; ++s)
+      qreg[s] = head_ok ? T::load1(a.q, qrow * D + wave * DQ + gi * QS + s) : 0.f;
+    uint4 qop[KLD];
+#pragma unroll
+    for (int s = 0; s < KLD; ++s)
+      qop[s] = head_ok ? load16(static_cast<const char*>(a.q) + (qrow * D + k_elem_offset<T>(lane, s)) * E)
+                       : make_uint4(0, 0, 0, 0);
+
+    // Running softmax state of heads 4*gi + v, channels dbase + 16*dt + hl.
+    float m_run[4], l_run[4];
+    floatx4 acc[NDT];
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      m_run[v] = NEG_INF;
+      l_run[v] = 0.f;
+    }
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) acc[dt] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+    for (int jj = j0; jj < j1; ++jj) {
+      const int jlog = a.selected[static_cast<int64_t>(b) * a.max_blocks + jj];
+      const int64_t phys = a.block_table[static_cast<int64_t>(b) * a.max_blocks + jlog];
+      const char* rec = a.records + (phys * a.Hkv + g) * a.rec_bytes;
+      const float* basis = reinterpret_cast<const float*>(rec + a.off_basis);
+
+      // ---- A: loads, W_K q partial, anchor term, residual logits ----------------
+      if (wave == 0 && lane < R) {
+        const int r = reinterpret_cast<const int32_t*>(rec + a.off_ridx)[lane];
+        if (r >= 0 && r < a.P) atomicOr(&res_mask[r >> 5], 1u << (r & 31));
+      }
+      {
+        const char* src = rec + a.off_coef + static_cast<int64_t>(wave) * TOKW * kRank * 4;
+#pragma unroll
+        for (int u = 0; u < 2 * TPW; ++u) {
+          const int vi = lane + kWave * u;  // 16-byte vector of the wave's rows
+          const uint4 v = load16(src + static_cast<int64_t>(vi) * 16);
+          *reinterpret_cast<uint4*>(&c_lds[wave][(vi / 8) * kCRow + (vi % 8) * 4]) = v;
+        }
+      }
+      float wk[2][QS];
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+        for (int s = 0; s < QS; ++s)
+          wk[nt][s] = basis[(16 * nt + hl) * 2 * D + wave * DQ + gi * QS + s];
+      float wv[NDT][8];
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+        for (int s = 0; s < 8; ++s) wv[dt][s] = basis[(gi * 8 + s) * 2 * D + D + dbase + 16 * dt + hl];
+      float va[NDT];
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) va[dt] = T::load1(rec, D + dbase + 16 * dt + hl);
+      float vr[RS][NDT];
+#pragma unroll
+      for (int s = 0; s < RS; ++s) {
+        const int row = 4 * s + gi;
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt)
+          vr[s][dt] = row < R ? T::load1(rec + a.off_rv, static_cast<int64_t>(row) * D + dbase + 16 * dt + hl)
+                              : 0.f;
+      }
+      float qa = 0.f;
+#pragma unroll
+      for (int s = 0; s < QS; ++s) qa += qreg[s] * T::load1(rec, wave * DQ + gi * QS + s);
+      floatx4 qt[2] = {floatx4{0.f, 0.f, 0.f, 0.f}, floatx4{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+        for (int s = 0; s < QS; ++s) qt[nt] = mfma4(qreg[s], wk[nt][s], qt[nt]);
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) qt_part[wave][4 * gi + v][16 * nt + hl] = qt[nt][v];
+      qa_part[wave][gi][hl] = qa;
+      float rmax = NEG_INF;
+      if (16 * wave < R) {
+        const int r = min(16 * wave + hl, R - 1);
+        const char* kr = rec + a.off_rk + static_cast<int64_t>(r) * D * E;
+        floatx4 sc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < KLD; ++s) sc = QkMfma<T>::step(load16(kr + k_elem_offset<T>(lane, s) * E), qop[s], sc);
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const int row = 16 * wave + 4 * gi + v;
+          const float z = row < R ? sc[v] * a.scale_log2 : NEG_INF;
+          p_res[row][hl] = z;
+          rmax = fmaxf(rmax, z);
+        }
+      }
+      __syncthreads();
+
+      // ---- B: low-rank logits of this wave's tokens --------------------------
+      float qtb[8];
+#pragma unroll
+      for (int s = 0; s < 8; ++s) {
+        const int j = gi * 8 + s;
+        qtb[s] = (qt_part[0][hl][j] + qt_part[1][hl][j]) + (qt_part[2][hl][j] + qt_part[3][hl][j]);
+      }
+      float qa_h = 0.f;
+#pragma unroll
+      for (int w = 0; w < 4; ++w)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) qa_h += qa_part[w][q][hl];
+      float s2[TPW][4];
+      float lmax = NEG_INF;
+#pragma unroll
+      for (int mt = 0; mt < TPW; ++mt) {
+        const float* crow = &c_lds[wave][(16 * mt + hl) * kCRow + gi * 8];
+        const float4 c0 = *reinterpret_cast<const float4*>(crow);
+        const float4 c1 = *reinterpret_cast<const float4*>(crow + 4);
+        const float cv[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+        floatx4 sc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < 8; ++s) sc = mfma4(cv[s], qtb[s], sc);
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const int tok = wave * TOKW + 16 * mt + 4 * gi + v;
+          const bool resid = (res_mask[tok >> 5] >> (tok & 31)) & 1u;
+          s2[mt][v] = resid ? NEG_INF : (sc[v] + qa_h) * a.scale_log2;
+          lmax = fmaxf(lmax, s2[mt][v]);
+        }
+      }
+      lmax = fold_max<16>(fmaxf(lmax, rmax));
+      if (gi == 0) wmax[wave][hl] = lmax;
+      __syncthreads();
+
+      // ---- C: probabilities, p^T C, residual probabilities ------------------
+      if (wave == 0 && lane < 8) res_mask[lane] = 0;  // every read of it is done
+      const float mb = fmaxf(fmaxf(wmax[0][hl], wmax[1][hl]), fmaxf(wmax[2][hl], wmax[3][hl]));
+      float ls = 0.f;
+#pragma unroll
+      for (int mt = 0; mt < TPW; ++mt)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const float p = __builtin_amdgcn_exp2f(s2[mt][v] - mb);
+          s2[mt][v] = p;
+          ls += p;
+        }
+      floatx4 cb[2] = {floatx4{0.f, 0.f, 0.f, 0.f}, floatx4{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+        for (int mt = 0; mt < TPW; ++mt)
+#pragma unroll
+          for (int v = 0; v < 4; ++v)
+            cb[nt] = mfma4(s2[mt][v], c_lds[wave][(16 * mt + 4 * gi + v) * kCRow + 16 * nt + hl], cb[nt]);
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) cb_part[wave][4 * gi + v][16 * nt + hl] = cb[nt][v];
+      ls = fold_sum<16>(ls);
+      if (gi == 0) wsum[wave][hl] = ls;
+      float rs = 0.f;
+      if (16 * wave < R) {
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const int row = 16 * wave + 4 * gi + v;
+          const float p = row < R ? __builtin_amdgcn_exp2f(p_res[row][hl] - mb) : 0.f;
+          p_res[row][hl] = p;
+          rs += p;
+        }
+      }
+      rs = fold_sum<16>(rs);
+      if (gi == 0) rsum[wave][hl] = rs;
+      __syncthreads();
+
+      // ---- D: output channels of this wave -----------------------------------
+      float alpha[4], beta[4], llr[4];
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int h = 4 * gi + v;
+        const float mbh = fmaxf(fmaxf(wmax[0][h], wmax[1][h]), fmaxf(wmax[2][h], wmax[3][h]));
+        llr[v] = (wsum[0][h] + wsum[1][h]) + (wsum[2][h] + wsum[3][h]);
+        const float lb = llr[v] + ((rsum[0][h] + rsum[1][h]) + (rsum[2][h] + rsum[3][h]));
+        const float mn = fmaxf(m_run[v], mbh);
+        alpha[v] = __builtin_amdgcn_exp2f(m_run[v] - mn);
+        beta[v] = __builtin_amdgcn_exp2f(mbh - mn);
+        l_run[v] = l_run[v] * alpha[v] + lb * beta[v];
+        m_run[v] = mn;
+      }
+      float ca[8];
+#pragma unroll
+      for (int s = 0; s < 8; ++s) {
+        const int j = gi * 8 + s;
+        ca[s] = (cb_part[0][hl][j] + cb_part[1][hl][j]) + (cb_part[2][hl][j] + cb_part[3][hl][j]);
+      }
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) {
+        floatx4 t = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < 8; ++s) t = mfma4(ca[s], wv[dt][s], t);
+#pragma unroll
+        for (int s = 0; s < RS; ++s)
+          if (4 * s < R) t = mfma4(p_res[4 * s + gi][hl], vr[s][dt], t);
+#pragma unroll
+        for (int v = 0; v < 4; ++v) acc[dt][v] = acc[dt][v] * alpha[v] + beta[v] * (t[v] + llr[v] * va[dt]);
+      }
+      __syncthreads();  // LDS is reused by the next block
+    }
+
+    // ---- merge the chunks of (b, g) and the window result --------------------
+    const int64_t slot = static_cast<int64_t>(pair) * a.n_chunks + c;
+    if (n_act == 1) {
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int h = 4 * gi + v;
+        if (h >= G) continue;
+        const int64_t hq = static_cast<int64_t>(b) * a.Hq + g * G + h;
+        const float lw = a.lse_w[hq];
+        const float mw = lw == NEG_INF ? NEG_INF : lw * kLog2e;
+        const float M = fmaxf(m_run[v], mw);
+        const float wc = M == NEG_INF ? 0.f : __builtin_amdgcn_exp2f(m_run[v] - M);
+        const float ww = M == NEG_INF ? 0.f : __builtin_amdgcn_exp2f(mw - M);
+        const float Ls = l_run[v] * wc + ww;
+        const float inv = Ls > 0.f ? 1.f / Ls : 0.f;
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) {
+          const int d = dbase + 16 * dt + hl;
+          a.out[hq * D + d] = (acc[dt][v] * wc + a.out_w[hq * D + d] * ww) * inv;
+        }
+        if (a.lse != nullptr && wave == 0 && hl == 0)
+          a.lse[hq] = Ls > 0.f ? (M + __builtin_log2f(Ls)) * kLn2 : NEG_INF;
+      }
+      continue;
+    }
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int h = 4 * gi + v;
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt)
+        store_coherent(a.part_acc + (slot * 16 + h) * D + dbase + 16 * dt + hl, acc[dt][v]);
+      if (wave == 0 && hl == 0) {
+        store_coherent(a.part_ml + (slot * 16 + h) * 2 + 0, m_run[v]);
+        store_coherent(a.part_ml + (slot * 16 + h) * 2 + 1, l_run[v]);
+      }
+    }
+    wait_stores_done();  // the partial is at the device coherence point before it is counted
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      const int old = __hip_atomic_fetch_add(a.counters + pair, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      last_flag = old == n_act - 1;
+    }
+    __syncthreads();
+    if (!last_flag) continue;
+    const int64_t slot0 = static_cast<int64_t>(pair) * a.n_chunks;
+    for (int o = threadIdx.x; o < G * D; o += blockDim.x) {
+      const int h = o / D;
+      const int d = o - h * D;
+      const int64_t hq = static_cast<int64_t>(b) * a.Hq + g * G + h;
+      const float lw = a.lse_w[hq];
+      float M = lw == NEG_INF ? NEG_INF : lw * kLog2e;
+      const float mw = M;
+      for (int cc = 0; cc < n_act; ++cc) {
+        const float l = load_coherent(a.part_ml + ((slot0 + cc) * 16 + h) * 2 + 1);
+        if (l > 0.f) M = fmaxf(M, load_coherent(a.part_ml + ((slot0 + cc) * 16 + h) * 2));
+      }
+      float Ls = 0.f, num = 0.f;
+      if (M != NEG_INF) {
+        for (int cc = 0; cc < n_act; ++cc) {
+          const float l = load_coherent(a.part_ml + ((slot0 + cc) * 16 + h) * 2 + 1);
+          if (l > 0.f) {
+            const float w = __builtin_amdgcn_exp2f(load_coherent(a.part_ml + ((slot0 + cc) * 16 + h) * 2) - M);
+            Ls += w * l;
+            num += w * load_coherent(a.part_acc + ((slot0 + cc) * 16 + h) * D + d);
+          }
+        }
+        const float ww = __builtin_amdgcn_exp2f(mw - M);
+        Ls += ww;
+        num += ww * a.out_w[hq * D + d];
+      }
+      a.out[hq * D + d] = Ls > 0.f ? num / Ls : 0.f;
+      if (a.lse != nullptr && d == 0) a.lse[hq] = Ls > 0.f ? (M + __builtin_log2f(Ls)) * kLn2 : NEG_INF;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) store_coherent_i(a.counters + pair, 0);  // ready for the next call
+  }
+}
+
+template <typename T, int D>
+hipError_t launch_dkv_decode_t(const DkvDecodeArgs& a, hipStream_t stream) {
+  const int total = a.B * a.Hkv * a.n_chunks;
+  const int grid = total < 2048 ? total : 2048;
+  switch (a.P) {
+    case 64: hipLaunchKernelGGL((dkv_attend_kernel<T, D, 1>), dim3(grid), dim3(256), 0, stream, a); break;
+    case 128: hipLaunchKernelGGL((dkv_attend_kernel<T, D, 2>), dim3(grid), dim3(256), 0, stream, a); break;
+    case 256: hipLaunchKernelGGL((dkv_attend_kernel<T, D, 4>), dim3(grid), dim3(256), 0, stream, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+template <typename T>
+hipError_t launch_dkv_decode_d(const DkvDecodeArgs& a, int D, hipStream_t stream) {
+  if (D == 64) return launch_dkv_decode_t<T, 64>(a, stream);
+  if (D == 128) return launch_dkv_decode_t<T, 128>(a, stream);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+hipError_t launch_dkv_decode(const DkvDecodeArgs& a, int dtype, int D, hipStream_t stream) {
+  switch (dtype) {
+    case KVSP_F32: return launch_dkv_decode_d<F32>(a, D, stream);
+    case KVSP_F16: return launch_dkv_decode_d<F16>(a, D, stream);
+    case KVSP_BF16: return launch_dkv_decode_d<BF16>(a, D, stream);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_dkv_compress(const DkvCompressArgs& a, int dtype, int D, hipStream_t stream) {
+  (void)a;
+  (void)dtype;
+  (void)D;
+  (void)stream;
+  return hipErrorNotSupported;
+}
+
+}  // namespace kvsp

@@ -81,6 +81,43 @@ struct DecodeArgs {
   float scale_log2;             // softmax scale * log2(e)
 };
 
+// DKV decode over compressed blocks. Work item (chunk c, pair = b * Hkv + g),
+// numbered item = c * B * Hkv + pair; chunk c takes selected blocks
+// [c * per, min(k, (c + 1) * per)) with per = ceil(k / n_chunks). Partials live
+// at slot pair * n_chunks + c; counters[pair] counts finished chunks. The
+// window result (out_w, lse_w) is merged in at the end.
+struct DkvDecodeArgs {
+  const void* q;
+  const char* records;
+  const int32_t* block_table;
+  const int32_t* context_lens;
+  const int32_t* selected;
+  const int32_t* num_selected;
+  const float* out_w;           // [B][Hq][D] window-only attention
+  const float* lse_w;           // [B][Hq] natural log
+  float* out;
+  float* lse;                   // may be NULL
+  float* part_acc;              // [slots][16][D]
+  float* part_ml;               // [slots][16][2]
+  int32_t* counters;            // [B * Hkv], zero between calls
+  int64_t rec_bytes;
+  int32_t off_basis, off_coef, off_rk, off_rv, off_ridx;
+  int32_t B, Hq, Hkv, P, max_blocks, recent_window, n_resid, n_chunks;
+  float scale_log2;
+};
+// DKV codec: one work item per (sequence, candidate block, KV head).
+struct DkvCompressArgs {
+  const void* k_pool;
+  const void* v_pool;
+  const int32_t* block_table;
+  const int32_t* context_lens;
+  char* records;
+  int64_t rec_bytes;
+  int32_t off_basis, off_coef, off_rk, off_rv, off_ridx;
+  int32_t B, Hkv, P, max_blocks, recent_window, n_resid, power_iters;
+};
+hipError_t launch_dkv_decode(const DkvDecodeArgs& a, int dtype, int D, hipStream_t stream);
+hipError_t launch_dkv_compress(const DkvCompressArgs& a, int dtype, int D, hipStream_t stream);
 hipError_t launch_append(const AppendArgs& a, int dtype, int D, hipStream_t stream);
 hipError_t launch_build_summaries(const SummaryArgs& a, int dtype, int D, hipStream_t stream);
 hipError_t launch_score(const ScoreArgs& a, int dtype, hipStream_t stream);

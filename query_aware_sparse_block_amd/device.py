@@ -124,3 +124,40 @@ def decode_step(dc: DeviceCase, buf: StepBuffers, params=None, stream=None):
     for flagged sequences). Summaries must already be resident."""
     score_topk(dc, buf, params, stream)
     sparse_decode(dc, buf, params, 0.0, stream)
+
+
+# ---- DKV variant --------------------------------------------------------------------
+
+def dkv_records_tensor(dc: DeviceCase, recs: dict, n_resid: int) -> torch.Tensor:
+    """Host records keyed by (phys, g) (stored values, see workloads.dkv_pack)
+    -> the device record array [num_phys][Hkv][record bytes]; absent records
+    are zero bytes."""
+    from . import workloads as wl
+    c = dc.case
+    lay = wl.dkv_record_layout(c.D, c.P, wl.ELEM_BYTES[c.dtype], n_resid)
+    host = np.zeros((c.num_phys, c.Hkv, lay["bytes"]), np.uint8)
+    for (phys, g), f in recs.items():
+        host[phys, g] = wl.dkv_pack(f, c.dtype, c.P, n_resid)
+    return torch.from_numpy(host).to(dc.q.device)
+
+
+def alloc_dkv_records(dc: DeviceCase, dkv: kvsp.DkvParams) -> torch.Tensor:
+    n = kvsp.kvsp_dkv_record_bytes(dc.layout, dkv)
+    assert n > 0, "unsupported DKV arguments"
+    L = dc.layout
+    return torch.zeros((L.num_phys_blocks, L.num_kv_heads, n), dtype=torch.uint8,
+                       device=dc.q.device)
+
+
+def dkv_compress(dc: DeviceCase, dkv: kvsp.DkvParams, records: torch.Tensor, stream=None):
+    kvsp.kvsp_dkv_compress(dc.layout, dkv, dc.params.recent_window, dc.k_pool, dc.v_pool,
+                           dc.block_table, dc.ctx_lens, records, stream)
+
+
+def dkv_decode(dc: DeviceCase, buf: StepBuffers, dkv: kvsp.DkvParams, records: torch.Tensor,
+               workspace: torch.Tensor, scale=0.0, stream=None):
+    """Attention over the compressed blocks buf.selected[:num_selected] and
+    the exact window, into buf.out / buf.lse."""
+    kvsp.kvsp_dkv_decode(dc.layout, dc.params, dkv, dc.q, dc.k_pool, dc.v_pool, records,
+                         dc.block_table, dc.ctx_lens, buf.selected, buf.num_selected, scale,
+                         buf.out, buf.lse, workspace, stream)

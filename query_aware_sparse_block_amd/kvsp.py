@@ -41,6 +41,11 @@ class kvsp_select_params(ctypes.Structure):
                 ("gamma_den", ctypes.c_int32)]
 
 
+class kvsp_dkv_params(ctypes.Structure):
+    _fields_ = [("rank", ctypes.c_int32), ("n_resid", ctypes.c_int32),
+                ("power_iters", ctypes.c_int32)]
+
+
 class KvspError(RuntimeError):
     def __init__(self, fn: str, status: int):
         super().__init__(f"{fn} returned {STATUS_NAMES.get(status, status)} "
@@ -77,6 +82,16 @@ def library() -> ctypes.CDLL:
                                          sz, P]
         L.kvsp_dense_decode.restype = ctypes.c_int
         L.kvsp_dense_decode.argtypes = [LP, P, P, P, P, P, ctypes.c_float, P, P, P, sz, P]
+        DP = ctypes.POINTER(kvsp_dkv_params)
+        L.kvsp_dkv_record_bytes.restype = sz
+        L.kvsp_dkv_record_bytes.argtypes = [LP, DP]
+        L.kvsp_dkv_workspace_bytes.restype = sz
+        L.kvsp_dkv_workspace_bytes.argtypes = [LP, DP]
+        L.kvsp_dkv_compress.restype = ctypes.c_int
+        L.kvsp_dkv_compress.argtypes = [LP, DP, i32, P, P, P, P, P, P]
+        L.kvsp_dkv_decode.restype = ctypes.c_int
+        L.kvsp_dkv_decode.argtypes = [LP, SP, DP, P, P, P, P, P, P, P, P, ctypes.c_float, P, P,
+                                      P, sz, P]
         _lib = L
     return _lib
 
@@ -189,4 +204,49 @@ def kvsp_dense_decode(layout, q, k_pool, v_pool, block_table, context_lens, scal
     _check("kvsp_dense_decode", library().kvsp_dense_decode(
         ctypes.byref(layout), _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_table),
         _ptr(context_lens), ctypes.c_float(scale), _ptr(out), _ptr(lse), _ptr(workspace),
+        workspace.numel(), _stream(stream)))
+
+
+@dataclass
+class DkvParams:
+    rank: int = 32
+    n_resid: int = 16
+    power_iters: int = 0
+
+    def c(self) -> kvsp_dkv_params:
+        return kvsp_dkv_params(self.rank, self.n_resid, self.power_iters)
+
+
+def kvsp_dkv_record_bytes(layout: kvsp_layout, dkv: DkvParams) -> int:
+    p = dkv.c()
+    return int(library().kvsp_dkv_record_bytes(ctypes.byref(layout), ctypes.byref(p)))
+
+
+def kvsp_dkv_workspace_bytes(layout: kvsp_layout, dkv: DkvParams) -> int:
+    p = dkv.c()
+    return int(library().kvsp_dkv_workspace_bytes(ctypes.byref(layout), ctypes.byref(p)))
+
+
+def alloc_dkv_workspace(layout: kvsp_layout, dkv: DkvParams, device="cuda") -> torch.Tensor:
+    n = kvsp_dkv_workspace_bytes(layout, dkv)
+    return torch.zeros(max(n, 1), dtype=torch.uint8, device=device)  # counters start at zero
+
+
+def kvsp_dkv_compress(layout, dkv: DkvParams, recent_window, k_pool, v_pool, block_table,
+                      context_lens, records, stream=None):
+    p = dkv.c()
+    _check("kvsp_dkv_compress", library().kvsp_dkv_compress(
+        ctypes.byref(layout), ctypes.byref(p), int(recent_window), _ptr(k_pool), _ptr(v_pool),
+        _ptr(block_table), _ptr(context_lens), _ptr(records), _stream(stream)))
+
+
+def kvsp_dkv_decode(layout, params: SelectParams, dkv: DkvParams, q, k_pool, v_pool, records,
+                    block_table, context_lens, selected, num_selected, scale, out, lse, workspace,
+                    stream=None):
+    p = params.c()
+    d = dkv.c()
+    _check("kvsp_dkv_decode", library().kvsp_dkv_decode(
+        ctypes.byref(layout), ctypes.byref(p), ctypes.byref(d), _ptr(q), _ptr(k_pool),
+        _ptr(v_pool), _ptr(records), _ptr(block_table), _ptr(context_lens), _ptr(selected),
+        _ptr(num_selected), ctypes.c_float(scale), _ptr(out), _ptr(lse), _ptr(workspace),
         workspace.numel(), _stream(stream)))

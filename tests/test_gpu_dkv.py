@@ -1,0 +1,128 @@
+"""GPU parity of the DKV variant (DKV abstract) through the C ABI.
+
+Decode: synthetic records (random anchors, bases, coefficients and residual
+rows from the seeded generator) and a random ascending block selection are
+decoded by kvsp_dkv_decode and by the numpy oracle, which decompresses every
+token explicitly and attends the union of the selected blocks and the exact
+window. Bars as for the exact path: max-abs output error 2e-3 for 16-bit
+caches and 1e-5 for fp32 caches, lse within 1e-4.
+
+Cases: every dtype, head dims 64 and 128, block sizes 64, 128 and 256,
+1 to 16 query heads per KV head, residual budgets 0 to 64, ragged contexts,
+sequences with nothing selected, an empty window, the chunk-merge path and a
+batch large enough that every work item folds several blocks."""
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import dkv as DKV
+from query_aware_sparse_block_amd import device as dev
+from query_aware_sparse_block_amd import kvsp
+from query_aware_sparse_block_amd import workloads as wl
+from tests import gpu_helpers as H
+
+pytestmark = pytest.mark.gpu
+
+
+def oracle_fields(f: dict, dtype: str) -> dict:
+    """Stored record values -> the oracle's float64 fields."""
+    dec = lambda x: wl.decode_f32(x, dtype).astype(np.float64)  # noqa: E731
+    return dict(anchor_k=dec(f["anchor_k"]), anchor_v=dec(f["anchor_v"]),
+                basis=np.asarray(f["basis"], np.float64), coef=np.asarray(f["coef"], np.float64),
+                resid=np.asarray(f["resid"], np.int64), resid_k=dec(f["resid_k"]),
+                resid_v=dec(f["resid_v"]))
+
+
+def random_selection(case, seed, k_max, empty=()):
+    rng = np.random.default_rng(seed)
+    sel = np.full((case.B, case.max_blocks), -1, np.int32)
+    nsel = np.zeros(case.B, np.int32)
+    for b in range(case.B):
+        C = DKV.window_start(int(case.ctx_lens[b]), case.P, case.recent_window)
+        k = 0 if b in empty else min(k_max, C)
+        if k:
+            sel[b, :k] = np.sort(rng.choice(C, size=k, replace=False))
+        nsel[b] = k
+    return sel, nsel
+
+
+def run_decode_parity(case, n_resid, k_max, seed=0, empty=()):
+    H.note(f"dkv decode {case.name} dtype={case.dtype} D={case.D} P={case.P} "
+           f"G={case.Hq // case.Hkv} R={n_resid} k<={k_max}")
+    sel, nsel = random_selection(case, seed, k_max, empty)
+    used = sorted({int(case.block_table[b, j]) for b in range(case.B) for j in sel[b, :nsel[b]]})
+    recs = wl.dkv_random_records(case, n_resid, seed + 1, blocks=used)
+    dc = dev.upload(case)
+    buf = dev.alloc_buffers(dc)
+    dkv = kvsp.DkvParams(n_resid=n_resid)
+    records = dev.dkv_records_tensor(dc, recs, n_resid)
+    ws = kvsp.alloc_dkv_workspace(dc.layout, dkv)
+    buf.selected.copy_(torch.from_numpy(sel))
+    buf.num_selected.copy_(torch.from_numpy(nsel))
+    scale = 1.0 / np.sqrt(case.D)
+    for rep in range(2):  # the second call checks that the workspace was left reusable
+        buf.out.fill_(np.nan)
+        dev.dkv_decode(dc, buf, dkv, records, ws)
+        torch.cuda.synchronize()
+        out = buf.out.cpu().numpy().astype(np.float64)
+        lse = buf.lse.cpu().numpy().astype(np.float64)
+        ofields = {key: oracle_fields(f, case.dtype) for key, f in recs.items()}
+        kp = wl.decode_f32(case.k_pool, case.dtype).astype(np.float64)
+        vp = wl.decode_f32(case.v_pool, case.dtype).astype(np.float64)
+        ref, ref_lse = DKV.decode(wl.decode_f32(case.q, case.dtype), kp, vp, ofields,
+                                  case.block_table, case.ctx_lens, sel, nsel, Hkv=case.Hkv,
+                                  P=case.P, recent_window=case.recent_window, scale=scale)
+        err = np.abs(out - ref).max()
+        assert err <= H.OUT_TOL[case.dtype], f"out err {err} (call {rep})"
+        fin = np.isfinite(ref_lse)
+        assert np.array_equal(np.isfinite(lse), fin)
+        assert np.abs(lse[fin] - ref_lse[fin]).max(initial=0.0) <= H.LSE_TOL
+        assert np.all(out[~fin] == 0.0)
+
+
+def small_case(dtype, D, P, Hq, Hkv, ctx, W, seed, num_phys=None):
+    max_blocks = -(-max(ctx) // P)
+    return wl.make_case(f"dkv-{dtype}-D{D}-P{P}", seed=seed, B=len(ctx), Hq=Hq, Hkv=Hkv, D=D,
+                        P=P, dtype=dtype, ctx_lens=ctx, shuffle=True,
+                        num_phys=num_phys or len(ctx) * max_blocks, max_blocks=max_blocks,
+                        recent_window=W, top_k=4)
+
+
+@pytest.mark.parametrize("dtype,D,P,Hq,Hkv,R", [
+    ("bf16", 128, 256, 12, 2, 16),
+    ("fp16", 128, 64, 4, 4, 0),
+    ("fp32", 64, 128, 32, 2, 64),
+    ("bf16", 64, 64, 8, 2, 64),
+    ("fp16", 128, 128, 6, 3, 5),
+    ("bf16", 128, 256, 16, 1, 33),
+])
+def test_decode_random_records(dtype, D, P, Hq, Hkv, R):
+    ctx = [9 * P + 37, 5 * P, 3 * P + 1]
+    case = small_case(dtype, D, P, Hq, Hkv, ctx, W=P + 20, seed=700 + D + P + R)
+    run_decode_parity(case, R, k_max=6, seed=R)
+
+
+def test_decode_nothing_selected_and_empty_window():
+    # sequence 0 selects nothing (window only); with W = 0 and whole blocks
+    # sequence 1 has an empty window (compressed blocks only)
+    case = small_case("bf16", 128, 64, 8, 2, [640, 512, 100], W=0, seed=731)
+    run_decode_parity(case, 8, k_max=5, seed=3, empty=(0,))
+
+
+def test_decode_window_only_batch():
+    case = small_case("fp16", 128, 128, 8, 2, [1000, 300], W=256, seed=732)
+    run_decode_parity(case, 16, k_max=4, seed=4, empty=(0, 1))
+
+
+def test_decode_long_selection_merges_many_chunks():
+    # 2 sequences x 2 KV heads: 64 chunks per pair, 100 blocks -> 2 per chunk
+    case = small_case("bf16", 64, 64, 4, 2, [130 * 64 + 5, 111 * 64], W=64, seed=733)
+    run_decode_parity(case, 4, k_max=100, seed=5)
+
+
+def test_decode_large_batch_items_fold_several_blocks():
+    # 32 x 8 pairs: one chunk per pair, every item walks all its blocks
+    ctx = [16 * 64 + 3 * b for b in range(32)]
+    case = small_case("bf16", 64, 64, 16, 8, ctx, W=100, seed=734)
+    run_decode_parity(case, 8, k_max=7, seed=6)
