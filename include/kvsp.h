@@ -265,14 +265,19 @@ size_t kvsp_dkv_workspace_bytes(const kvsp_layout* layout, const kvsp_dkv_params
 /* DKV codec: for every sequence b and every logical block j < C (C = floor(max(0,
  * L - recent_window) / P), the blocks wholly older than the window) writes the
  * record of (block_table[b][j], g) for every KV head g from the exact K/V rows
- * in the pools. The basis is computed in float32 by subspace iteration
- * (power_iters rounds of X^T X applied to the basis, each followed by a
- * re-orthonormalisation), started from a fixed pseudo-random basis; with a
- * gap between the 32nd and 33rd singular values of X it converges to the
- * truncated SVD's subspace. coef = X basis^T; residual tokens are the n_resid
- * rows with the largest float32 reconstruction error (ties to the lower
- * offset); anchor and residual rows are bit-exact copies. Records of other
- * blocks are not touched. Needs no workspace. */
+ * in the pools. The basis is computed by subspace iteration: power_iters
+ * rounds of X^T X applied to it (float32 products), each followed by a
+ * re-orthonormalisation (Cholesky QR in double of the column-scaled matrix),
+ * started from a fixed pseudo-random basis. With a gap between the 32nd and
+ * 33rd singular values of X it converges to the truncated SVD's subspace;
+ * without one it spans a near-optimal 32-dimensional subspace. A direction
+ * X does not have (rank below 32) gives a zero basis row. coef = X basis^T;
+ * residual tokens are the n_resid rows with the largest float32
+ * reconstruction error ||X_t - coef_t basis|| (ties to the lower offset);
+ * anchor and residual rows are bit-exact copies. Records of other blocks are
+ * not touched; sequences sharing a physical block write identical records.
+ * Needs no workspace. It runs off the per-step path: a block is compressed
+ * once, when it leaves the window. */
 kvsp_status kvsp_dkv_compress(const kvsp_layout* layout, const kvsp_dkv_params* dkv,
                               int32_t recent_window, const void* k_pool, const void* v_pool,
                               const int32_t* block_table, const int32_t* context_lens,

@@ -448,6 +448,7 @@ kvsp_status kvsp_dkv_compress(const kvsp_layout* layout, const kvsp_dkv_params* 
   a.Hkv = l.num_kv_heads;
   a.P = l.block_size;
   a.max_blocks = l.max_blocks_per_seq;
+  a.num_phys = l.num_phys_blocks;
   a.recent_window = recent_window;
   a.n_resid = dkv->n_resid;
   a.power_iters = dkv->power_iters > 0 ? dkv->power_iters : kDkvDefaultIters;

@@ -403,6 +403,325 @@ hipError_t launch_dkv_decode_d(const DkvDecodeArgs& a, int D, hipStream_t stream
   return hipErrorInvalidValue;
 }
 
+
+// ---- codec ----------------------------------------------------------------------
+// One workgroup (4 waves) per (sequence, block j < C, KV head). X = [K - k_a |
+// V - v_a] (P x N, N = 2D, anchor a = token 0) streams through LDS as float32
+// in 64-token chunks; the differences of two 16-bit values are exact there.
+// Subspace iteration keeps an orthonormal N x 32 basis Q and applies
+// Q <- orth(X^T (X Q)) power_iters times:
+//   Y = X Q   fp32 MFMA, wave w takes the chunk's tokens [16w, 16w + 16);
+//   Z += X^T Y  fp32 MFMA, wave w takes channels [N/4 w, N/4 (w + 1)); Z stays
+//             in registers across the chunks;
+//   orth(Z)   Cholesky QR in double of the column-scaled Z: Q = Z S R^-1
+//             with S the inverse column norms and R^T R the Gram of Z S. A
+//             column whose squared pivot falls below kDropTol (its part
+//             independent of the earlier columns is under 1e-5 of its norm)
+//             is dropped, i.e. set to zero; so are zero columns. A zero basis
+//             row adds nothing to any reconstruction.
+// The start is a fixed pseudo-random matrix (murmur3's 32-bit finaliser of
+// the element index), orthonormalised the same way. A last pass writes
+// coef = X Q and each token's squared float32 reconstruction error
+// ||X_t - coef_t Q^T||^2; the n_resid largest (ties to the lower offset)
+// become the residual tokens.
+constexpr int kChunk = 64;
+constexpr int kZRow = 36;   // LDS row stride (floats) of Z and of Y
+constexpr double kDropTol = 1e-10;
+
+template <int N>
+struct CodecShared {
+  union {
+    float x[kChunk][N + 4];  // X chunk
+    float z[N][kZRow];       // Z = X^T X Q before orthonormalisation
+  } u;
+  float qt[kRank][N + 4];    // Q^T: row r is basis vector r
+  float y[kChunk][kZRow];    // Y = X Q of the chunk
+  double g[kRank][kRank + 1];  // scaled Gram (upper part), R^T (strict lower part)
+  double rdiag[kRank];
+  double cs[kRank];          // column scales
+  float anc[N];              // anchor row [k_a | v_a]
+  float err2[256];           // per-token squared reconstruction error
+  int32_t flag[256];
+  int32_t ridx[kMaxResid];
+};
+
+__device__ __forceinline__ float codec_start_value(uint32_t i) {
+  uint32_t x = i * 0x9E3779B9u + 0x7F4A7C15u;
+  x ^= x >> 16;
+  x *= 0x85EBCA6Bu;
+  x ^= x >> 13;
+  x *= 0xC2B2AE35u;
+  x ^= x >> 16;
+  return static_cast<float>(x >> 8) * (1.0f / 8388608.0f) - 1.0f;
+}
+
+// Q^T <- orth(Z) as described above; reads sh.u.z, writes sh.qt. Starts after
+// a barrier that published Z and ends with one.
+template <int N>
+__device__ void codec_orthonormalize(CodecShared<N>& sh, int tid) {
+  {
+    const int i = tid / 8, jq = tid % 8;
+    double g0 = 0.0, g1 = 0.0, g2 = 0.0, g3 = 0.0;
+    for (int c = 0; c < N; ++c) {
+      const double zi = sh.u.z[c][i];
+      const float4 zj = *reinterpret_cast<const float4*>(&sh.u.z[c][4 * jq]);
+      g0 += zi * static_cast<double>(zj.x);
+      g1 += zi * static_cast<double>(zj.y);
+      g2 += zi * static_cast<double>(zj.z);
+      g3 += zi * static_cast<double>(zj.w);
+    }
+    sh.g[i][4 * jq + 0] = g0;
+    sh.g[i][4 * jq + 1] = g1;
+    sh.g[i][4 * jq + 2] = g2;
+    sh.g[i][4 * jq + 3] = g3;
+  }
+  __syncthreads();
+  if (tid < kRank) {
+    const double d = sh.g[tid][tid];
+    sh.cs[tid] = d > 0.0 ? 1.0 / sqrt(d) : 0.0;
+  }
+  __syncthreads();
+  for (int e = tid; e < kRank * kRank; e += 256) {
+    const int i = e / kRank, j = e % kRank;
+    sh.g[i][j] *= sh.cs[i] * sh.cs[j];
+  }
+  __syncthreads();
+  for (int k = 0; k < kRank; ++k) {
+    const double d = sh.g[k][k];
+    const bool keep = d > kDropTol;
+    const double rkk = keep ? sqrt(d) : 0.0;
+    const double inv = keep ? 1.0 / rkk : 0.0;
+    for (int e = tid; e < kRank * kRank; e += 256) {
+      const int i = e / kRank, j = e % kRank;
+      if (i > k && j >= i) sh.g[i][j] -= (sh.g[k][i] * inv) * (sh.g[k][j] * inv);
+    }
+    if (tid > k && tid < kRank) sh.g[tid][k] = sh.g[k][tid] * inv;
+    if (tid == k) sh.rdiag[k] = rkk;
+    __syncthreads();
+  }
+  if (tid < N) {
+    double x[kRank];
+#pragma unroll
+    for (int j = 0; j < kRank; ++j) {
+      double s = static_cast<double>(sh.u.z[tid][j]) * sh.cs[j];
+#pragma unroll
+      for (int i = 0; i < j; ++i) s -= x[i] * sh.g[j][i];
+      const double r = sh.rdiag[j];
+      x[j] = r > 0.0 ? s / r : 0.0;
+    }
+#pragma unroll
+    for (int j = 0; j < kRank; ++j) sh.qt[j][tid] = static_cast<float>(x[j]);
+  }
+  __syncthreads();
+}
+
+// X rows [64 ch, 64 ch + 64) of the tile pair into sh.u.x (anchor subtracted).
+template <typename T, int D>
+__device__ __forceinline__ void codec_load_chunk(CodecShared<2 * D>& sh, const char* ktile,
+                                                 const char* vtile, int ch, int tid) {
+  constexpr int E = T::kBytes;
+  constexpr int EPV = T::kPerVec;
+  constexpr int VPR = D * E / 16;
+  constexpr int VPC = kChunk * VPR;
+#pragma unroll 4
+  for (int v = tid; v < 2 * VPC; v += 256) {
+    const bool isv = v >= VPC;
+    const int w = isv ? v - VPC : v;
+    const int row = w / VPR;
+    const int col = (w % VPR) * EPV;
+    const char* src = (isv ? vtile : ktile) + (static_cast<int64_t>(kChunk * ch + row) * D + col) * E;
+    float f[EPV];
+    T::widen(load16(src), f);
+    const int c0 = (isv ? D : 0) + col;
+#pragma unroll
+    for (int e = 0; e < EPV; e += 4) {
+      float4 o;
+      o.x = f[e + 0] - sh.anc[c0 + e + 0];
+      o.y = f[e + 1] - sh.anc[c0 + e + 1];
+      o.z = f[e + 2] - sh.anc[c0 + e + 2];
+      o.w = f[e + 3] - sh.anc[c0 + e + 3];
+      *reinterpret_cast<float4*>(&sh.u.x[row][c0 + e]) = o;
+    }
+  }
+}
+
+template <typename T, int D>
+__global__ __launch_bounds__(256) void dkv_compress_kernel(DkvCompressArgs a) {
+  constexpr int E = T::kBytes;
+  constexpr int N = 2 * D;
+  constexpr int NCG = N / 16;      // 16-channel groups (contraction of Y)
+  constexpr int NCT = N / 64;      // 16-channel Z tiles per wave
+  constexpr int VPR = D * E / 16;  // 16-byte vectors per K (or V) row
+  __shared__ CodecShared<N> sh;
+
+  const int tid = threadIdx.x;
+  const int lane = tid % kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int hl = lane % 16;
+  const int gi = lane / 16;
+  const int64_t total = static_cast<int64_t>(a.B) * a.max_blocks * a.Hkv;
+  const int n_chunks = a.P / kChunk;
+  const int R = a.n_resid;
+
+  for (int64_t item = blockIdx.x; item < total; item += gridDim.x) {
+    const int g = static_cast<int>(item % a.Hkv);
+    const int64_t bj = item / a.Hkv;
+    const int j = static_cast<int>(bj % a.max_blocks);
+    const int b = static_cast<int>(bj / a.max_blocks);
+    if (j >= window_start_block(a.context_lens[b], a.P, a.recent_window)) continue;
+    const int64_t phys = a.block_table[static_cast<int64_t>(b) * a.max_blocks + j];
+    if (phys < 0 || phys >= a.num_phys) continue;
+    const int64_t tile_off = (phys * a.Hkv + g) * a.P * static_cast<int64_t>(D) * E;
+    const char* ktile = static_cast<const char*>(a.k_pool) + tile_off;
+    const char* vtile = static_cast<const char*>(a.v_pool) + tile_off;
+    char* rec = a.records + (phys * a.Hkv + g) * a.rec_bytes;
+
+    // anchor: float32 copy for the differences, raw copy into the record
+    for (int c = tid; c < N; c += 256) sh.anc[c] = c < D ? T::load1(ktile, c) : T::load1(vtile, c - D);
+    if (tid < 2 * VPR) store16(rec + tid * 16, load16((tid < VPR ? ktile : vtile) + (tid % VPR) * 16));
+    for (int e = tid; e < N * kRank; e += 256) sh.u.z[e / kRank][e % kRank] = codec_start_value(e);
+    __syncthreads();
+    codec_orthonormalize<N>(sh, tid);
+
+    for (int it = 0; it <= a.power_iters; ++it) {
+      const bool last = it == a.power_iters;
+      floatx4 zacc[NCT][2];
+#pragma unroll
+      for (int ct = 0; ct < NCT; ++ct) zacc[ct][0] = zacc[ct][1] = floatx4{0.f, 0.f, 0.f, 0.f};
+      for (int ch = 0; ch < n_chunks; ++ch) {
+        codec_load_chunk<T, D>(sh, ktile, vtile, ch, tid);
+        __syncthreads();
+        // Y = X Q for tokens [16 wave, 16 wave + 16) of the chunk
+        floatx4 yv[2] = {floatx4{0.f, 0.f, 0.f, 0.f}, floatx4{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll 4
+        for (int cg = 0; cg < NCG; ++cg) {
+          const float4 xa = *reinterpret_cast<const float4*>(&sh.u.x[16 * wave + hl][16 * cg + 4 * gi]);
+#pragma unroll
+          for (int rt = 0; rt < 2; ++rt) {
+            const float4 qb = *reinterpret_cast<const float4*>(&sh.qt[16 * rt + hl][16 * cg + 4 * gi]);
+            yv[rt] = mfma4(xa.x, qb.x, yv[rt]);
+            yv[rt] = mfma4(xa.y, qb.y, yv[rt]);
+            yv[rt] = mfma4(xa.z, qb.z, yv[rt]);
+            yv[rt] = mfma4(xa.w, qb.w, yv[rt]);
+          }
+        }
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            const int t = 16 * wave + 4 * gi + v;
+            sh.y[t][16 * rt + hl] = yv[rt][v];
+            if (last)
+              reinterpret_cast<float*>(rec + a.off_coef)[(kChunk * ch + t) * kRank + 16 * rt + hl] = yv[rt][v];
+          }
+        __syncthreads();
+        if (!last) {
+          // Z += X^T Y over the chunk; k-slot gi of step s is token 4 s + gi
+#pragma unroll 4
+          for (int s = 0; s < kChunk / 4; ++s) {
+            const int t = 4 * s + gi;
+            const float yb0 = sh.y[t][hl];
+            const float yb1 = sh.y[t][16 + hl];
+#pragma unroll
+            for (int ct = 0; ct < NCT; ++ct) {
+              const float xa = sh.u.x[t][16 * (wave * NCT + ct) + hl];
+              zacc[ct][0] = mfma4(xa, yb0, zacc[ct][0]);
+              zacc[ct][1] = mfma4(xa, yb1, zacc[ct][1]);
+            }
+          }
+        } else {
+          // squared error of X - Y Q^T for tokens [16 wave, 16 wave + 16)
+          float sq[4] = {0.f, 0.f, 0.f, 0.f};
+          for (int ct = 0; ct < NCG; ++ct) {
+            floatx4 xh = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int rg = 0; rg < 2; ++rg) {
+              const float4 ya = *reinterpret_cast<const float4*>(&sh.y[16 * wave + hl][16 * rg + 4 * gi]);
+              const int r0 = 16 * rg + 4 * gi;
+              xh = mfma4(ya.x, sh.qt[r0 + 0][16 * ct + hl], xh);
+              xh = mfma4(ya.y, sh.qt[r0 + 1][16 * ct + hl], xh);
+              xh = mfma4(ya.z, sh.qt[r0 + 2][16 * ct + hl], xh);
+              xh = mfma4(ya.w, sh.qt[r0 + 3][16 * ct + hl], xh);
+            }
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+              const float e = sh.u.x[16 * wave + 4 * gi + v][16 * ct + hl] - xh[v];
+              sq[v] += e * e;
+            }
+          }
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            sq[v] = group_sum<16>(sq[v]);
+            if (hl == 0) sh.err2[kChunk * ch + 16 * wave + 4 * gi + v] = sq[v];
+          }
+        }
+        __syncthreads();  // x and y are overwritten next
+      }
+      if (!last) {
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+          for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+            for (int v = 0; v < 4; ++v)
+              sh.u.z[16 * (wave * NCT + ct) + 4 * gi + v][16 * rt + hl] = zacc[ct][rt][v];
+        __syncthreads();
+        codec_orthonormalize<N>(sh, tid);
+      }
+    }
+
+    // basis rows
+    for (int e = 4 * tid; e < kRank * N; e += 4 * 256) {
+      const int r = e / N, c = e % N;
+      *reinterpret_cast<float4*>(rec + a.off_basis + static_cast<int64_t>(e) * 4) =
+          *reinterpret_cast<const float4*>(&sh.qt[r][c]);
+    }
+    // residual tokens: rank of each token's error, then ascending offsets
+    if (tid < a.P) {
+      const float e = sh.err2[tid];
+      int rank = 0;
+      for (int u = 0; u < a.P; ++u) {
+        const float f = sh.err2[u];
+        rank += (f > e) || (f == e && u < tid);
+      }
+      sh.flag[tid] = rank < R;
+    }
+    __syncthreads();
+    if (tid < a.P && sh.flag[tid]) {
+      int pos = 0;
+      for (int u = 0; u < tid; ++u) pos += sh.flag[u];
+      if (pos < R) sh.ridx[pos] = tid;
+    }
+    __syncthreads();
+    if (tid < R) reinterpret_cast<int32_t*>(rec + a.off_ridx)[tid] = sh.ridx[tid];
+    for (int v = tid; v < R * 2 * VPR; v += 256) {
+      const int row = v / (2 * VPR);
+      const int w = v % (2 * VPR);
+      const bool isv = w >= VPR;
+      const int64_t src_off = static_cast<int64_t>(sh.ridx[row]) * D * E + (w % VPR) * 16;
+      char* dst = rec + (isv ? a.off_rv : a.off_rk) + static_cast<int64_t>(row) * D * E + (w % VPR) * 16;
+      store16(dst, load16((isv ? vtile : ktile) + src_off));
+    }
+    __syncthreads();  // LDS is reused by the next item
+  }
+}
+
+template <typename T>
+hipError_t launch_dkv_compress_d(const DkvCompressArgs& a, int D, hipStream_t stream) {
+  const int64_t total = static_cast<int64_t>(a.B) * a.max_blocks * a.Hkv;
+  if (total <= 0) return hipSuccess;
+  const int grid = total < 1024 ? static_cast<int>(total) : 1024;
+  if (a.P % kChunk != 0 || a.P > 256) return hipErrorInvalidValue;
+  if (D == 64) {
+    hipLaunchKernelGGL((dkv_compress_kernel<T, 64>), dim3(grid), dim3(256), 0, stream, a);
+  } else if (D == 128) {
+    hipLaunchKernelGGL((dkv_compress_kernel<T, 128>), dim3(grid), dim3(256), 0, stream, a);
+  } else {
+    return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_dkv_decode(const DkvDecodeArgs& a, int dtype, int D, hipStream_t stream) {
@@ -415,11 +734,12 @@ hipError_t launch_dkv_decode(const DkvDecodeArgs& a, int dtype, int D, hipStream
 }
 
 hipError_t launch_dkv_compress(const DkvCompressArgs& a, int dtype, int D, hipStream_t stream) {
-  (void)a;
-  (void)dtype;
-  (void)D;
-  (void)stream;
-  return hipErrorNotSupported;
+  switch (dtype) {
+    case KVSP_F32: return launch_dkv_compress_d<F32>(a, D, stream);
+    case KVSP_F16: return launch_dkv_compress_d<F16>(a, D, stream);
+    case KVSP_BF16: return launch_dkv_compress_d<BF16>(a, D, stream);
+  }
+  return hipErrorInvalidValue;
 }
 
 }  // namespace kvsp

@@ -114,7 +114,7 @@ struct DkvCompressArgs {
   char* records;
   int64_t rec_bytes;
   int32_t off_basis, off_coef, off_rk, off_rv, off_ridx;
-  int32_t B, Hkv, P, max_blocks, recent_window, n_resid, power_iters;
+  int32_t B, Hkv, P, max_blocks, num_phys, recent_window, n_resid, power_iters;
 };
 hipError_t launch_dkv_decode(const DkvDecodeArgs& a, int dtype, int D, hipStream_t stream);
 hipError_t launch_dkv_compress(const DkvCompressArgs& a, int dtype, int D, hipStream_t stream);
