@@ -12,6 +12,12 @@ Prints ONE JSON line: steps/s for the step, selected-KV GB/s of the attention
 call against the 8 TB/s HBM3E peak, and the CPU oracle timed on this host.
 
   python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+                  [--host-pool] [--dkv]
+
+--dkv adds the DKV variant (DKV abstract) on its own workload, Qwen2.5-1.5B-
+like heads with 256-token jointly low-rank blocks: the codec over every older
+block, and a DKV step (scores + attention over the compressed kept blocks and
+the exact window) beside the exact sparse step on the same selection.
 """
 
 from __future__ import annotations
@@ -132,6 +138,114 @@ def time_cpu_oracle_sampled(case, n_pairs=64, budget_s=20.0):
                        f"single-threaded C++ double")
 
 
+DKV_WORKLOAD = "qwen2.5-1.5b-gqa-bf16-L65536-top16-dkv-R16"
+
+
+def dkv_record_payload(case, n_resid):
+    """Bytes of one compressed (block, KV head) record that carry data: anchor
+    rows, rank-32 basis and coefficients (float32), residual rows and offsets."""
+    E = {"fp32": 4, "fp16": 2, "bf16": 2}[case.dtype]
+    return (2 * case.D * E + 32 * 2 * case.D * 4 + case.P * 32 * 4 + n_resid * 2 * case.D * E
+            + 4 * n_resid)
+
+
+def bench_dkv(args, capture, timed):
+    """The DKV variant on its own workload (see the module docstring)."""
+    import torch
+
+    from query_aware_sparse_block_amd import device as dev
+    from query_aware_sparse_block_amd import kvsp
+    from query_aware_sparse_block_amd import workloads as wl
+
+    n_resid = 16
+    print(f"[bench] generating {DKV_WORKLOAD}", file=sys.stderr, flush=True)
+    case = wl.c4_dkv(L=65536, n_resid=n_resid)
+    dkv = kvsp.DkvParams(n_resid=n_resid)
+    dc0 = dev.upload(case)
+    buf0 = dev.alloc_buffers(dc0)
+    dev.build_summaries(dc0, buf0)  # routing summaries are made before compression
+    recs0 = dev.alloc_dkv_records(dc0, dkv)
+    torch.cuda.synchronize()
+
+    # the codec: one launch compresses every block older than the window
+    dev.dkv_compress(dc0, dkv, recs0)  # warm
+    torch.cuda.synchronize()
+    n_comp = 5
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(n_comp):
+        dev.dkv_compress(dc0, dkv, recs0)
+    t1.record()
+    torch.cuda.synchronize()
+    comp_us = t0.elapsed_time(t1) / n_comp * 1e3
+
+    # replicas of pool, summaries and records, rotated per step (cache hygiene
+    # as for the headline workload)
+    pool_bytes = dc0.k_pool.numel() * dc0.k_pool.element_size() * 2
+    rec_total = recs0.numel()
+    R = max(3, -(-(2 << 30) // (pool_bytes + rec_total)))
+    reps, bufs, recs, wss = [dc0], [buf0], [recs0], [kvsp.alloc_dkv_workspace(dc0.layout, dkv)]
+    for _ in range(R - 1):
+        d = dev.DeviceCase(case, dc0.q.clone(), dc0.k_pool.clone(), dc0.v_pool.clone(),
+                           dc0.block_table.clone(), dc0.ctx_lens.clone(), dc0.layout, dc0.params)
+        b = dev.alloc_buffers(d)
+        b.summaries.copy_(buf0.summaries)
+        reps.append(d)
+        bufs.append(b)
+        recs.append(recs0.clone())
+        wss.append(kvsp.alloc_dkv_workspace(d.layout, dkv))
+    torch.cuda.synchronize()
+
+    def dkv_step(i):
+        j = i % R
+        dev.score_topk(reps[j], bufs[j])
+        dev.dkv_decode(reps[j], bufs[j], dkv, recs[j], wss[j])
+
+    def exact_step(i):
+        dev.decode_step(reps[i % R], bufs[i % R])
+
+    for i in range(max(args.warmup, R)):
+        dkv_step(i)
+        exact_step(i)
+    torch.cuda.synchronize()
+    dkv_s = timed(capture(dkv_step))
+    dec_s = timed(capture(lambda i: dev.dkv_decode(reps[i % R], bufs[i % R], dkv, recs[i % R],
+                                                   wss[i % R])))
+    exact_s = timed(capture(exact_step))
+    exact_dec_s = timed(capture(lambda i: dev.sparse_decode(reps[i % R], bufs[i % R])))
+
+    E = {"fp32": 4, "fp16": 2, "bf16": 2}[case.dtype]
+    L = int(case.ctx_lens[0])
+    C = max(0, L - case.recent_window) // case.P
+    k = int(bufs[0].num_selected[0].item())
+    window = L - C * case.P
+    payload = dkv_record_payload(case, n_resid)
+    exact_block = 2 * case.P * case.D * E
+    dkv_bytes = (case.B * case.Hkv * (k * payload + window * 2 * case.D * E)
+                 + case.B * case.Hq * case.D * E + case.B * case.Hq * (case.D + 1) * 4)
+    exact_bytes = (case.B * case.Hkv * (k * case.P + window) * 2 * case.D * E
+                   + case.B * case.Hq * case.D * E + case.B * case.Hq * (case.D + 1) * 4)
+    steps = args.steps
+    return {
+        "workload": DKV_WORKLOAD,
+        "n_resid": n_resid, "rank": 32, "kept_blocks": k, "candidate_blocks": C,
+        "window_tokens": window, "pool_replicas": R,
+        "record_payload_bytes": payload, "exact_block_bytes": exact_block,
+        "block_size_ratio": exact_block / payload,
+        "compress": {"us_per_launch": comp_us, "records": case.B * C * case.Hkv,
+                     "us_per_record": comp_us / (case.B * C * case.Hkv)},
+        "step_us": dkv_s / steps * 1e6,
+        "decode_us": dec_s / steps * 1e6,
+        "decode_bytes": dkv_bytes,
+        "decode_gbps": dkv_bytes / (dec_s / steps) / 1e9,
+        "exact_step_us": exact_s / steps * 1e6,
+        "exact_decode_us": exact_dec_s / steps * 1e6,
+        "exact_decode_bytes": exact_bytes,
+        "note": "latency-bound (a few MiB per call): us/step is the figure of merit",
+    }
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -144,6 +258,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--host-pool", action="store_true",
                     help="also time the decode over a host-resident (pinned, mapped) pool")
+    ap.add_argument("--dkv", action="store_true",
+                    help="also time the DKV codec and decode on the 256-token-block workload")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the library has "
@@ -270,6 +386,8 @@ def main():
         cpu = time_cpu_oracle_sampled(case) if big else time_cpu_oracle(case)
         cpu["cores_available"] = os.cpu_count()
 
+    dkv = bench_dkv(args, capture, timed) if args.dkv else None
+
     E = {"fp32": 4, "fp16": 2, "bf16": 2}[case.dtype]
     rec = {
         "metric": METRIC,
@@ -329,6 +447,7 @@ def main():
         },
         "scoring": {"bytes_per_launch": scoring_bytes(case, Cs),
                     "gbps": scoring_bytes(case, Cs) / (sel_s / args.steps) / 1e9},
+        "dkv": dkv,
         "cpu_baseline": cpu,
     }
     print(json.dumps(rec), flush=True)

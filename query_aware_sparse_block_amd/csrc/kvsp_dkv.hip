@@ -70,6 +70,8 @@ __global__ __launch_bounds__(256) void dkv_attend_kernel(DkvDecodeArgs a) {
   __shared__ float rsum[4][16];
   __shared__ uint32_t res_mask[8];
   __shared__ int last_flag;
+  __shared__ float merge_w[16][kWave];  // split-KV merge: chunk weights per head
+  __shared__ float merge_h[16][3];      // per head: normaliser, window weight, max
 
   const int lane = threadIdx.x % kWave;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
@@ -349,34 +351,59 @@ __global__ __launch_bounds__(256) void dkv_attend_kernel(DkvDecodeArgs a) {
     }
     __syncthreads();
     if (!last_flag) continue;
+    // Every chunk's (m, l) at once: a wave per head, a lane per chunk; the
+    // chunk weights 2^(m_c - M) go to LDS.
     const int64_t slot0 = static_cast<int64_t>(pair) * a.n_chunks;
-    for (int o = threadIdx.x; o < G * D; o += blockDim.x) {
-      const int h = o / D;
-      const int d = o - h * D;
+    for (int h = wave; h < G; h += 4) {
       const int64_t hq = static_cast<int64_t>(b) * a.Hq + g * G + h;
       const float lw = a.lse_w[hq];
-      float M = lw == NEG_INF ? NEG_INF : lw * kLog2e;
-      const float mw = M;
+      const float mw = lw == NEG_INF ? NEG_INF : lw * kLog2e;
+      const bool has = lane < n_act;
+      const float mc = has ? load_coherent(a.part_ml + ((slot0 + lane) * 16 + h) * 2) : NEG_INF;
+      const float lc = has ? load_coherent(a.part_ml + ((slot0 + lane) * 16 + h) * 2 + 1) : 0.f;
+      const bool valid = lc > 0.f;
+      const float M = fmaxf(group_max<64>(valid ? mc : NEG_INF), mw);
+      const float wc = valid ? __builtin_amdgcn_exp2f(mc - M) : 0.f;
+      const float ww = M == NEG_INF ? 0.f : __builtin_amdgcn_exp2f(mw - M);
+      const float Ls = group_sum<64>(wc * lc) + ww;
+      merge_w[h][lane] = wc;
+      if (lane == 0) {
+        merge_h[h][0] = Ls;
+        merge_h[h][1] = ww;
+        merge_h[h][2] = M;
+      }
+    }
+    __syncthreads();
+    // Weighted sums over the chunks: independent 16-byte device-coherent loads.
+    const __amdgpu_buffer_rsrc_t prs = coherent_rsrc(
+        a.part_acc + slot0 * 16 * D, static_cast<uint32_t>(n_act * 16 * D * sizeof(float)));
+    for (int o = threadIdx.x; o < G * (D / 4); o += blockDim.x) {
+      const int h = o / (D / 4);
+      const int d = (o - h * (D / 4)) * 4;
+      const int64_t hq = static_cast<int64_t>(b) * a.Hq + g * G + h;
+      float4 num = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll 8
       for (int cc = 0; cc < n_act; ++cc) {
-        const float l = load_coherent(a.part_ml + ((slot0 + cc) * 16 + h) * 2 + 1);
-        if (l > 0.f) M = fmaxf(M, load_coherent(a.part_ml + ((slot0 + cc) * 16 + h) * 2));
+        const float w = merge_w[h][cc];
+        const float4 p = load_coherent4(prs, static_cast<uint32_t>(((cc * 16 + h) * D + d) * sizeof(float)));
+        num.x += w * p.x;
+        num.y += w * p.y;
+        num.z += w * p.z;
+        num.w += w * p.w;
       }
-      float Ls = 0.f, num = 0.f;
-      if (M != NEG_INF) {
-        for (int cc = 0; cc < n_act; ++cc) {
-          const float l = load_coherent(a.part_ml + ((slot0 + cc) * 16 + h) * 2 + 1);
-          if (l > 0.f) {
-            const float w = __builtin_amdgcn_exp2f(load_coherent(a.part_ml + ((slot0 + cc) * 16 + h) * 2) - M);
-            Ls += w * l;
-            num += w * load_coherent(a.part_acc + ((slot0 + cc) * 16 + h) * D + d);
-          }
-        }
-        const float ww = __builtin_amdgcn_exp2f(mw - M);
-        Ls += ww;
-        num += ww * a.out_w[hq * D + d];
+      const float Ls = merge_h[h][0];
+      const float ww = merge_h[h][1];
+      const float4 ow = *reinterpret_cast<const float4*>(a.out_w + hq * D + d);
+      float4 o4 = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (Ls > 0.f) {
+        o4.x = (num.x + ww * ow.x) / Ls;
+        o4.y = (num.y + ww * ow.y) / Ls;
+        o4.z = (num.z + ww * ow.z) / Ls;
+        o4.w = (num.w + ww * ow.w) / Ls;
       }
-      a.out[hq * D + d] = Ls > 0.f ? num / Ls : 0.f;
-      if (a.lse != nullptr && d == 0) a.lse[hq] = Ls > 0.f ? (M + __builtin_log2f(Ls)) * kLn2 : NEG_INF;
+      *reinterpret_cast<float4*>(a.out + hq * D + d) = o4;
+      if (a.lse != nullptr && d == 0)
+        a.lse[hq] = Ls > 0.f ? (merge_h[h][2] + __builtin_log2f(Ls)) * kLn2 : NEG_INF;
     }
     __syncthreads();
     if (threadIdx.x == 0) store_coherent_i(a.counters + pair, 0);  // ready for the next call
