@@ -128,3 +128,75 @@ def test_small_workspace_rejected():
     args[4] = None
     assert lib.kvsp_score_topk(ctypes.byref(lay), ctypes.byref(par), *args, FAKE, need - 1,
                                None) == -3
+
+
+# ---- DKV entry points (host checks only) ---------------------------------------
+
+@pytest.mark.parametrize("D,P,dtype,R", [(128, 256, 2, 16), (64, 64, 0, 0), (128, 128, 1, 64),
+                                         (64, 256, 2, 33)])
+def test_dkv_record_bytes_match_the_packer(D, P, dtype, R):
+    from query_aware_sparse_block_amd import workloads as wl
+    lay = _layout(head_dim=D, block_size=P, dtype=dtype)
+    n = kvsp.kvsp_dkv_record_bytes(lay, kvsp.DkvParams(n_resid=R))
+    E = 4 if dtype == 0 else 2
+    assert n == wl.dkv_record_layout(D, P, E, R)["bytes"] and n % 256 == 0
+    ws = kvsp.kvsp_dkv_workspace_bytes(lay, kvsp.DkvParams(n_resid=R))
+    assert ws >= kvsp.library().kvsp_workspace_bytes(ctypes.byref(lay), ctypes.byref(_params()))
+
+
+@pytest.mark.parametrize("lay_over,dkv", [
+    ({}, kvsp.DkvParams(rank=16)),
+    ({}, kvsp.DkvParams(n_resid=65)),
+    ({"block_size": 32}, kvsp.DkvParams()),
+    ({"head_dim": 96}, kvsp.DkvParams()),
+    ({"num_q_heads": 34, "num_kv_heads": 2}, kvsp.DkvParams()),
+])
+def test_dkv_unsupported_arguments(lay_over, dkv):
+    lay = _layout(**lay_over)
+    assert kvsp.kvsp_dkv_record_bytes(lay, dkv) == 0
+    assert kvsp.kvsp_dkv_workspace_bytes(lay, dkv) == 0
+    lib = kvsp.library()
+    d = dkv.c()
+    st = lib.kvsp_dkv_compress(ctypes.byref(lay), ctypes.byref(d), 64, *([FAKE] * 5), None)
+    assert st in (-1, -2)
+
+
+def test_dkv_compress_rejects_bad_calls():
+    lib = kvsp.library()
+    lay = _layout()
+    d = kvsp.DkvParams().c()
+    assert lib.kvsp_dkv_compress(ctypes.byref(lay), None, 64, *([FAKE] * 5), None) == -1
+    assert lib.kvsp_dkv_compress(ctypes.byref(lay), ctypes.byref(d), -1, *([FAKE] * 5), None) == -1
+    for i in range(5):
+        args = [FAKE] * 5
+        args[i] = None
+        assert lib.kvsp_dkv_compress(ctypes.byref(lay), ctypes.byref(d), 64, *args, None) == -1
+    bad = kvsp.DkvParams(power_iters=-1).c()
+    assert lib.kvsp_dkv_compress(ctypes.byref(lay), ctypes.byref(bad), 64, *([FAKE] * 5),
+                                 None) == -1
+
+
+def test_dkv_decode_rejects_bad_calls():
+    lib = kvsp.library()
+    lay, par = _layout(), _params()
+    d = kvsp.DkvParams().c()
+    for i in range(8):  # q, pools, records, table, lengths, selection
+        args = [FAKE] * 8
+        args[i] = None
+        assert lib.kvsp_dkv_decode(ctypes.byref(lay), ctypes.byref(par), ctypes.byref(d), *args,
+                                   ctypes.c_float(0), FAKE, FAKE, FAKE, 1 << 30, None) == -1
+    assert lib.kvsp_dkv_decode(ctypes.byref(lay), ctypes.byref(par), ctypes.byref(d), *([FAKE] * 8),
+                               ctypes.c_float(0), None, FAKE, FAKE, 1 << 30, None) == -1  # out
+    assert lib.kvsp_dkv_decode(ctypes.byref(lay), None, ctypes.byref(d), *([FAKE] * 8),
+                               ctypes.c_float(0), FAKE, FAKE, FAKE, 1 << 30, None) == -1
+
+
+@pytest.mark.skipif(_have_gpu(), reason="fake pointers must never reach a real device")
+def test_dkv_decode_small_workspace_rejected():
+    lib = kvsp.library()
+    lay, par = _layout(), _params()
+    dkv = kvsp.DkvParams()
+    need = kvsp.kvsp_dkv_workspace_bytes(lay, dkv)
+    d = dkv.c()
+    assert lib.kvsp_dkv_decode(ctypes.byref(lay), ctypes.byref(par), ctypes.byref(d), *([FAKE] * 8),
+                               ctypes.c_float(0), FAKE, FAKE, FAKE, need - 1, None) == -3
