@@ -81,10 +81,11 @@ def scoring_bytes(case, plans_C):
     return sum(plans_C) * case.Hkv * case.D * 4 + case.B * case.Hq * case.D * 2
 
 
-def time_cpu_oracle(case, budget_s=10.0):
+def time_cpu_oracle(case, budget_s=10.0, threads=1):
     """The oracle, as it stands, timed on this host: one whole decode step
     (scores, Top-k, spans, attention for every (sequence, head); summaries
-    precomputed like the GPU's). Repeated until `budget_s` of CPU work."""
+    precomputed like the GPU's). Repeated until `budget_s` of CPU work. With
+    `threads` > 1 the (sequence, head) attentions run on that many threads."""
     import oracle
     summ = oracle.summaries(case.dtype, case.k_pool, case.block_table, case.ctx_lens, case.Hkv,
                             case.P, case.D)
@@ -93,18 +94,20 @@ def time_cpu_oracle(case, budget_s=10.0):
     while True:
         t0 = time.perf_counter()
         oracle.decode_step(case.dtype, case.q, case.k_pool, case.v_pool, case.block_table,
-                           case.ctx_lens, summ, Hkv=case.Hkv, P=case.P, **case.select_params)
+                           case.ctx_lens, summ, Hkv=case.Hkv, P=case.P, threads=threads,
+                           **case.select_params)
         times.append(time.perf_counter() - t0)
         if time.perf_counter() - t_start > budget_s or len(times) >= 50:
             break
     times.sort()
     med = times[len(times) // 2]
-    return dict(value=1.0 / med, unit="steps/s", cores=1, kind="oracle",
+    how = "single-threaded" if threads == 1 else f"OpenMP over (sequence, head), {threads} threads"
+    return dict(value=1.0 / med, unit="steps/s", cores=threads, kind="oracle",
                 sample=f"{len(times)} whole steps of the same workload "
-                       f"(median {med * 1e3:.1f} ms/step), single-threaded C++ double")
+                       f"(median {med * 1e3:.1f} ms/step), {how}, C++ double")
 
 
-def time_cpu_oracle_sampled(case, n_pairs=64, budget_s=20.0):
+def time_cpu_oracle_sampled(case, n_pairs=64, budget_s=20.0, threads=1):
     """For workloads too large for whole oracle steps: scores + Top-k for every
     sequence, attention for a sample of (sequence, head) pairs, scaled to the
     whole batch."""
@@ -121,21 +124,23 @@ def time_cpu_oracle_sampled(case, n_pairs=64, budget_s=20.0):
     t0 = time.perf_counter()
     oracle.decode_step(case.dtype, case.q, case.k_pool, case.v_pool, case.block_table,
                        case.ctx_lens, summ, Hkv=case.Hkv, P=case.P, head_mask=mask,
-                       **case.select_params)
+                       threads=threads, **case.select_params)
     t_sel = time.perf_counter() - t0
     for b, h in pairs:
         mask[b, h] = 1
     t0 = time.perf_counter()
     oracle.decode_step(case.dtype, case.q, case.k_pool, case.v_pool, case.block_table,
                        case.ctx_lens, summ, Hkv=case.Hkv, P=case.P, head_mask=mask,
-                       **case.select_params)
+                       threads=threads, **case.select_params)
     t_with = time.perf_counter() - t0
-    per_pair = max(t_with - t_sel, 1e-9) / len(pairs)
-    total = t_sel + per_pair * case.B * case.Hq
-    return dict(value=1.0 / total, unit="steps/s", cores=1, kind="oracle",
+    # with several threads the sampled pairs run in rounds of `threads`
+    per_round = max(t_with - t_sel, 1e-9) / -(-len(pairs) // threads)
+    total = t_sel + per_round * -(-(case.B * case.Hq) // threads)
+    how = "single-threaded" if threads == 1 else f"OpenMP over (sequence, head), {threads} threads"
+    return dict(value=1.0 / total, unit="steps/s", cores=threads, kind="oracle",
                 sample=f"selection for all {case.B} sequences + attention for {len(pairs)} of "
                        f"{case.B * case.Hq} (sequence, head) pairs, scaled to the batch; "
-                       f"single-threaded C++ double")
+                       f"{how}, C++ double")
 
 
 DKV_WORKLOAD = "qwen2.5-1.5b-gqa-bf16-L65536-top16-dkv-R16"
@@ -385,6 +390,12 @@ def main():
         big = sum(tokens) * case.Hq * case.D > 2e9
         cpu = time_cpu_oracle_sampled(case) if big else time_cpu_oracle(case)
         cpu["cores_available"] = os.cpu_count()
+        # the same oracle with its (sequence, head) loop on the host's thread share
+        threads = max(1, int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1)))
+        if threads > 1:
+            mt = (time_cpu_oracle_sampled(case, threads=threads) if big
+                  else time_cpu_oracle(case, budget_s=5.0, threads=threads))
+            cpu["openmp"] = {k: mt[k] for k in ("value", "unit", "cores", "sample")}
 
     dkv = bench_dkv(args, capture, timed) if args.dkv else None
 

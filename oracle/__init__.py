@@ -27,7 +27,7 @@ def build(force: bool = True, src: str = _SRC, out: str = _LIB) -> str:
     if force or not os.path.exists(out):
         tmp = out + ".tmp"
         cmd = ["g++", "-O2", "-std=c++17", "-fPIC", "-shared", "-ffp-contract=off",
-               "-fno-fast-math", "-Wall", "-Wextra", "-o", tmp, src]
+               "-fno-fast-math", "-fopenmp", "-Wall", "-Wextra", "-o", tmp, src]
         subprocess.check_call(cmd)
         os.replace(tmp, out)
     return out
@@ -56,7 +56,7 @@ def _bind(path: str):
     L.kvsp_oracle_append.argtypes = [ctypes.c_int, P, P, i32, i32, i32, P, P, P, i32, P, i32, P,
                                      P]
     L.kvsp_oracle_decode_step.argtypes = ([ctypes.c_int] + [i32] * 6 + [P] * 6 + [i32] * 7
-                                          + [f64] + [P] * 8)
+                                          + [f64] + [P] * 8 + [i32])
     return L
 
 
@@ -218,8 +218,10 @@ def attend_tokens(dtype, q_h, k_pool, v_pool, Hkv, P, D, g, bt_row, tokens, scal
 
 def decode_step(dtype, q, k_pool, v_pool, block_table, ctx_lens, summ, *, Hkv, P, top_k=0,
                 keep_num=1, keep_den=1, keep_floor=1, recent_window=0, gamma_num=1,
-                gamma_den=1, scale=0.0, head_mask=None):
-    """Steps 2-5 and the dense fallback for a batch (summaries given).
+                gamma_den=1, scale=0.0, head_mask=None, threads=1):
+    """Steps 2-5 and the dense fallback for a batch (summaries given);
+    ``threads`` > 1 runs the (sequence, head) attentions on that many host
+    threads.
 
     Returns a dict with plan [B][5], scores, sel, spans, nspans, out, lse
     (out/lse NaN where head_mask is 0)."""
@@ -241,6 +243,6 @@ def decode_step(dtype, q, k_pool, v_pool, block_table, ctx_lens, summ, *, Hkv, P
         _p(np.ascontiguousarray(ctx_lens, np.int32)), _p(np.ascontiguousarray(summ)), top_k,
         keep_num, keep_den, keep_floor, recent_window, gamma_num, gamma_den, scale,
         _p(mask) if mask is not None else None, _p(plan_a), _p(scores_a), _p(sel_a), _p(spans_a),
-        _p(nspans_a), _p(out), _p(lse))
+        _p(nspans_a), _p(out), _p(lse), int(threads))
     return dict(plan=plan_a, scores=scores_a, sel=sel_a, spans=spans_a, nspans=nspans_a, out=out,
                 lse=lse)

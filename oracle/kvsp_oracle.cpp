@@ -359,7 +359,9 @@ int32_t kvsp_oracle_attended_tokens(int32_t L, int32_t P, int32_t C, const int32
 //   spans     [B][max_blocks+1][2], nspans [B]
 //   out       [B][Hq][D], lse [B][Hq] — only for (b, h) with head_mask[b*Hq+h]
 //             != 0 (head_mask NULL means all).
-// scale <= 0 means 1/sqrt(D).
+// scale <= 0 means 1/sqrt(D). The (sequence, query head) attentions are
+// independent; `threads` > 1 spreads them over that many host threads
+// (OpenMP) without changing what each one computes.
 void kvsp_oracle_decode_step(int dtype, int32_t B, int32_t Hq, int32_t Hkv, int32_t D,
                              int32_t P, int32_t max_blocks, const void* q, const void* k_pool,
                              const void* v_pool, const int32_t* block_table,
@@ -368,10 +370,12 @@ void kvsp_oracle_decode_step(int dtype, int32_t B, int32_t Hq, int32_t Hkv, int3
                              int32_t recent_window, int32_t gamma_num, int32_t gamma_den,
                              double scale, const uint8_t* head_mask, int32_t* plan,
                              double* scores, int32_t* sel, int32_t* spans, int32_t* nspans,
-                             double* out, double* lse) {
+                             double* out, double* lse, int32_t threads) {
   const int64_t elem = dtype == 0 ? 4 : 2;
   if (!(scale > 0.0)) scale = 1.0 / std::sqrt(static_cast<double>(D));
   const int32_t G = Hq / Hkv;
+  std::vector<std::vector<int32_t>> tokens(static_cast<size_t>(B));
+  std::vector<int32_t> ntok(static_cast<size_t>(B));
   for (int32_t b = 0; b < B; ++b) {
     const int32_t L = ctx_lens[b];
     int32_t* pl = plan + 5 * b;
@@ -386,16 +390,18 @@ void kvsp_oracle_decode_step(int dtype, int32_t B, int32_t Hq, int32_t Hkv, int3
     kvsp_oracle_topk(score_b, C, k, sel_b);
     nspans[b] = kvsp_oracle_spans(sel_b, k, C, n,
                                   spans + static_cast<int64_t>(b) * (max_blocks + 1) * 2);
-    std::vector<int32_t> tokens(static_cast<size_t>(L));
-    const int32_t ntok = kvsp_oracle_attended_tokens(L, P, C, sel_b, k, dense, tokens.data());
-    const int32_t* bt_row = block_table + static_cast<int64_t>(b) * max_blocks;
-    for (int32_t h = 0; h < Hq; ++h) {
-      if (head_mask && !head_mask[static_cast<int64_t>(b) * Hq + h]) continue;
-      kvsp_oracle_attend_tokens(dtype, q_b + static_cast<int64_t>(h) * D * elem, k_pool, v_pool,
-                                Hkv, P, D, h / G, bt_row, tokens.data(), ntok, scale,
-                                out + (static_cast<int64_t>(b) * Hq + h) * D,
-                                lse + static_cast<int64_t>(b) * Hq + h);
-    }
+    tokens[b].resize(static_cast<size_t>(L));
+    ntok[b] = kvsp_oracle_attended_tokens(L, P, C, sel_b, k, dense, tokens[b].data());
+  }
+  const int64_t pairs = static_cast<int64_t>(B) * Hq;
+#pragma omp parallel for num_threads(threads > 1 ? threads : 1) schedule(dynamic, 1)
+  for (int64_t i = 0; i < pairs; ++i) {
+    if (head_mask && !head_mask[i]) continue;
+    const int32_t b = static_cast<int32_t>(i / Hq), h = static_cast<int32_t>(i % Hq);
+    const char* q_h = static_cast<const char*>(q) + i * D * elem;
+    kvsp_oracle_attend_tokens(dtype, q_h, k_pool, v_pool, Hkv, P, D, h / G,
+                              block_table + static_cast<int64_t>(b) * max_blocks,
+                              tokens[b].data(), ntok[b], scale, out + i * D, lse + i);
   }
 }
 

@@ -175,3 +175,16 @@ def test_empty_sequence_step():
     assert r["nspans"][0] == 0
     assert not r["out"][0].any() and np.isneginf(r["lse"][0]).all()
     assert np.isfinite(r["lse"][1]).all()
+
+
+def test_threaded_decode_step_is_bit_identical():
+    """Spreading the (sequence, head) attentions over host threads changes no
+    result: every output of the step equals the single-threaded one."""
+    case = wl.c2(L=1024, keep="1/10")
+    summ = oracle.summaries(case.dtype, case.k_pool, case.block_table, case.ctx_lens, case.Hkv,
+                            case.P, case.D)
+    args = (case.dtype, case.q, case.k_pool, case.v_pool, case.block_table, case.ctx_lens, summ)
+    one = oracle.decode_step(*args, Hkv=case.Hkv, P=case.P, threads=1, **case.select_params)
+    many = oracle.decode_step(*args, Hkv=case.Hkv, P=case.P, threads=4, **case.select_params)
+    for key in one:
+        assert np.array_equal(one[key], many[key], equal_nan=True), key
