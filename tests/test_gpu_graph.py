@@ -115,3 +115,52 @@ def test_graph_of_append_score_decode_replays():
         for k in KEYS:
             assert np.array_equal(got[k], eager[k]), f"replay {rep}: {k} differs"
         assert torch.equal(buf.summaries, summ0) and torch.equal(dc.k_pool, k0)
+
+
+def test_graph_of_dkv_compress_score_decode_replays():
+    # the DKV variant in one graph: compress every older block, then score,
+    # select and decode over the compressed blocks and the exact window. The
+    # codec is deterministic, so every replay must reproduce the eager step
+    # and the eager records byte for byte.
+    from query_aware_sparse_block_amd import kvsp
+    case = wl.c4_dkv(L=8192, n_resid=8)
+    H.note("[graph] dkv compress + score + decode, qwen-like 8192")
+    dc = dev.upload(case)
+    buf = dev.alloc_buffers(dc)
+    dev.build_summaries(dc, buf)
+    dkv = kvsp.DkvParams(n_resid=8)
+    recs = dev.alloc_dkv_records(dc, dkv)
+    ws = kvsp.alloc_dkv_workspace(dc.layout, dkv)
+
+    def step():
+        dev.dkv_compress(dc, dkv, recs)
+        dev.score_topk(dc, buf)
+        dev.dkv_decode(dc, buf, dkv, recs, ws)
+
+    step()
+    torch.cuda.synchronize()
+    eager = _snapshot(buf)
+    recs0 = recs.clone()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    torch.cuda.synchronize()
+    for rep in range(3):
+        buf.selected.fill_(-1)
+        buf.spans.fill_(-1)
+        for k in ("out", "lse", "scores", "num_selected", "num_spans", "use_dense"):
+            getattr(buf, k).zero_()
+        recs.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        got = _snapshot(buf)
+        for k in KEYS:
+            assert np.array_equal(got[k], eager[k]), f"replay {rep}: {k} differs"
+        assert torch.equal(recs, recs0), f"replay {rep}: records differ"
