@@ -24,6 +24,10 @@ the abstract fixes, not bit by bit:
   decode of the same records at the exact-path bars (2e-3 for 16-bit caches,
   1e-5 for fp32 caches; lse 1e-4).
 
+Full size: the benchmark's DKV workload (65536 tokens, 504 records) in the
+benchmark's launch configuration, on a seeded sample of records and every
+output.
+
 Special cases: a block of identical tokens (X = 0: zero basis and
 coefficients, residual tokens the first n_resid offsets), an exactly rank-5
 fp32 block (reconstruction exact to float32 rounding), n_resid 0 and 64, and
@@ -258,3 +262,50 @@ def test_compress_skips_window_blocks_and_empty_sequences():
     # sequence 1 is empty, sequence 2 lies wholly inside the window
     case = codec_case("bf16", 128, 64, 8, 2, [10 * 64 + 5, 0, 100], W=128, seed=843, values="iid")
     run_codec_parity(case, 4, gapped=False)
+
+
+def test_dkv_workload_full_size():
+    # the benchmark's DKV workload at its full size (65536 tokens, 252 older
+    # 256-token blocks x 2 KV heads) in the benchmark's launch configuration:
+    # codec over every older block, then scores, Top-k and the DKV decode.
+    # A seeded sample of records is checked against the SVD (the planted
+    # blocks have a clear gap); the decode is compared with the oracle on the
+    # GPU's own selection and records, and with the oracle's records.
+    case = wl.c4_dkv(L=65536, n_resid=16)
+    H.note(f"dkv full size {case.name}")
+    dc, dkv, recs, host = compress_on_gpu(case, 16)
+    kp, vp = pools_f64(case)
+    older = older_blocks(case)
+    rng = np.random.default_rng(4242)
+    sample = [older[i] for i in rng.choice(len(older), size=24, replace=False)]
+    for _, _, phys in sample:
+        for g in range(case.Hkv):
+            f = wl.dkv_unpack(host[phys, g], case.dtype, case.D, case.P, 16)
+            check_record(case, raw_rows(case, phys, g), f, kp[phys, g], vp[phys, g], 16,
+                         gapped=True)
+    buf = dev.alloc_buffers(dc)
+    dev.build_summaries(dc, buf)
+    dev.score_topk(dc, buf)
+    ws = kvsp.alloc_dkv_workspace(dc.layout, dkv)
+    dev.dkv_decode(dc, buf, dkv, recs, ws)
+    torch.cuda.synchronize()
+    k = int(buf.num_selected[0].item())
+    assert k == 16
+    sel = buf.selected.cpu().numpy()
+    nsel = buf.num_selected.cpu().numpy()
+    out = buf.out.cpu().numpy().astype(np.float64)
+    lse = buf.lse.cpu().numpy().astype(np.float64)
+    used = {(int(case.block_table[0, j]), g) for j in sel[0, :k] for g in range(case.Hkv)}
+    gpu_recs = {key: oracle_fields(wl.dkv_unpack(host[key[0], key[1]], case.dtype, case.D,
+                                                 case.P, 16), case.dtype) for key in used}
+    ref_recs = {key: DKV.compress_block(kp[key[0], key[1]], vp[key[0], key[1]], 32, 16)
+                for key in used}
+    q = wl.decode_f32(case.q, case.dtype)
+    args = dict(Hkv=case.Hkv, P=case.P, recent_window=case.recent_window,
+                scale=1.0 / np.sqrt(case.D))
+    ref, ref_lse = DKV.decode(q, kp, vp, gpu_recs, case.block_table, case.ctx_lens, sel, nsel,
+                              **args)
+    assert np.abs(out - ref).max() <= H.OUT_TOL[case.dtype]
+    assert np.abs(lse - ref_lse).max() <= H.LSE_TOL
+    ref2, _ = DKV.decode(q, kp, vp, ref_recs, case.block_table, case.ctx_lens, sel, nsel, **args)
+    assert np.abs(ref - ref2).max() <= CODEC_OUT_TOL
