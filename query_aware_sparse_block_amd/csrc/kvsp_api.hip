@@ -3,6 +3,7 @@
 // entry point allocates, synchronises or copies to the host.
 
 #include <stddef.h>
+#include <algorithm>
 #include <stdint.h>
 
 #include "kvsp.h"
@@ -119,10 +120,8 @@ WorkspaceLayout workspace_layout(const kvsp_layout& l) {
 
 kvsp_status from_hip(hipError_t e) { return e == hipSuccess ? KVSP_OK : KVSP_ERR_HIP; }
 
-// window_only: attend only the exact window [C*P, L) of every sequence (the
-// exact half of the DKV decode); selected, num_selected and use_dense unused.
 kvsp_status run_decode(const kvsp_layout* layout, const kvsp_select_params* params, bool all_dense,
-                       bool window_only, const void* q, const void* k_pool, const void* v_pool,
+                       const void* q, const void* k_pool, const void* v_pool,
                        const int32_t* block_table, const int32_t* context_lens,
                        const int32_t* selected, const int32_t* num_selected,
                        const int32_t* use_dense, float scale, float* out, float* lse,
@@ -132,7 +131,7 @@ kvsp_status run_decode(const kvsp_layout* layout, const kvsp_select_params* para
   if (!all_dense && (st = check_params(params)) != KVSP_OK) return st;
   if (!q || !k_pool || !v_pool || !block_table || !context_lens || !out)
     return KVSP_ERR_INVALID_ARG;
-  if (!all_dense && !window_only && (!selected || !num_selected)) return KVSP_ERR_INVALID_ARG;
+  if (!all_dense && (!selected || !num_selected)) return KVSP_ERR_INVALID_ARG;
   const kvsp_layout& l = *layout;
   const WorkspaceLayout wl = workspace_layout(l);
   if (workspace == nullptr || workspace_bytes < wl.total) return KVSP_ERR_WORKSPACE;
@@ -143,10 +142,9 @@ kvsp_status run_decode(const kvsp_layout* layout, const kvsp_select_params* para
   a.v_pool = v_pool;
   a.block_table = block_table;
   a.context_lens = context_lens;
-  const bool no_sel = all_dense || window_only;
-  a.selected = no_sel ? nullptr : selected;
-  a.num_selected = no_sel ? nullptr : num_selected;
-  a.use_dense = no_sel ? nullptr : use_dense;
+  a.selected = all_dense ? nullptr : selected;
+  a.num_selected = all_dense ? nullptr : num_selected;
+  a.use_dense = all_dense ? nullptr : use_dense;
   a.out = out;
   a.lse = lse;
   a.part_acc = reinterpret_cast<float*>(static_cast<char*>(workspace) + wl.part_acc);
@@ -174,7 +172,8 @@ constexpr int kDkvRank = 32;
 constexpr int kDkvMaxResid = 64;
 constexpr int kDkvMaxHeads = 16;      // query heads per KV head (MFMA columns)
 constexpr int kDkvTargetItems = 256;  // decode work items a launch aims for
-constexpr int kDkvMaxChunks = 64;
+constexpr int kDkvMaxChunks = 32;     // compressed-block chunks per (sequence, KV head)
+constexpr int kDkvMaxWindowChunks = 32;  // window chunks per (sequence, KV head)
 constexpr int kDkvDefaultIters = 10;
 
 struct DkvRecordLayout {
@@ -224,20 +223,25 @@ int dkv_chunks(const kvsp_layout& l) {
   return nc;
 }
 
+// Window chunks: the window holds at most W + P - 1 tokens (and no more than
+// the table), cut into 64-token groups; at most kDkvMaxWindowChunks chunks.
+int dkv_window_chunks(const kvsp_layout& l, int32_t recent_window) {
+  const int64_t cap = static_cast<int64_t>(l.max_blocks_per_seq) * l.block_size;
+  const int64_t tokens = std::min<int64_t>(static_cast<int64_t>(recent_window) + l.block_size - 1, cap);
+  const int64_t groups = (tokens + 63) / 64;
+  return static_cast<int>(std::max<int64_t>(1, std::min<int64_t>(groups, kDkvMaxWindowChunks)));
+}
+
 struct DkvWorkspace {
-  size_t decode, out_w, lse_w, counters, part_acc, part_ml, total;
+  size_t counters, part_acc, part_ml, total;
 };
 
+// Sized for the most window chunks, so it does not depend on the window.
 DkvWorkspace dkv_workspace(const kvsp_layout& l) {
   DkvWorkspace w;
-  const size_t slots = static_cast<size_t>(l.batch) * l.num_kv_heads * dkv_chunks(l);
+  const size_t slots = static_cast<size_t>(l.batch) * l.num_kv_heads *
+                       (dkv_chunks(l) + kDkvMaxWindowChunks);
   size_t off = 0;
-  w.decode = off;
-  off += workspace_layout(l).total;
-  w.out_w = off;
-  off += align_up(static_cast<size_t>(l.batch) * l.num_q_heads * l.head_dim * sizeof(float));
-  w.lse_w = off;
-  off += align_up(static_cast<size_t>(l.batch) * l.num_q_heads * sizeof(float));
   w.counters = off;
   off += align_up(static_cast<size_t>(l.batch) * l.num_kv_heads * sizeof(int32_t));
   w.part_acc = off;
@@ -400,7 +404,7 @@ kvsp_status kvsp_sparse_decode(const kvsp_layout* layout, const kvsp_select_para
                                const int32_t* selected, const int32_t* num_selected,
                                const int32_t* use_dense, float scale, float* out, float* lse,
                                void* workspace, size_t workspace_bytes, hipStream_t stream) {
-  return run_decode(layout, params, false, false, q, k_pool, v_pool, block_table, context_lens, selected,
+  return run_decode(layout, params, false, q, k_pool, v_pool, block_table, context_lens, selected,
                     num_selected, use_dense, scale, out, lse, workspace, workspace_bytes, stream);
 }
 
@@ -408,7 +412,7 @@ kvsp_status kvsp_dense_decode(const kvsp_layout* layout, const void* q, const vo
                               const void* v_pool, const int32_t* block_table,
                               const int32_t* context_lens, float scale, float* out, float* lse,
                               void* workspace, size_t workspace_bytes, hipStream_t stream) {
-  return run_decode(layout, nullptr, true, false, q, k_pool, v_pool, block_table, context_lens, nullptr,
+  return run_decode(layout, nullptr, true, q, k_pool, v_pool, block_table, context_lens, nullptr,
                     nullptr, nullptr, scale, out, lse, workspace, workspace_bytes, stream);
 }
 
@@ -473,31 +477,16 @@ kvsp_status kvsp_dkv_decode(const kvsp_layout* layout, const kvsp_select_params*
   const DkvWorkspace ws = dkv_workspace(l);
   if (workspace == nullptr || workspace_bytes < ws.total) return KVSP_ERR_WORKSPACE;
   char* wsb = static_cast<char*>(workspace);
-  float* out_w = reinterpret_cast<float*>(wsb + ws.out_w);
-  float* lse_w = reinterpret_cast<float*>(wsb + ws.lse_w);
-  // The exact half: the window of every sequence, on the split-KV kernel.
-  kvsp_select_params wp = *params;
-  if (wp.keep_floor == 0 && wp.recent_window == 0) wp.keep_floor = 1;  // only the window is read
-  if (wp.keep_den <= 0) wp.keep_den = 1;
-  if (wp.gamma_den <= 0) wp.gamma_den = 1;
-  if (wp.top_k < 0) wp.top_k = 0;
-  if (wp.keep_num < 0) wp.keep_num = 0;
-  if (wp.keep_floor < 0) wp.keep_floor = 0;
-  if (wp.gamma_num < 0) wp.gamma_num = 0;
-  st = run_decode(layout, &wp, false, true, q, k_pool, v_pool, block_table, context_lens, nullptr,
-                  nullptr, nullptr, scale, out_w, lse_w, wsb + ws.decode, ws.out_w - ws.decode,
-                  stream);
-  if (st != KVSP_OK) return st;
   const DkvRecordLayout r = dkv_record_layout(l, dkv->n_resid);
   DkvDecodeArgs a;
   a.q = q;
+  a.k_pool = k_pool;
+  a.v_pool = v_pool;
   a.records = static_cast<const char*>(records);
   a.block_table = block_table;
   a.context_lens = context_lens;
   a.selected = selected;
   a.num_selected = num_selected;
-  a.out_w = out_w;
-  a.lse_w = lse_w;
   a.out = out;
   a.lse = lse;
   a.part_acc = reinterpret_cast<float*>(wsb + ws.part_acc);
@@ -517,6 +506,7 @@ kvsp_status kvsp_dkv_decode(const kvsp_layout* layout, const kvsp_select_params*
   a.recent_window = params->recent_window;
   a.n_resid = dkv->n_resid;
   a.n_chunks = dkv_chunks(l);
+  a.n_wchunks = dkv_window_chunks(l, params->recent_window);
   const float s = scale > 0.f ? scale : 1.0f / __builtin_sqrtf(static_cast<float>(l.head_dim));
   a.scale_log2 = s * 1.4426950408889634f;
   return from_hip(launch_dkv_decode(a, l.dtype, l.head_dim, stream));

@@ -11,11 +11,14 @@
 //   (sum_t p_t) v_a + (sum_t p_t C_t) W_V + sum_residual p_r v_r,
 // so a block costs one pass over C, W and the residual rows.
 //
-// Decode work split. The exact window is attended first by the split-KV
-// kernel of kvsp_decode.hip (window only) into the workspace. Here a
-// workgroup of 4 waves takes a (chunk, sequence, KV head) item: a run of the
-// sequence's selected blocks, folded into one online softmax; each of the
-// group's query heads (at most 16) is one MFMA column. Per block:
+// Decode work split. One launch covers both halves. A workgroup of 4 waves
+// takes a (chunk, sequence, KV head) item, folded into one online softmax;
+// each of the group's query heads (at most 16) is one MFMA column. A chunk is
+// either a run of the sequence's selected compressed blocks or a run of
+// 64-token groups of the exact window. A window group is treated as a block
+// with no compressed token and up to 64 exact rows read from the pool (64
+// divides every supported block size, so a group lies in one block); it takes
+// the residual-row path below and skips the low-rank parts. Per block:
 //   A. every wave stages its quarter of C in LDS, computes a partial
 //      W_K q over a quarter of the channels (fp32 MFMA 16x16x4), the anchor
 //      term, and the exact logits of one tile of 16 residual rows (the
@@ -28,8 +31,7 @@
 //   D. each wave owns D/4 output channels: (p^T C) W_V, the anchor term and
 //      the residual PV on fp32 MFMA, then the online-softmax rescale.
 // Chunks of one (sequence, KV head) merge through the workspace (device-scope
-// stores, a completion counter, the last chunk merges) together with the
-// window result.
+// stores, a completion counter, the last chunk merges).
 #include <stddef.h>
 #include <stdint.h>
 
@@ -71,16 +73,16 @@ __global__ __launch_bounds__(256) void dkv_attend_kernel(DkvDecodeArgs a) {
   __shared__ uint32_t res_mask[8];
   __shared__ int last_flag;
   __shared__ float merge_w[16][kWave];  // split-KV merge: chunk weights per head
-  __shared__ float merge_h[16][3];      // per head: normaliser, window weight, max
+  __shared__ float merge_h[16][2];      // per head: normaliser, max
 
   const int lane = threadIdx.x % kWave;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int hl = lane % 16;  // MFMA column: query head (or rank / channel)
   const int gi = lane / 16;  // lane group: MFMA k-slot, and row quad of outputs
   const int G = a.Hq / a.Hkv;
-  const int R = a.n_resid;
   const int n_pairs = a.B * a.Hkv;
-  const int total = n_pairs * a.n_chunks;
+  const int S = a.n_chunks + a.n_wchunks;  // chunk slots per (sequence, KV head)
+  const int total = n_pairs * S;
   const float NEG_INF = -__builtin_huge_valf();
   const int dbase = wave * 16 * NDT;  // this wave's output channels
 
@@ -96,10 +98,28 @@ __global__ __launch_bounds__(256) void dkv_attend_kernel(DkvDecodeArgs a) {
     int k = a.num_selected[b];
     k = k < 0 ? 0 : (k > C ? C : k);
     const int per = k > 0 ? (k + a.n_chunks - 1) / a.n_chunks : 1;
-    const int n_act = k > 0 ? (k + per - 1) / per : 1;
-    if (c >= n_act) continue;  // uniform over the workgroup
-    const int j0 = c * per;
-    const int j1 = min(k, j0 + per);
+    const int n_act_c = k > 0 ? (k + per - 1) / per : 0;
+    const int wtok = L - C * a.P;            // exact window tokens
+    const int wg = (wtok + 63) / 64;         // 64-token window groups
+    const int wper = (wg + a.n_wchunks - 1) / a.n_wchunks;
+    const int n_act_w = wg > 0 ? (wg + wper - 1) / wper : 0;
+    // Active chunks: compressed ones first, then the window's. An empty
+    // sequence keeps chunk 0 alone (no work: out 0, lse -inf).
+    const int n_act = max(n_act_c + n_act_w, 1);
+    const bool win = c >= a.n_chunks;        // uniform over the workgroup
+    int idx, j0, j1;
+    if (!win) {
+      if (c >= max(n_act_c, n_act_c + n_act_w == 0 ? 1 : 0)) continue;
+      idx = c;
+      j0 = c * per;
+      j1 = min(k, j0 + per);
+    } else {
+      const int w = c - a.n_chunks;
+      if (w >= n_act_w) continue;
+      idx = n_act_c + w;
+      j0 = w * wper;
+      j1 = min(wg, j0 + wper);
+    }
 
     // Query operands (fixed for the item). Heads past G are zero columns.
     const bool head_ok = hl < G;
@@ -126,65 +146,92 @@ __global__ __launch_bounds__(256) void dkv_attend_kernel(DkvDecodeArgs a) {
     for (int dt = 0; dt < NDT; ++dt) acc[dt] = floatx4{0.f, 0.f, 0.f, 0.f};
 
     for (int jj = j0; jj < j1; ++jj) {
-      const int jlog = a.selected[static_cast<int64_t>(b) * a.max_blocks + jj];
-      const int64_t phys = a.block_table[static_cast<int64_t>(b) * a.max_blocks + jlog];
-      const char* rec = a.records + (phys * a.Hkv + g) * a.rec_bytes;
-      const float* basis = reinterpret_cast<const float*>(rec + a.off_basis);
-
-      // ---- A: loads, W_K q partial, anchor term, residual logits ----------------
-      if (wave == 0 && lane < R) {
-        const int r = reinterpret_cast<const int32_t*>(rec + a.off_ridx)[lane];
-        if (r >= 0 && r < a.P) atomicOr(&res_mask[r >> 5], 1u << (r & 31));
+      // Exact rows of this block: the record's residual rows, or a window
+      // group's rows in the pool.
+      const char* rec = nullptr;
+      const char* rk_base;
+      const char* rv_base;
+      int R;
+      if (!win) {
+        const int jlog = a.selected[static_cast<int64_t>(b) * a.max_blocks + jj];
+        const int64_t phys = a.block_table[static_cast<int64_t>(b) * a.max_blocks + jlog];
+        rec = a.records + (phys * a.Hkv + g) * a.rec_bytes;
+        rk_base = rec + a.off_rk;
+        rv_base = rec + a.off_rv;
+        R = a.n_resid;
+      } else {
+        const int t0 = C * a.P + 64 * jj;  // first token of the group
+        const int lb = t0 / a.P;
+        const int64_t phys = a.block_table[static_cast<int64_t>(b) * a.max_blocks + lb];
+        const int64_t row0 = (phys * a.Hkv + g) * a.P + (t0 - lb * a.P);
+        rk_base = static_cast<const char*>(a.k_pool) + row0 * D * E;
+        rv_base = static_cast<const char*>(a.v_pool) + row0 * D * E;
+        R = min(64, wtok - 64 * jj);
       }
-      {
-        const char* src = rec + a.off_coef + static_cast<int64_t>(wave) * TOKW * kRank * 4;
+
+      // ---- A: loads, W_K q partial, anchor term, exact-row logits ---------------
+      float wv[NDT][8];
+      float va[NDT];
+      if (!win) {
+        const float* basis = reinterpret_cast<const float*>(rec + a.off_basis);
+        if (wave == 0 && lane < R) {
+          const int r = reinterpret_cast<const int32_t*>(rec + a.off_ridx)[lane];
+          if (r >= 0 && r < a.P) atomicOr(&res_mask[r >> 5], 1u << (r & 31));
+        }
+        {
+          const char* src = rec + a.off_coef + static_cast<int64_t>(wave) * TOKW * kRank * 4;
 #pragma unroll
-        for (int u = 0; u < 2 * TPW; ++u) {
-          const int vi = lane + kWave * u;  // 16-byte vector of the wave's rows
-          const uint4 v = load16(src + static_cast<int64_t>(vi) * 16);
-          *reinterpret_cast<uint4*>(&c_lds[wave][(vi / 8) * kCRow + (vi % 8) * 4]) = v;
+          for (int u = 0; u < 2 * TPW; ++u) {
+            const int vi = lane + kWave * u;  // 16-byte vector of the wave's rows
+            const uint4 v = load16(src + static_cast<int64_t>(vi) * 16);
+            *reinterpret_cast<uint4*>(&c_lds[wave][(vi / 8) * kCRow + (vi % 8) * 4]) = v;
+          }
+        }
+        float wk[2][QS];
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+          for (int s = 0; s < QS; ++s)
+            wk[nt][s] = basis[(16 * nt + hl) * 2 * D + wave * DQ + gi * QS + s];
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+          for (int s = 0; s < 8; ++s) wv[dt][s] = basis[(gi * 8 + s) * 2 * D + D + dbase + 16 * dt + hl];
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) va[dt] = T::load1(rec, D + dbase + 16 * dt + hl);
+        float qa = 0.f;
+#pragma unroll
+        for (int s = 0; s < QS; ++s) qa += qreg[s] * T::load1(rec, wave * DQ + gi * QS + s);
+        floatx4 qt[2] = {floatx4{0.f, 0.f, 0.f, 0.f}, floatx4{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+          for (int s = 0; s < QS; ++s) qt[nt] = mfma4(qreg[s], wk[nt][s], qt[nt]);
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+          for (int v = 0; v < 4; ++v) qt_part[wave][4 * gi + v][16 * nt + hl] = qt[nt][v];
+        qa_part[wave][gi][hl] = qa;
+      } else {
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) {
+          va[dt] = 0.f;
+#pragma unroll
+          for (int s = 0; s < 8; ++s) wv[dt][s] = 0.f;
         }
       }
-      float wk[2][QS];
-#pragma unroll
-      for (int nt = 0; nt < 2; ++nt)
-#pragma unroll
-        for (int s = 0; s < QS; ++s)
-          wk[nt][s] = basis[(16 * nt + hl) * 2 * D + wave * DQ + gi * QS + s];
-      float wv[NDT][8];
-#pragma unroll
-      for (int dt = 0; dt < NDT; ++dt)
-#pragma unroll
-        for (int s = 0; s < 8; ++s) wv[dt][s] = basis[(gi * 8 + s) * 2 * D + D + dbase + 16 * dt + hl];
-      float va[NDT];
-#pragma unroll
-      for (int dt = 0; dt < NDT; ++dt) va[dt] = T::load1(rec, D + dbase + 16 * dt + hl);
       float vr[RS][NDT];
 #pragma unroll
       for (int s = 0; s < RS; ++s) {
         const int row = 4 * s + gi;
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt)
-          vr[s][dt] = row < R ? T::load1(rec + a.off_rv, static_cast<int64_t>(row) * D + dbase + 16 * dt + hl)
-                              : 0.f;
+          vr[s][dt] = row < R ? T::load1(rv_base, static_cast<int64_t>(row) * D + dbase + 16 * dt + hl) : 0.f;
       }
-      float qa = 0.f;
-#pragma unroll
-      for (int s = 0; s < QS; ++s) qa += qreg[s] * T::load1(rec, wave * DQ + gi * QS + s);
-      floatx4 qt[2] = {floatx4{0.f, 0.f, 0.f, 0.f}, floatx4{0.f, 0.f, 0.f, 0.f}};
-#pragma unroll
-      for (int nt = 0; nt < 2; ++nt)
-#pragma unroll
-        for (int s = 0; s < QS; ++s) qt[nt] = mfma4(qreg[s], wk[nt][s], qt[nt]);
-#pragma unroll
-      for (int nt = 0; nt < 2; ++nt)
-#pragma unroll
-        for (int v = 0; v < 4; ++v) qt_part[wave][4 * gi + v][16 * nt + hl] = qt[nt][v];
-      qa_part[wave][gi][hl] = qa;
       float rmax = NEG_INF;
       if (16 * wave < R) {
         const int r = min(16 * wave + hl, R - 1);
-        const char* kr = rec + a.off_rk + static_cast<int64_t>(r) * D * E;
+        const char* kr = rk_base + static_cast<int64_t>(r) * D * E;
         floatx4 sc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int s = 0; s < KLD; ++s) sc = QkMfma<T>::step(load16(kr + k_elem_offset<T>(lane, s) * E), qop[s], sc);
@@ -198,36 +245,43 @@ __global__ __launch_bounds__(256) void dkv_attend_kernel(DkvDecodeArgs a) {
       }
       __syncthreads();
 
-      // ---- B: low-rank logits of this wave's tokens --------------------------
-      float qtb[8];
-#pragma unroll
-      for (int s = 0; s < 8; ++s) {
-        const int j = gi * 8 + s;
-        qtb[s] = (qt_part[0][hl][j] + qt_part[1][hl][j]) + (qt_part[2][hl][j] + qt_part[3][hl][j]);
-      }
-      float qa_h = 0.f;
-#pragma unroll
-      for (int w = 0; w < 4; ++w)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) qa_h += qa_part[w][q][hl];
+      // ---- B: low-rank logits of this wave's tokens (none for a window group)
       float s2[TPW][4];
       float lmax = NEG_INF;
+      if (!win) {
+        float qtb[8];
 #pragma unroll
-      for (int mt = 0; mt < TPW; ++mt) {
-        const float* crow = &c_lds[wave][(16 * mt + hl) * kCRow + gi * 8];
-        const float4 c0 = *reinterpret_cast<const float4*>(crow);
-        const float4 c1 = *reinterpret_cast<const float4*>(crow + 4);
-        const float cv[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
-        floatx4 sc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int s = 0; s < 8; ++s) sc = mfma4(cv[s], qtb[s], sc);
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const int tok = wave * TOKW + 16 * mt + 4 * gi + v;
-          const bool resid = (res_mask[tok >> 5] >> (tok & 31)) & 1u;
-          s2[mt][v] = resid ? NEG_INF : (sc[v] + qa_h) * a.scale_log2;
-          lmax = fmaxf(lmax, s2[mt][v]);
+        for (int s = 0; s < 8; ++s) {
+          const int j = gi * 8 + s;
+          qtb[s] = (qt_part[0][hl][j] + qt_part[1][hl][j]) + (qt_part[2][hl][j] + qt_part[3][hl][j]);
         }
+        float qa_h = 0.f;
+#pragma unroll
+        for (int w = 0; w < 4; ++w)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) qa_h += qa_part[w][q][hl];
+#pragma unroll
+        for (int mt = 0; mt < TPW; ++mt) {
+          const float* crow = &c_lds[wave][(16 * mt + hl) * kCRow + gi * 8];
+          const float4 c0 = *reinterpret_cast<const float4*>(crow);
+          const float4 c1 = *reinterpret_cast<const float4*>(crow + 4);
+          const float cv[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+          floatx4 sc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int s = 0; s < 8; ++s) sc = mfma4(cv[s], qtb[s], sc);
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            const int tok = wave * TOKW + 16 * mt + 4 * gi + v;
+            const bool resid = (res_mask[tok >> 5] >> (tok & 31)) & 1u;
+            s2[mt][v] = resid ? NEG_INF : (sc[v] + qa_h) * a.scale_log2;
+            lmax = fmaxf(lmax, s2[mt][v]);
+          }
+        }
+      } else {
+#pragma unroll
+        for (int mt = 0; mt < TPW; ++mt)
+#pragma unroll
+          for (int v = 0; v < 4; ++v) s2[mt][v] = NEG_INF;
       }
       lmax = fold_max<16>(fmaxf(lmax, rmax));
       if (gi == 0) wmax[wave][hl] = lmax;
@@ -245,18 +299,20 @@ __global__ __launch_bounds__(256) void dkv_attend_kernel(DkvDecodeArgs a) {
           s2[mt][v] = p;
           ls += p;
         }
-      floatx4 cb[2] = {floatx4{0.f, 0.f, 0.f, 0.f}, floatx4{0.f, 0.f, 0.f, 0.f}};
+      if (!win) {  // a window group has no coefficients (its p here are all 0)
+        floatx4 cb[2] = {floatx4{0.f, 0.f, 0.f, 0.f}, floatx4{0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
-      for (int nt = 0; nt < 2; ++nt)
+        for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
-        for (int mt = 0; mt < TPW; ++mt)
+          for (int mt = 0; mt < TPW; ++mt)
 #pragma unroll
-          for (int v = 0; v < 4; ++v)
-            cb[nt] = mfma4(s2[mt][v], c_lds[wave][(16 * mt + 4 * gi + v) * kCRow + 16 * nt + hl], cb[nt]);
+            for (int v = 0; v < 4; ++v)
+              cb[nt] = mfma4(s2[mt][v], c_lds[wave][(16 * mt + 4 * gi + v) * kCRow + 16 * nt + hl], cb[nt]);
 #pragma unroll
-      for (int nt = 0; nt < 2; ++nt)
+        for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
-        for (int v = 0; v < 4; ++v) cb_part[wave][4 * gi + v][16 * nt + hl] = cb[nt][v];
+          for (int v = 0; v < 4; ++v) cb_part[wave][4 * gi + v][16 * nt + hl] = cb[nt][v];
+      }
       ls = fold_sum<16>(ls);
       if (gi == 0) wsum[wave][hl] = ls;
       float rs = 0.f;
@@ -291,13 +347,15 @@ __global__ __launch_bounds__(256) void dkv_attend_kernel(DkvDecodeArgs a) {
 #pragma unroll
       for (int s = 0; s < 8; ++s) {
         const int j = gi * 8 + s;
-        ca[s] = (cb_part[0][hl][j] + cb_part[1][hl][j]) + (cb_part[2][hl][j] + cb_part[3][hl][j]);
+        ca[s] = win ? 0.f : (cb_part[0][hl][j] + cb_part[1][hl][j]) + (cb_part[2][hl][j] + cb_part[3][hl][j]);
       }
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt) {
         floatx4 t = {0.f, 0.f, 0.f, 0.f};
+        if (!win) {
 #pragma unroll
-        for (int s = 0; s < 8; ++s) t = mfma4(ca[s], wv[dt][s], t);
+          for (int s = 0; s < 8; ++s) t = mfma4(ca[s], wv[dt][s], t);
+        }
 #pragma unroll
         for (int s = 0; s < RS; ++s)
           if (4 * s < R) t = mfma4(p_res[4 * s + gi][hl], vr[s][dt], t);
@@ -307,28 +365,19 @@ __global__ __launch_bounds__(256) void dkv_attend_kernel(DkvDecodeArgs a) {
       __syncthreads();  // LDS is reused by the next block
     }
 
-    // ---- merge the chunks of (b, g) and the window result --------------------
-    const int64_t slot = static_cast<int64_t>(pair) * a.n_chunks + c;
+    // ---- merge the chunks of (b, g) ------------------------------------------------
+    const int64_t slot = static_cast<int64_t>(pair) * S + idx;
     if (n_act == 1) {
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
         const int h = 4 * gi + v;
         if (h >= G) continue;
         const int64_t hq = static_cast<int64_t>(b) * a.Hq + g * G + h;
-        const float lw = a.lse_w[hq];
-        const float mw = lw == NEG_INF ? NEG_INF : lw * kLog2e;
-        const float M = fmaxf(m_run[v], mw);
-        const float wc = M == NEG_INF ? 0.f : __builtin_amdgcn_exp2f(m_run[v] - M);
-        const float ww = M == NEG_INF ? 0.f : __builtin_amdgcn_exp2f(mw - M);
-        const float Ls = l_run[v] * wc + ww;
-        const float inv = Ls > 0.f ? 1.f / Ls : 0.f;
+        const float inv = l_run[v] > 0.f ? 1.f / l_run[v] : 0.f;
 #pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) {
-          const int d = dbase + 16 * dt + hl;
-          a.out[hq * D + d] = (acc[dt][v] * wc + a.out_w[hq * D + d] * ww) * inv;
-        }
+        for (int dt = 0; dt < NDT; ++dt) a.out[hq * D + dbase + 16 * dt + hl] = acc[dt][v] * inv;
         if (a.lse != nullptr && wave == 0 && hl == 0)
-          a.lse[hq] = Ls > 0.f ? (M + __builtin_log2f(Ls)) * kLn2 : NEG_INF;
+          a.lse[hq] = l_run[v] > 0.f ? (m_run[v] + __builtin_log2f(l_run[v])) * kLn2 : NEG_INF;
       }
       continue;
     }
@@ -353,24 +402,19 @@ __global__ __launch_bounds__(256) void dkv_attend_kernel(DkvDecodeArgs a) {
     if (!last_flag) continue;
     // Every chunk's (m, l) at once: a wave per head, a lane per chunk; the
     // chunk weights 2^(m_c - M) go to LDS.
-    const int64_t slot0 = static_cast<int64_t>(pair) * a.n_chunks;
+    const int64_t slot0 = static_cast<int64_t>(pair) * S;
     for (int h = wave; h < G; h += 4) {
-      const int64_t hq = static_cast<int64_t>(b) * a.Hq + g * G + h;
-      const float lw = a.lse_w[hq];
-      const float mw = lw == NEG_INF ? NEG_INF : lw * kLog2e;
       const bool has = lane < n_act;
       const float mc = has ? load_coherent(a.part_ml + ((slot0 + lane) * 16 + h) * 2) : NEG_INF;
       const float lc = has ? load_coherent(a.part_ml + ((slot0 + lane) * 16 + h) * 2 + 1) : 0.f;
       const bool valid = lc > 0.f;
-      const float M = fmaxf(group_max<64>(valid ? mc : NEG_INF), mw);
+      const float M = group_max<64>(valid ? mc : NEG_INF);
       const float wc = valid ? __builtin_amdgcn_exp2f(mc - M) : 0.f;
-      const float ww = M == NEG_INF ? 0.f : __builtin_amdgcn_exp2f(mw - M);
-      const float Ls = group_sum<64>(wc * lc) + ww;
+      const float Ls = group_sum<64>(wc * lc);
       merge_w[h][lane] = wc;
       if (lane == 0) {
         merge_h[h][0] = Ls;
-        merge_h[h][1] = ww;
-        merge_h[h][2] = M;
+        merge_h[h][1] = M;
       }
     }
     __syncthreads();
@@ -392,18 +436,16 @@ __global__ __launch_bounds__(256) void dkv_attend_kernel(DkvDecodeArgs a) {
         num.w += w * p.w;
       }
       const float Ls = merge_h[h][0];
-      const float ww = merge_h[h][1];
-      const float4 ow = *reinterpret_cast<const float4*>(a.out_w + hq * D + d);
       float4 o4 = make_float4(0.f, 0.f, 0.f, 0.f);
       if (Ls > 0.f) {
-        o4.x = (num.x + ww * ow.x) / Ls;
-        o4.y = (num.y + ww * ow.y) / Ls;
-        o4.z = (num.z + ww * ow.z) / Ls;
-        o4.w = (num.w + ww * ow.w) / Ls;
+        o4.x = num.x / Ls;
+        o4.y = num.y / Ls;
+        o4.z = num.z / Ls;
+        o4.w = num.w / Ls;
       }
       *reinterpret_cast<float4*>(a.out + hq * D + d) = o4;
       if (a.lse != nullptr && d == 0)
-        a.lse[hq] = Ls > 0.f ? (merge_h[h][2] + __builtin_log2f(Ls)) * kLn2 : NEG_INF;
+        a.lse[hq] = Ls > 0.f ? (merge_h[h][1] + __builtin_log2f(Ls)) * kLn2 : NEG_INF;
     }
     __syncthreads();
     if (threadIdx.x == 0) store_coherent_i(a.counters + pair, 0);  // ready for the next call
@@ -412,7 +454,7 @@ __global__ __launch_bounds__(256) void dkv_attend_kernel(DkvDecodeArgs a) {
 
 template <typename T, int D>
 hipError_t launch_dkv_decode_t(const DkvDecodeArgs& a, hipStream_t stream) {
-  const int total = a.B * a.Hkv * a.n_chunks;
+  const int total = a.B * a.Hkv * (a.n_chunks + a.n_wchunks);
   const int grid = total < 2048 ? total : 2048;
   switch (a.P) {
     case 64: hipLaunchKernelGGL((dkv_attend_kernel<T, D, 1>), dim3(grid), dim3(256), 0, stream, a); break;

@@ -81,20 +81,23 @@ struct DecodeArgs {
   float scale_log2;             // softmax scale * log2(e)
 };
 
-// DKV decode over compressed blocks. Work item (chunk c, pair = b * Hkv + g),
-// numbered item = c * B * Hkv + pair; chunk c takes selected blocks
-// [c * per, min(k, (c + 1) * per)) with per = ceil(k / n_chunks). Partials live
-// at slot pair * n_chunks + c; counters[pair] counts finished chunks. The
-// window result (out_w, lse_w) is merged in at the end.
+// DKV decode over compressed blocks and the exact window, one launch. Work
+// item (chunk slot c, pair = b * Hkv + g), numbered item = c * B * Hkv + pair,
+// with S = n_chunks + n_wchunks slots per pair. Slot c < n_chunks takes
+// selected blocks [c * per, min(k, (c + 1) * per)), per = ceil(k / n_chunks);
+// slot n_chunks + w takes 64-token window groups [w * wper, ...), wper =
+// ceil(groups / n_wchunks). Active chunks are numbered compressed first;
+// partials live at slot pair * S + that number; counters[pair] counts
+// finished chunks.
 struct DkvDecodeArgs {
   const void* q;
+  const void* k_pool;
+  const void* v_pool;
   const char* records;
   const int32_t* block_table;
   const int32_t* context_lens;
   const int32_t* selected;
   const int32_t* num_selected;
-  const float* out_w;           // [B][Hq][D] window-only attention
-  const float* lse_w;           // [B][Hq] natural log
   float* out;
   float* lse;                   // may be NULL
   float* part_acc;              // [slots][16][D]
@@ -102,7 +105,7 @@ struct DkvDecodeArgs {
   int32_t* counters;            // [B * Hkv], zero between calls
   int64_t rec_bytes;
   int32_t off_basis, off_coef, off_rk, off_rv, off_ridx;
-  int32_t B, Hq, Hkv, P, max_blocks, recent_window, n_resid, n_chunks;
+  int32_t B, Hq, Hkv, P, max_blocks, recent_window, n_resid, n_chunks, n_wchunks;
   float scale_log2;
 };
 // DKV codec: one work item per (sequence, candidate block, KV head).

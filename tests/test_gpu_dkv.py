@@ -9,8 +9,9 @@ caches and 1e-5 for fp32 caches, lse within 1e-4.
 
 Cases: every dtype, head dims 64 and 128, block sizes 64, 128 and 256,
 1 to 16 query heads per KV head, residual budgets 0 to 64, ragged contexts,
-sequences with nothing selected, an empty window, the chunk-merge path and a
-batch large enough that every work item folds several blocks."""
+sequences with nothing selected, an empty window, the chunk-merge path, a
+batch large enough that every work item folds several blocks, and windows
+long enough that every window chunk folds several 64-token groups."""
 
 import numpy as np
 import pytest
@@ -126,3 +127,16 @@ def test_decode_large_batch_items_fold_several_blocks():
     ctx = [16 * 64 + 3 * b for b in range(32)]
     case = small_case("bf16", 64, 64, 16, 8, ctx, W=100, seed=734)
     run_decode_parity(case, 8, k_max=7, seed=6)
+
+
+def test_decode_long_window_folds_several_groups():
+    # windows of up to ~5000 tokens: 80 groups of 64 exact tokens in at most
+    # 32 window chunks, so each window chunk folds several groups; ragged ends
+    case = small_case("bf16", 128, 64, 8, 2, [100 * 64 + 7, 80 * 64, 5001], W=4999, seed=735)
+    run_decode_parity(case, 8, k_max=12, seed=7)
+
+
+def test_decode_window_in_256_token_blocks_with_fp32():
+    # fp32 caches at the tighter bar; window groups from several 256-token blocks
+    case = small_case("fp32", 64, 256, 8, 2, [7 * 256 + 200, 2 * 256 + 1], W=700, seed=736)
+    run_decode_parity(case, 16, k_max=4, seed=8)
