@@ -12,12 +12,13 @@ Prints ONE JSON line: steps/s for the step, selected-KV GB/s of the attention
 call against the 8 TB/s HBM3E peak, and the CPU oracle timed on this host.
 
   python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
-                  [--host-pool] [--dkv]
+                  [--host-pool] [--no-dkv]
 
---dkv adds the DKV variant (DKV abstract) on its own workload, Qwen2.5-1.5B-
-like heads with 256-token jointly low-rank blocks: the codec over every older
-block, and a DKV step (scores + attention over the compressed kept blocks and
-the exact window) beside the exact sparse step on the same selection.
+After the headline timing the line also carries the DKV variant (DKV
+abstract) on its own workload, Qwen2.5-1.5B-like heads with 256-token jointly
+low-rank blocks: the codec over every older block, and a DKV step (scores +
+attention over the compressed kept blocks and the exact window) beside the
+exact sparse step on the same selection (skip it with --no-dkv).
 """
 
 from __future__ import annotations
@@ -263,8 +264,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--host-pool", action="store_true",
                     help="also time the decode over a host-resident (pinned, mapped) pool")
-    ap.add_argument("--dkv", action="store_true",
-                    help="also time the DKV codec and decode on the 256-token-block workload")
+    ap.add_argument("--no-dkv", action="store_true",
+                    help="skip the DKV codec and decode on the 256-token-block workload")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the library has "
@@ -397,7 +398,7 @@ def main():
                   else time_cpu_oracle(case, budget_s=5.0, threads=threads))
             cpu["openmp"] = {k: mt[k] for k in ("value", "unit", "cores", "sample")}
 
-    dkv = bench_dkv(args, capture, timed) if args.dkv else None
+    dkv = None if args.no_dkv else bench_dkv(args, capture, timed)
 
     E = {"fp32": 4, "fp16": 2, "bf16": 2}[case.dtype]
     rec = {
