@@ -531,6 +531,7 @@ __device__ void codec_orthonormalize(CodecShared<N>& sh, int tid) {
   {
     const int i = tid / 8, jq = tid % 8;
     double g0 = 0.0, g1 = 0.0, g2 = 0.0, g3 = 0.0;
+#pragma unroll 8
     for (int c = 0; c < N; ++c) {
       const double zi = sh.u.z[c][i];
       const float4 zj = *reinterpret_cast<const float4*>(&sh.u.z[c][4 * jq]);
@@ -584,23 +585,48 @@ __device__ void codec_orthonormalize(CodecShared<N>& sh, int tid) {
   __syncthreads();
 }
 
-// X rows [64 ch, 64 ch + 64) of the tile pair into sh.u.x (anchor subtracted).
+// X rows [64 ch, 64 ch + 64) of the tile pair: codec_issue_chunk requests
+// them into registers, codec_commit_chunk writes them to sh.u.x with the
+// anchor subtracted. (Requesting the next chunk while the current one is
+// computed measured no faster: the tiles are L2-resident after the first
+// round.)
 template <typename T, int D>
-__device__ __forceinline__ void codec_load_chunk(CodecShared<2 * D>& sh, const char* ktile,
-                                                 const char* vtile, int ch, int tid) {
-  constexpr int E = T::kBytes;
+struct CodecChunk {
+  static constexpr int VPR = D * T::kBytes / 16;   // 16-byte vectors per K (or V) row
+  static constexpr int VPC = kChunk * VPR;          // per pool and chunk
+  static constexpr int PER_THREAD = 2 * VPC / 256;  // K and V vectors per thread
+  uint4 v[PER_THREAD];
+};
+
+template <typename T, int D>
+__device__ __forceinline__ void codec_issue_chunk(CodecChunk<T, D>& cc, const char* ktile,
+                                                  const char* vtile, int ch, int tid) {
+  using CC = CodecChunk<T, D>;
+#pragma unroll
+  for (int u = 0; u < CC::PER_THREAD; ++u) {
+    const int v = tid + 256 * u;
+    const bool isv = v >= CC::VPC;
+    const int w = isv ? v - CC::VPC : v;
+    const int row = w / CC::VPR;
+    const int col = (w % CC::VPR) * T::kPerVec;
+    cc.v[u] = load16((isv ? vtile : ktile) + (static_cast<int64_t>(kChunk * ch + row) * D + col) * T::kBytes);
+  }
+}
+
+template <typename T, int D>
+__device__ __forceinline__ void codec_commit_chunk(CodecShared<2 * D>& sh, const CodecChunk<T, D>& cc,
+                                                   int tid) {
+  using CC = CodecChunk<T, D>;
   constexpr int EPV = T::kPerVec;
-  constexpr int VPR = D * E / 16;
-  constexpr int VPC = kChunk * VPR;
-#pragma unroll 4
-  for (int v = tid; v < 2 * VPC; v += 256) {
-    const bool isv = v >= VPC;
-    const int w = isv ? v - VPC : v;
-    const int row = w / VPR;
-    const int col = (w % VPR) * EPV;
-    const char* src = (isv ? vtile : ktile) + (static_cast<int64_t>(kChunk * ch + row) * D + col) * E;
+#pragma unroll
+  for (int u = 0; u < CC::PER_THREAD; ++u) {
+    const int v = tid + 256 * u;
+    const bool isv = v >= CC::VPC;
+    const int w = isv ? v - CC::VPC : v;
+    const int row = w / CC::VPR;
+    const int col = (w % CC::VPR) * EPV;
     float f[EPV];
-    T::widen(load16(src), f);
+    T::widen(cc.v[u], f);
     const int c0 = (isv ? D : 0) + col;
 #pragma unroll
     for (int e = 0; e < EPV; e += 4) {
@@ -658,7 +684,9 @@ __global__ __launch_bounds__(256) void dkv_compress_kernel(DkvCompressArgs a) {
 #pragma unroll
       for (int ct = 0; ct < NCT; ++ct) zacc[ct][0] = zacc[ct][1] = floatx4{0.f, 0.f, 0.f, 0.f};
       for (int ch = 0; ch < n_chunks; ++ch) {
-        codec_load_chunk<T, D>(sh, ktile, vtile, ch, tid);
+        CodecChunk<T, D> now;
+        codec_issue_chunk<T, D>(now, ktile, vtile, ch, tid);
+        codec_commit_chunk<T, D>(sh, now, tid);
         __syncthreads();
         // Y = X Q for tokens [16 wave, 16 wave + 16) of the chunk
         floatx4 yv[2] = {floatx4{0.f, 0.f, 0.f, 0.f}, floatx4{0.f, 0.f, 0.f, 0.f}};
