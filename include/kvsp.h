@@ -91,13 +91,14 @@ typedef enum { KVSP_F32 = 0, KVSP_F16 = 1, KVSP_BF16 = 2 } kvsp_dtype;
 
 /* Shape of the batch and the pool (host struct). */
 typedef struct {
-  int32_t batch;              /* B >= 1 */
-  int32_t num_q_heads;        /* Hq, a multiple of num_kv_heads */
+  int32_t batch;              /* B: 1 .. 65536 */
+  int32_t num_q_heads;        /* Hq: a multiple of num_kv_heads, <= 1024 */
   int32_t num_kv_heads;       /* Hkv >= 1 */
   int32_t head_dim;           /* D: 64 or 128 */
   int32_t block_size;         /* P: 16, 32, 64, 128 or 256 tokens */
   int32_t num_phys_blocks;    /* pool capacity in blocks */
   int32_t max_blocks_per_seq; /* row stride of block_table, <= 16384 */
+                              /* also: num_kv_heads * head_dim <= 7168 */
   int32_t dtype;              /* kvsp_dtype of q, K and V */
 } kvsp_layout;
 

@@ -15,6 +15,9 @@ namespace {
 
 constexpr size_t kAlign = 256;
 constexpr int kMaxBlocksPerSeq = 16384;
+// Bounds that keep every work-item count and per-head product in int32.
+constexpr int kMaxBatch = 65536;
+constexpr int kMaxQHeads = 1024;
 constexpr int kMaxSummaryRow = 7168;   // Hkv * D: the score kernel stages it in LDS as double
 // Workgroup items per decode launch (about one per resident workgroup) and the
 // cap on launched workgroups; items beyond it are taken in grid-stride order.
@@ -62,6 +65,7 @@ kvsp_status check_layout(const kvsp_layout* l) {
       l->max_blocks_per_seq < 1)
     return KVSP_ERR_INVALID_ARG;
   if (l->num_q_heads % l->num_kv_heads != 0) return KVSP_ERR_INVALID_ARG;
+  if (l->batch > kMaxBatch || l->num_q_heads > kMaxQHeads) return KVSP_ERR_UNSUPPORTED;
   if (l->head_dim != 64 && l->head_dim != 128) return KVSP_ERR_UNSUPPORTED;
   if (!pow2(l->block_size) || l->block_size < 16 || l->block_size > 256) return KVSP_ERR_UNSUPPORTED;
   if (l->dtype != KVSP_F32 && l->dtype != KVSP_F16 && l->dtype != KVSP_BF16) return KVSP_ERR_UNSUPPORTED;

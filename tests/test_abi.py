@@ -67,6 +67,10 @@ def test_workspace_bytes():
     (dict(batch=0), -1),
     (dict(max_blocks_per_seq=20000), -2),
     (dict(num_kv_heads=64, num_q_heads=64), -2),
+    (dict(batch=65537), -2),
+    (dict(batch=2**31 - 1), -2),
+    (dict(num_q_heads=2048, num_kv_heads=2), -2),
+    (dict(num_q_heads=2**31 - 1, num_kv_heads=1), -2),
 ])
 def test_bad_layout_rejected(over, code):
     lib = kvsp.library()
