@@ -133,15 +133,47 @@ def make_layout(q: torch.Tensor, k_pool: torch.Tensor, block_table: torch.Tensor
     return kvsp_layout(B, Hq, Hkv, D, P, num_phys, block_table.shape[1], DTYPE_CODES[q.dtype])
 
 
-def _ptr(t):
+_ELEM_BYTES = {0: 4, 1: 2, 2: 2}
+_CODE_DTYPES = {0: torch.float32, 1: torch.float16, 2: torch.bfloat16}
+
+
+def _ptr(t, name="argument", nbytes=None, dtype=None):
     """Device address of a contiguous device tensor, or of a mapped pinned
-    host buffer (an object with `device_ptr`)."""
+    host buffer (an object with `device_ptr` and `nbytes`). With `nbytes`
+    and `dtype` the buffer is checked against what the layout needs, so a
+    short or mistyped buffer raises here instead of reaching a kernel. None
+    passes through (the C entry points reject missing required pointers)."""
     if t is None:
         return None
     if hasattr(t, "device_ptr"):
+        if nbytes is not None and t.nbytes < nbytes:
+            raise ValueError(f"{name}: {t.nbytes} bytes, the layout needs {nbytes}")
         return ctypes.c_void_p(t.device_ptr)
-    assert t.is_cuda and t.is_contiguous(), "device tensors must be contiguous"
+    if not (t.is_cuda and t.is_contiguous()):
+        raise ValueError(f"{name}: a contiguous device tensor is required")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name}: dtype {t.dtype}, expected {dtype}")
+    if nbytes is not None and t.numel() * t.element_size() < nbytes:
+        raise ValueError(f"{name}: {t.numel() * t.element_size()} bytes, the layout needs {nbytes}")
     return ctypes.c_void_p(t.data_ptr())
+
+
+class _Sizes:
+    """Bytes each buffer of the C ABI holds for a layout (kvsp.h layouts)."""
+
+    def __init__(self, L: kvsp_layout):
+        E = _ELEM_BYTES.get(L.dtype, 0)
+        self.cache_dtype = _CODE_DTYPES.get(L.dtype)
+        self.q = L.batch * L.num_q_heads * L.head_dim * E
+        self.pool = L.num_phys_blocks * L.num_kv_heads * L.block_size * L.head_dim * E
+        self.table = L.batch * L.max_blocks_per_seq * 4
+        self.per_seq = L.batch * 4
+        self.summaries = L.num_phys_blocks * L.num_kv_heads * L.head_dim * 4
+        self.row = L.batch * L.max_blocks_per_seq * 4
+        self.spans = L.batch * (L.max_blocks_per_seq + 1) * 2 * 4
+        self.out = L.batch * L.num_q_heads * L.head_dim * 4
+        self.lse = L.batch * L.num_q_heads * 4
+        self.new_rows = L.batch * L.num_kv_heads * L.head_dim * E
 
 
 def _stream(stream) -> ctypes.c_void_p:
@@ -165,45 +197,68 @@ def alloc_workspace(layout: kvsp_layout, params: SelectParams | None = None,
     return torch.zeros(max(n, 1), dtype=torch.uint8, device=device)  # counters start at zero
 
 
+I32, F32 = torch.int32, torch.float32
+
+
 def kvsp_append_kv(layout, k_new, v_new, block_table, positions, k_pool, v_pool, summaries,
                    stream=None):
+    z = _Sizes(layout)
     _check("kvsp_append_kv", library().kvsp_append_kv(
-        ctypes.byref(layout), _ptr(k_new), _ptr(v_new), _ptr(block_table), _ptr(positions),
-        _ptr(k_pool), _ptr(v_pool), _ptr(summaries), _stream(stream)))
+        ctypes.byref(layout), _ptr(k_new, "k_new", z.new_rows, z.cache_dtype),
+        _ptr(v_new, "v_new", z.new_rows, z.cache_dtype), _ptr(block_table, "block_table", z.table, I32),
+        _ptr(positions, "positions", z.per_seq, I32), _ptr(k_pool, "k_pool", z.pool, z.cache_dtype),
+        _ptr(v_pool, "v_pool", z.pool, z.cache_dtype), _ptr(summaries, "summaries", z.summaries, F32),
+        _stream(stream)))
 
 
 def kvsp_build_summaries(layout, k_pool, block_table, context_lens, summaries, stream=None):
+    z = _Sizes(layout)
     _check("kvsp_build_summaries", library().kvsp_build_summaries(
-        ctypes.byref(layout), _ptr(k_pool), _ptr(block_table), _ptr(context_lens),
-        _ptr(summaries), _stream(stream)))
+        ctypes.byref(layout), _ptr(k_pool, "k_pool", z.pool, z.cache_dtype),
+        _ptr(block_table, "block_table", z.table, I32),
+        _ptr(context_lens, "context_lens", z.per_seq, I32),
+        _ptr(summaries, "summaries", z.summaries, F32), _stream(stream)))
 
 
 def kvsp_score_topk(layout, params: SelectParams, q, summaries, block_table, context_lens, scores,
                     selected, num_selected, spans, num_spans, use_dense, workspace=None,
                     stream=None):
     p = params.c()
+    z = _Sizes(layout)
     ws_bytes = workspace.numel() if workspace is not None else 0
     _check("kvsp_score_topk", library().kvsp_score_topk(
-        ctypes.byref(layout), ctypes.byref(p), _ptr(q), _ptr(summaries), _ptr(block_table),
-        _ptr(context_lens), _ptr(scores), _ptr(selected), _ptr(num_selected), _ptr(spans),
-        _ptr(num_spans), _ptr(use_dense), _ptr(workspace), ws_bytes, _stream(stream)))
+        ctypes.byref(layout), ctypes.byref(p), _ptr(q, "q", z.q, z.cache_dtype),
+        _ptr(summaries, "summaries", z.summaries, F32), _ptr(block_table, "block_table", z.table, I32),
+        _ptr(context_lens, "context_lens", z.per_seq, I32), _ptr(scores, "scores", z.row, F32),
+        _ptr(selected, "selected", z.row, I32), _ptr(num_selected, "num_selected", z.per_seq, I32),
+        _ptr(spans, "spans", z.spans, I32), _ptr(num_spans, "num_spans", z.per_seq, I32),
+        _ptr(use_dense, "use_dense", z.per_seq, I32), _ptr(workspace, "workspace"), ws_bytes,
+        _stream(stream)))
 
 
 def kvsp_sparse_decode(layout, params: SelectParams, q, k_pool, v_pool, block_table, context_lens,
                        selected, num_selected, use_dense, scale, out, lse, workspace, stream=None):
     p = params.c()
+    z = _Sizes(layout)
     _check("kvsp_sparse_decode", library().kvsp_sparse_decode(
-        ctypes.byref(layout), ctypes.byref(p), _ptr(q), _ptr(k_pool), _ptr(v_pool),
-        _ptr(block_table), _ptr(context_lens), _ptr(selected), _ptr(num_selected),
-        _ptr(use_dense), ctypes.c_float(scale), _ptr(out), _ptr(lse), _ptr(workspace),
-        workspace.numel(), _stream(stream)))
+        ctypes.byref(layout), ctypes.byref(p), _ptr(q, "q", z.q, z.cache_dtype),
+        _ptr(k_pool, "k_pool", z.pool, z.cache_dtype), _ptr(v_pool, "v_pool", z.pool, z.cache_dtype),
+        _ptr(block_table, "block_table", z.table, I32),
+        _ptr(context_lens, "context_lens", z.per_seq, I32), _ptr(selected, "selected", z.row, I32),
+        _ptr(num_selected, "num_selected", z.per_seq, I32), _ptr(use_dense, "use_dense", z.per_seq, I32),
+        ctypes.c_float(scale), _ptr(out, "out", z.out, F32), _ptr(lse, "lse", z.lse, F32),
+        _ptr(workspace, "workspace"), workspace.numel(), _stream(stream)))
 
 
 def kvsp_dense_decode(layout, q, k_pool, v_pool, block_table, context_lens, scale, out, lse,
                       workspace, stream=None):
+    z = _Sizes(layout)
     _check("kvsp_dense_decode", library().kvsp_dense_decode(
-        ctypes.byref(layout), _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_table),
-        _ptr(context_lens), ctypes.c_float(scale), _ptr(out), _ptr(lse), _ptr(workspace),
+        ctypes.byref(layout), _ptr(q, "q", z.q, z.cache_dtype),
+        _ptr(k_pool, "k_pool", z.pool, z.cache_dtype), _ptr(v_pool, "v_pool", z.pool, z.cache_dtype),
+        _ptr(block_table, "block_table", z.table, I32),
+        _ptr(context_lens, "context_lens", z.per_seq, I32), ctypes.c_float(scale),
+        _ptr(out, "out", z.out, F32), _ptr(lse, "lse", z.lse, F32), _ptr(workspace, "workspace"),
         workspace.numel(), _stream(stream)))
 
 
@@ -235,9 +290,14 @@ def alloc_dkv_workspace(layout: kvsp_layout, dkv: DkvParams, device="cuda") -> t
 def kvsp_dkv_compress(layout, dkv: DkvParams, recent_window, k_pool, v_pool, block_table,
                       context_lens, records, stream=None):
     p = dkv.c()
+    z = _Sizes(layout)
+    rec = kvsp_dkv_record_bytes(layout, dkv) * layout.num_phys_blocks * layout.num_kv_heads
     _check("kvsp_dkv_compress", library().kvsp_dkv_compress(
-        ctypes.byref(layout), ctypes.byref(p), int(recent_window), _ptr(k_pool), _ptr(v_pool),
-        _ptr(block_table), _ptr(context_lens), _ptr(records), _stream(stream)))
+        ctypes.byref(layout), ctypes.byref(p), int(recent_window),
+        _ptr(k_pool, "k_pool", z.pool, z.cache_dtype), _ptr(v_pool, "v_pool", z.pool, z.cache_dtype),
+        _ptr(block_table, "block_table", z.table, I32),
+        _ptr(context_lens, "context_lens", z.per_seq, I32), _ptr(records, "records", rec),
+        _stream(stream)))
 
 
 def kvsp_dkv_decode(layout, params: SelectParams, dkv: DkvParams, q, k_pool, v_pool, records,
@@ -245,8 +305,13 @@ def kvsp_dkv_decode(layout, params: SelectParams, dkv: DkvParams, q, k_pool, v_p
                     stream=None):
     p = params.c()
     d = dkv.c()
+    z = _Sizes(layout)
+    rec = kvsp_dkv_record_bytes(layout, dkv) * layout.num_phys_blocks * layout.num_kv_heads
     _check("kvsp_dkv_decode", library().kvsp_dkv_decode(
-        ctypes.byref(layout), ctypes.byref(p), ctypes.byref(d), _ptr(q), _ptr(k_pool),
-        _ptr(v_pool), _ptr(records), _ptr(block_table), _ptr(context_lens), _ptr(selected),
-        _ptr(num_selected), ctypes.c_float(scale), _ptr(out), _ptr(lse), _ptr(workspace),
+        ctypes.byref(layout), ctypes.byref(p), ctypes.byref(d), _ptr(q, "q", z.q, z.cache_dtype),
+        _ptr(k_pool, "k_pool", z.pool, z.cache_dtype), _ptr(v_pool, "v_pool", z.pool, z.cache_dtype),
+        _ptr(records, "records", rec), _ptr(block_table, "block_table", z.table, I32),
+        _ptr(context_lens, "context_lens", z.per_seq, I32), _ptr(selected, "selected", z.row, I32),
+        _ptr(num_selected, "num_selected", z.per_seq, I32), ctypes.c_float(scale),
+        _ptr(out, "out", z.out, F32), _ptr(lse, "lse", z.lse, F32), _ptr(workspace, "workspace"),
         workspace.numel(), _stream(stream)))

@@ -204,3 +204,35 @@ def test_dkv_decode_small_workspace_rejected():
     d = dkv.c()
     assert lib.kvsp_dkv_decode(ctypes.byref(lay), ctypes.byref(par), ctypes.byref(d), *([FAKE] * 8),
                                ctypes.c_float(0), FAKE, FAKE, FAKE, need - 1, None) == -3
+
+
+# ---- binding checks (no GPU: they raise before any pointer reaches the library) ----
+
+class _FakeHostBuffer:
+    def __init__(self, nbytes):
+        self.nbytes = nbytes
+        self.device_ptr = 0x1000
+
+
+def test_binding_sizes_follow_the_header_layouts():
+    lay = _layout(batch=3, num_q_heads=8, num_kv_heads=2, head_dim=64, block_size=16,
+                  num_phys_blocks=10, max_blocks_per_seq=5, dtype=1)
+    z = kvsp._Sizes(lay)
+    assert z.q == 3 * 8 * 64 * 2 and z.pool == 10 * 2 * 16 * 64 * 2
+    assert z.table == z.row == 3 * 5 * 4 and z.per_seq == 3 * 4
+    assert z.summaries == 10 * 2 * 64 * 4 and z.spans == 3 * 6 * 2 * 4
+    assert z.out == 3 * 8 * 64 * 4 and z.lse == 3 * 8 * 4 and z.new_rows == 3 * 2 * 64 * 2
+    assert z.cache_dtype == torch.float16
+
+
+def test_binding_rejects_host_tensors_and_short_buffers():
+    with pytest.raises(ValueError, match="contiguous device tensor"):
+        kvsp._ptr(torch.zeros(4), "x", 16, torch.float32)
+    with pytest.raises(ValueError, match="needs 64"):
+        kvsp._ptr(_FakeHostBuffer(32), "k_pool", 64)
+    assert kvsp._ptr(_FakeHostBuffer(64), "k_pool", 64).value == 0x1000
+    assert kvsp._ptr(None, "lse") is None
+    lay = _layout()
+    with pytest.raises(ValueError):
+        kvsp.kvsp_build_summaries(lay, torch.zeros(4), torch.zeros(4, dtype=torch.int32),
+                                  torch.zeros(2, dtype=torch.int32), torch.zeros(4))
