@@ -14,7 +14,11 @@ Every pin checks the numpy oracle against something other than itself:
    projector, and equals the planted distinctive tokens of the low-rank
    workload;
 5. a hand-built record decompresses to closed-form rows;
-6. with no block selected only the window is attended.
+6. with no block selected only the window is attended;
+7. the decode equals the engine's own evaluation: low-rank logits from the
+   query projected on the basis (keys never decompressed), value sums
+   through p^T C, the exact window as a separate partial, and a
+   log-sum-exp merge of the halves.
 A mutant copy of the module must fail at least one pin
 (``test_dkv_mutant_is_caught``)."""
 
@@ -200,9 +204,74 @@ def pin_empty_selection_is_window_only(mod=DKV):
     assert np.allclose(lse, ref_lse, rtol=0, atol=1e-12)
 
 
+def pin_low_rank_form_and_lse_merge(mod=DKV):
+    """The decode evaluated the way the abstract describes the engine: a
+    compressed token's logit from the query projected on the basis
+    (<q, k_a> + c_t . (W_K q)), never a decompressed key; the block's value
+    sum as (sum p) v_a + (p^T C) W_V plus the residual rows; the exact window
+    as its own softmax partial; the two halves joined by a log-sum-exp merge.
+    It must equal the oracle's decode, which decompresses every token and
+    attends the union. The basis here is random, not orthonormal: the
+    identity does not depend on it."""
+    rng = np.random.default_rng(17)
+    D, P, r, Hkv, G = 8, 16, 32, 1, 2
+    L, W = 3 * P + 5, 10
+    C = mod.window_start(L, P, W)
+    n = -(-L // P)
+    q = rng.standard_normal((1, Hkv * G, D))
+    k_pool = rng.standard_normal((n, Hkv, P, D))
+    v_pool = rng.standard_normal((n, Hkv, P, D))
+    table = np.arange(n, dtype=np.int32)[None, :]
+    sel = np.arange(C, dtype=np.int32)[None, :]
+    recs = {}
+    for j in range(C):
+        resid = np.sort(rng.choice(P, size=3, replace=False))
+        recs[(j, 0)] = dict(anchor_k=rng.standard_normal(D), anchor_v=rng.standard_normal(D),
+                            basis=rng.standard_normal((r, 2 * D)),
+                            coef=rng.standard_normal((P, r)), resid=resid,
+                            resid_k=rng.standard_normal((3, D)),
+                            resid_v=rng.standard_normal((3, D)))
+    scale = 0.37
+    out, lse = mod.decode(q, k_pool, v_pool, recs, table, np.array([L]), sel, np.array([C]),
+                          Hkv=Hkv, P=P, recent_window=W, scale=scale)
+    for h in range(G):
+        qh = q[0, h]
+        parts = []
+        # compressed half: one partial (m, l, acc) over every selected block
+        z_all, v_terms = [], []
+        for j in range(C):
+            rec = recs[(j, 0)]
+            wk = rec["basis"][:, :D] @ qh
+            is_res = np.zeros(P, bool)
+            is_res[rec["resid"]] = True
+            z = np.where(is_res, -np.inf, scale * (qh @ rec["anchor_k"] + rec["coef"] @ wk))
+            z_res = scale * (rec["resid_k"] @ qh)
+            z_all.append((z, z_res, rec, is_res))
+        m = max(max(np.max(z), np.max(zr)) for z, zr, _, _ in z_all)
+        l, acc = 0.0, np.zeros(D)
+        for z, z_res, rec, is_res in z_all:
+            p = np.exp(z - m)
+            p_res = np.exp(z_res - m)
+            l += p.sum() + p_res.sum()
+            acc += p.sum() * rec["anchor_v"] + (p @ rec["coef"]) @ rec["basis"][:, D:]
+            acc += p_res @ rec["resid_v"]
+        parts.append((m, l, acc))
+        # exact window half
+        kw = np.concatenate([k_pool[j, 0, :min(P, L - j * P)] for j in range(C, n)])
+        vw = np.concatenate([v_pool[j, 0, :min(P, L - j * P)] for j in range(C, n)])
+        zw = scale * (kw @ qh)
+        mw = zw.max()
+        parts.append((mw, np.exp(zw - mw).sum(), np.exp(zw - mw) @ vw))
+        M = max(pm for pm, _, _ in parts)
+        Lsum = sum(pl * np.exp(pm - M) for pm, pl, _ in parts)
+        merged = sum(pa * np.exp(pm - M) for pm, _, pa in parts) / Lsum
+        assert np.allclose(out[0, h], merged, rtol=0, atol=1e-12), h
+        assert abs(lse[0, h] - (M + np.log(Lsum))) <= 1e-12
+
+
 PINS = [pin_eckart_young, pin_residual_brute_force, pin_planted_spikes, pin_hand_record,
         pin_low_rank_blocks_decode_exactly, pin_all_residual_equals_exact,
-        pin_empty_selection_is_window_only]
+        pin_empty_selection_is_window_only, pin_low_rank_form_and_lse_merge]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
