@@ -260,9 +260,17 @@ DkvWorkspace dkv_workspace(const kvsp_layout& l) {
 
 int decode_group_pad(const kvsp_layout& l) {
   const int G = l.num_q_heads / l.num_kv_heads;
-  int gp = G <= 1 ? 1 : G <= 2 ? 2 : G <= 4 ? 4 : G <= 8 ? 8 : 16;
+  const int gp0 = G <= 1 ? 1 : G <= 2 ? 2 : G <= 4 ? 4 : G <= 8 ? 8 : 16;
+  int gp = gp0;
   const int64_t pairs = static_cast<int64_t>(l.batch) * l.num_kv_heads;
   while (gp > KVSP_DECODE_MIN_GP && pairs * ((G + gp - 1) / gp) < KVSP_DECODE_SPLIT_GROUPS) gp /= 2;
+  // Once split, halve again while that removes padded head slots (6 heads in
+  // items of 4 pad 2 slots, in items of 2 none): measured 14.5 -> 12.8 us on
+  // the Qwen-like shape, while 16 heads stay in items of 4 (2 was slower).
+  if (gp < gp0) {
+    auto slots = [G](int g) { return (G + g - 1) / g * g; };
+    while (gp > 2 && slots(gp / 2) < slots(gp)) gp /= 2;
+  }
   return gp;
 }
 
