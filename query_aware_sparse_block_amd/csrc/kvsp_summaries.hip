@@ -9,12 +9,15 @@
 // the wave covers 64 / LPR rows per load. Each lane accumulates its slice of
 // the row in double, the row groups are folded with lane shuffles, and the
 // mean is rounded once to float32. HBM-bound: P*D*E bytes read and D*4 bytes
-// written per (block, KV head).
+// written per (block, KV head). A lane adds its rows in a fixed order (the
+// append kernel repeats it, so both give the same bits).
 
 #include "kvsp_device.h"
 #include "kvsp_internal.h"
 
 namespace kvsp {
+
+constexpr int kRowBatch = 8;  // row loads a lane keeps in flight
 
 template <typename T, int D>
 __global__ __launch_bounds__(256) void build_summaries_kernel(SummaryArgs a) {
@@ -37,11 +40,24 @@ __global__ __launch_bounds__(256) void build_summaries_kernel(SummaryArgs a) {
     double acc[EPV];
 #pragma unroll
     for (int e = 0; e < EPV; ++e) acc[e] = 0.0;
-    for (int t = row0; t < a.P; t += RPL) {
-      float v[EPV];
-      T::widen(load16(tile + (static_cast<int64_t>(t) * D + col) * E), v);
+    // Rows t = row0, row0 + RPL, ... in that order; eight rows' loads are
+    // requested before any of them is added, so they are in flight together.
+    for (int t0 = row0; t0 < a.P; t0 += kRowBatch * RPL) {
+      uint4 raw[kRowBatch];
 #pragma unroll
-      for (int e = 0; e < EPV; ++e) acc[e] += static_cast<double>(v[e]);
+      for (int u = 0; u < kRowBatch; ++u) {
+        const int t = t0 + u * RPL;
+        raw[u] = t < a.P ? load16_stream(tile + (static_cast<int64_t>(t) * D + col) * E) : make_uint4(0, 0, 0, 0);
+      }
+#pragma unroll
+      for (int u = 0; u < kRowBatch; ++u) {
+        if (t0 + u * RPL < a.P) {
+          float v[EPV];
+          T::widen(raw[u], v);
+#pragma unroll
+          for (int e = 0; e < EPV; ++e) acc[e] += static_cast<double>(v[e]);
+        }
+      }
     }
 #pragma unroll
     for (int e = 0; e < EPV; ++e) acc[e] = fold_sum<LPR>(acc[e]);
