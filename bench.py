@@ -78,6 +78,14 @@ def attention_bytes(case, tokens):
     return kv + q + out + table, kv
 
 
+def summary_bytes(case):
+    """Algorithmic bytes of one summary build: the keys of every full block
+    (P*D*E per KV head) read, one float32 row per (block, KV head) written."""
+    E = {"fp32": 4, "fp16": 2, "bf16": 2}[case.dtype]
+    full = sum(int(L) // case.P for L in case.ctx_lens)
+    return full * case.Hkv * (case.P * case.D * E + case.D * 4)
+
+
 def scoring_bytes(case, plans_C):
     return sum(plans_C) * case.Hkv * case.D * 4 + case.B * case.Hq * case.D * 2
 
@@ -298,9 +306,17 @@ def main():
                                    dc0.block_table.clone(), dc0.ctx_lens.clone(), dc0.layout,
                                    dc0.params))
     bufs = [dev.alloc_buffers(d) for d in reps]
+    # Summaries of every replica (step 1, before timing: they are resident
+    # between steps); each build is timed on its own.
+    build_ev = []
     for d, bf in zip(reps, bufs):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
         dev.build_summaries(d, bf)
+        e1.record()
+        build_ev.append((e0, e1))
     torch.cuda.synchronize()
+    build_us = sorted(a.elapsed_time(b) * 1e3 for a, b in build_ev)[len(build_ev) // 2]
     print(f"[bench] {R} replica(s) of {pool_bytes / 2**30:.2f} GiB resident", file=sys.stderr,
           flush=True)
 
@@ -459,6 +475,9 @@ def main():
         },
         "scoring": {"bytes_per_launch": scoring_bytes(case, Cs),
                     "gbps": scoring_bytes(case, Cs) / (sel_s / args.steps) / 1e9},
+        "summaries": {"us": build_us, "bytes_per_launch": summary_bytes(case),
+                      "gbps": summary_bytes(case) / (build_us * 1e-6) / 1e9,
+                      "note": "kvsp_build_summaries over every full block, median over replicas"},
         "dkv": dkv,
         "cpu_baseline": cpu,
     }
