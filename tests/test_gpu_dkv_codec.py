@@ -211,6 +211,7 @@ def test_compress_gapped_blocks_match_the_svd(dtype, D, P, Hkv, R):
     ("bf16", 128, 256, "iid", 0),
     ("fp32", 128, 128, "iid", 64),
     ("bf16", 128, 256, "lowrank", 40),  # more residual tokens than planted spikes
+    ("bf16", 64, 64, "iid", 64),        # every token residual: the decode is exact attention
 ])
 def test_compress_properties_without_a_gap(dtype, D, P, values, R):
     case = codec_case(dtype, D, P, 4, 2, [6 * P + 3, 2 * P + P // 2], W=P // 2,
