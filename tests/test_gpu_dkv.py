@@ -83,7 +83,7 @@ def run_decode_parity(case, n_resid, k_max, seed=0, empty=()):
 
 
 def small_case(dtype, D, P, Hq, Hkv, ctx, W, seed, num_phys=None):
-    max_blocks = -(-max(ctx) // P)
+    max_blocks = max(1, -(-max(ctx) // P))  # a table has at least one column
     return wl.make_case(f"dkv-{dtype}-D{D}-P{P}", seed=seed, B=len(ctx), Hq=Hq, Hkv=Hkv, D=D,
                         P=P, dtype=dtype, ctx_lens=ctx, shuffle=True,
                         num_phys=num_phys or len(ctx) * max_blocks, max_blocks=max_blocks,
@@ -140,3 +140,27 @@ def test_decode_window_in_256_token_blocks_with_fp32():
     # fp32 caches at the tighter bar; window groups from several 256-token blocks
     case = small_case("fp32", 64, 256, 8, 2, [7 * 256 + 200, 2 * 256 + 1], W=700, seed=736)
     run_decode_parity(case, 16, k_max=4, seed=8)
+
+
+def _random_dkv_case(i):
+    rng = np.random.default_rng(95_000 + i)
+    dtype = ["fp32", "fp16", "bf16"][rng.integers(3)]
+    D = int(rng.choice([64, 128]))
+    P = int(rng.choice([64, 128, 256]))
+    Hkv = int(rng.integers(1, 5))
+    G = int(rng.choice([1, 2, 3, 4, 6, 8, 12, 16]))
+    B = int(rng.integers(1, 5))
+    max_blocks = int(rng.integers(1, 17))
+    ctx = [0 if rng.random() < 0.1 else int(rng.integers(1, max_blocks * P + 1)) for _ in range(B)]
+    W = int(rng.choice([0, int(rng.integers(1, 3 * P + 1))]))
+    R = int(rng.integers(0, min(64, P) + 1))
+    case = small_case(dtype, D, P, Hkv * G, Hkv, ctx, W, seed=96_000 + i)
+    return case, R, int(rng.integers(1, max_blocks + 1))
+
+
+@pytest.mark.parametrize("i", range(30))
+def test_decode_random_configurations(i):
+    # seeded random shapes: dtype, head dim, block size, group size, residual
+    # budget, window, selection size and ragged (some empty) contexts
+    case, R, k_max = _random_dkv_case(i)
+    run_decode_parity(case, R, k_max=k_max, seed=i)
