@@ -310,3 +310,22 @@ def test_dkv_workload_full_size():
     assert np.abs(lse - ref_lse).max() <= H.LSE_TOL
     ref2, _ = DKV.decode(q, kp, vp, ref_recs, case.block_table, case.ctx_lens, sel, nsel, **args)
     assert np.abs(ref - ref2).max() <= CODEC_OUT_TOL
+
+
+@pytest.mark.parametrize("i", range(12))
+def test_compress_random_configurations(i):
+    # seeded random shapes through the property checks and the decode:
+    # dtype, head dim, block size, KV heads, residual budget, values, ragged
+    # contexts and windows
+    rng = np.random.default_rng(97_000 + i)
+    dtype = ["fp32", "fp16", "bf16"][rng.integers(3)]
+    D = int(rng.choice([64, 128]))
+    P = int(rng.choice([64, 128, 256]))
+    Hkv = int(rng.integers(1, 4))
+    R = int(rng.integers(0, min(64, P) + 1))
+    values = "lowrank" if rng.random() < 0.5 else "iid"
+    ctx = [int(rng.integers(P, 5 * P + 1)) for _ in range(int(rng.integers(1, 4)))]
+    W = int(rng.integers(0, 2 * P))
+    case = codec_case(dtype, D, P, 2 * Hkv, Hkv, ctx, W, seed=98_000 + i, values=values,
+                      n_spikes=max(R, 1))
+    run_codec_parity(case, R, gapped=False)
