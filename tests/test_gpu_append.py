@@ -31,7 +31,8 @@ def _ulp_close(got, ref):
 
 
 @pytest.mark.parametrize("dtype,Hq,Hkv,D,P", [("bf16", 8, 2, 128, 16), ("fp16", 4, 4, 64, 16),
-                                              ("fp32", 6, 3, 64, 32)])
+                                              ("fp32", 6, 3, 64, 32), ("bf16", 16, 1, 128, 64),
+                                              ("fp16", 12, 2, 128, 32), ("fp32", 8, 8, 128, 16)])
 def test_decode_loop_appends_match_oracle(dtype, Hq, Hkv, D, P):
     B, steps = 3, 2 * P + 3
     start = np.array([P - 2, 3 * P, 5], np.int32)
