@@ -90,6 +90,17 @@ def scoring_bytes(case, plans_C):
     return sum(plans_C) * case.Hkv * case.D * 4 + case.B * case.Hq * case.D * 2
 
 
+def cpu_model() -> str:
+    """The host CPU's model name (Linux /proc/cpuinfo), or "unknown"."""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def time_cpu_oracle(case, budget_s=10.0, threads=1):
     """The oracle, as it stands, timed on this host: one whole decode step
     (scores, Top-k, spans, attention for every (sequence, head); summaries
@@ -407,6 +418,7 @@ def main():
         big = sum(tokens) * case.Hq * case.D > 2e9
         cpu = time_cpu_oracle_sampled(case) if big else time_cpu_oracle(case)
         cpu["cores_available"] = os.cpu_count()
+        cpu["cpu_model"] = cpu_model()
         # the same oracle with its (sequence, head) loop on the host's thread share
         threads = max(1, int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1)))
         if threads > 1:
@@ -443,6 +455,9 @@ def main():
         },
         "selected_kv_gbps": achieved,
         "selected_kv_hbm_frac": achieved / HBM_PEAK_GBPS,
+        "step_gbps": (attn_bytes + scoring_bytes(case, Cs)) / (ms_per_step * 1e-3) / 1e9,
+        "step_gbps_note": "attention bytes (selected K/V, q, table, out) + scoring bytes "
+                          "(summaries, q) per step, over the step time",
         "kernels_us": {"score_topk": sel_s / args.steps * 1e6,
                        "sparse_decode": attn_avg * 1e6,
                        "step": ms_per_step * 1e3,
