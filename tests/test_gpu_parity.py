@@ -275,3 +275,49 @@ def test_largest_block_table():
                         ctx_lens=[16384 * 16], top_k=40, keep_floor=1, recent_window=100)
     assert case.max_blocks == 16384
     H.full_parity(case)
+
+
+def test_optional_outputs_may_be_null():
+    # scores NULL (the selection keeps them in its workspace) and lse NULL on
+    # every decode entry point: selection and outputs are bit-identical to
+    # the run that returns them
+    from query_aware_sparse_block_amd import device as dev
+    from query_aware_sparse_block_amd import kvsp
+    case = wl.c5(keep="1/32", B=4, L=2048)
+    H.note("[optional] scores and lse NULL")
+    gpu, dc, buf = H.run_gpu(case)
+    sel2 = torch.full_like(buf.selected, -1)
+    nsel2, nsp2, dense2 = (torch.zeros_like(buf.num_selected) for _ in range(3))
+    spans2 = torch.full_like(buf.spans, -1)
+    kvsp.kvsp_score_topk(dc.layout, dc.params, dc.q, buf.summaries, dc.block_table, dc.ctx_lens,
+                         None, sel2, nsel2, spans2, nsp2, dense2, buf.workspace)
+    out2 = torch.zeros_like(buf.out)
+    kvsp.kvsp_sparse_decode(dc.layout, dc.params, dc.q, dc.k_pool, dc.v_pool, dc.block_table,
+                            dc.ctx_lens, sel2, nsel2, dense2, 0.0, out2, None, buf.workspace)
+    torch.cuda.synchronize()
+    assert torch.equal(sel2, buf.selected) and torch.equal(nsel2, buf.num_selected)
+    assert torch.equal(spans2, buf.spans) and torch.equal(nsp2, buf.num_spans)
+    assert torch.equal(out2, buf.out)
+    dev.dense_decode(dc, buf)
+    out3 = torch.zeros_like(buf.out)
+    kvsp.kvsp_dense_decode(dc.layout, dc.q, dc.k_pool, dc.v_pool, dc.block_table, dc.ctx_lens, 0.0,
+                           out3, None, buf.workspace)
+    torch.cuda.synchronize()
+    assert torch.equal(out3, buf.out)
+    # DKV decode with lse NULL against the call that returns it
+    case = wl.c4_dkv(L=4096, n_resid=8)
+    dc = dev.upload(case)
+    buf = dev.alloc_buffers(dc)
+    dev.build_summaries(dc, buf)
+    dkv = kvsp.DkvParams(n_resid=8)
+    recs = dev.alloc_dkv_records(dc, dkv)
+    ws = kvsp.alloc_dkv_workspace(dc.layout, dkv)
+    dev.dkv_compress(dc, dkv, recs)
+    dev.score_topk(dc, buf)
+    dev.dkv_decode(dc, buf, dkv, recs, ws)
+    out4 = torch.zeros_like(buf.out)
+    kvsp.kvsp_dkv_decode(dc.layout, dc.params, dkv, dc.q, dc.k_pool, dc.v_pool, recs,
+                         dc.block_table, dc.ctx_lens, buf.selected, buf.num_selected, 0.0, out4,
+                         None, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(out4, buf.out)
