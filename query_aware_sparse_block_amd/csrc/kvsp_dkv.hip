@@ -52,6 +52,8 @@ __device__ __forceinline__ floatx4 mfma4(float a, float b, floatx4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
+constexpr int kMergeBatch = 32;  // chunk partials requested together in the merge
+
 template <typename T, int D, int TPW>
 __global__ __launch_bounds__(256) void dkv_attend_kernel(DkvDecodeArgs a) {
   constexpr int E = T::kBytes;
@@ -121,18 +123,22 @@ __global__ __launch_bounds__(256) void dkv_attend_kernel(DkvDecodeArgs a) {
       j1 = min(wg, j0 + wper);
     }
 
-    // Query operands (fixed for the item). Heads past G are zero columns.
+    // Query operands (fixed for the item). Heads past G are zero columns: their
+    // lanes read head 0 and zero it afterwards, so that no load sits behind a
+    // per-lane branch (the compiler then waits for each such load alone).
     const bool head_ok = hl < G;
-    const int64_t qrow = static_cast<int64_t>(b) * a.Hq + g * G + hl;
+    const int64_t qrow = static_cast<int64_t>(b) * a.Hq + g * G + (head_ok ? hl : 0);
     float qreg[QS];
 #pragma unroll
-    for (int s = 0; s < QS; ++s)
-      qreg[s] = head_ok ? T::load1(a.q, qrow * D + wave * DQ + gi * QS + s) : 0.f;
+    for (int s = 0; s < QS; ++s) qreg[s] = T::load1(a.q, qrow * D + wave * DQ + gi * QS + s);
     uint4 qop[KLD];
 #pragma unroll
     for (int s = 0; s < KLD; ++s)
-      qop[s] = head_ok ? load16(static_cast<const char*>(a.q) + (qrow * D + k_elem_offset<T>(lane, s)) * E)
-                       : make_uint4(0, 0, 0, 0);
+      qop[s] = load16(static_cast<const char*>(a.q) + (qrow * D + k_elem_offset<T>(lane, s)) * E);
+#pragma unroll
+    for (int s = 0; s < QS; ++s) qreg[s] = head_ok ? qreg[s] : 0.f;
+#pragma unroll
+    for (int s = 0; s < KLD; ++s) qop[s] = head_ok ? qop[s] : make_uint4(0, 0, 0, 0);
 
     // Running softmax state of heads 4*gi + v, channels dbase + 16*dt + hl.
     float m_run[4], l_run[4];
@@ -170,24 +176,23 @@ __global__ __launch_bounds__(256) void dkv_attend_kernel(DkvDecodeArgs a) {
       }
 
       // ---- A: loads, W_K q partial, anchor term, exact-row logits ---------------
+      // Every load of the block is issued before any of them is used, and
+      // none sits behind a per-lane branch (rows past R are clamped to row
+      // R - 1 and masked afterwards): the block's lines then arrive in one
+      // round trip instead of one round trip per load.
       float wv[NDT][8];
       float va[NDT];
+      float wk[2][QS];
+      float ka[QS];
+      uint4 cvec[2 * TPW];
+      int rid = -1;
       if (!win) {
         const float* basis = reinterpret_cast<const float*>(rec + a.off_basis);
-        if (wave == 0 && lane < R) {
-          const int r = reinterpret_cast<const int32_t*>(rec + a.off_ridx)[lane];
-          if (r >= 0 && r < a.P) atomicOr(&res_mask[r >> 5], 1u << (r & 31));
-        }
-        {
-          const char* src = rec + a.off_coef + static_cast<int64_t>(wave) * TOKW * kRank * 4;
+        if (R > 0) rid = reinterpret_cast<const int32_t*>(rec + a.off_ridx)[min(lane, R - 1)];
+        const char* src = rec + a.off_coef + static_cast<int64_t>(wave) * TOKW * kRank * 4;
 #pragma unroll
-          for (int u = 0; u < 2 * TPW; ++u) {
-            const int vi = lane + kWave * u;  // 16-byte vector of the wave's rows
-            const uint4 v = load16(src + static_cast<int64_t>(vi) * 16);
-            *reinterpret_cast<uint4*>(&c_lds[wave][(vi / 8) * kCRow + (vi % 8) * 4]) = v;
-          }
-        }
-        float wk[2][QS];
+        for (int u = 0; u < 2 * TPW; ++u)  // 16-byte vectors of the wave's coefficient rows
+          cvec[u] = load16(src + static_cast<int64_t>(lane + kWave * u) * 16);
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
@@ -199,9 +204,36 @@ __global__ __launch_bounds__(256) void dkv_attend_kernel(DkvDecodeArgs a) {
           for (int s = 0; s < 8; ++s) wv[dt][s] = basis[(gi * 8 + s) * 2 * D + D + dbase + 16 * dt + hl];
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt) va[dt] = T::load1(rec, D + dbase + 16 * dt + hl);
+#pragma unroll
+        for (int s = 0; s < QS; ++s) ka[s] = T::load1(rec, wave * DQ + gi * QS + s);
+      }
+      float vr[RS][NDT] = {};
+      const int rlast = R > 0 ? R - 1 : 0;
+#pragma unroll
+      for (int s = 0; s < RS; ++s) {
+        if (4 * s >= R) break;  // uniform
+        const int row = min(4 * s + gi, rlast);
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt)
+          vr[s][dt] = T::load1(rv_base, static_cast<int64_t>(row) * D + dbase + 16 * dt + hl);
+      }
+      const bool krows = 16 * wave < R;  // uniform over the wave
+      uint4 kv[KLD];
+      if (krows) {
+        const char* kr = rk_base + static_cast<int64_t>(min(16 * wave + hl, R - 1)) * D * E;
+#pragma unroll
+        for (int s = 0; s < KLD; ++s) kv[s] = load16(kr + k_elem_offset<T>(lane, s) * E);
+      }
+      if (!win) {
+        if (wave == 0 && lane < R && rid >= 0 && rid < a.P) atomicOr(&res_mask[rid >> 5], 1u << (rid & 31));
+#pragma unroll
+        for (int u = 0; u < 2 * TPW; ++u) {
+          const int vi = lane + kWave * u;
+          *reinterpret_cast<uint4*>(&c_lds[wave][(vi / 8) * kCRow + (vi % 8) * 4]) = cvec[u];
+        }
         float qa = 0.f;
 #pragma unroll
-        for (int s = 0; s < QS; ++s) qa += qreg[s] * T::load1(rec, wave * DQ + gi * QS + s);
+        for (int s = 0; s < QS; ++s) qa += qreg[s] * ka[s];
         floatx4 qt[2] = {floatx4{0.f, 0.f, 0.f, 0.f}, floatx4{0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt)
@@ -220,21 +252,11 @@ __global__ __launch_bounds__(256) void dkv_attend_kernel(DkvDecodeArgs a) {
           for (int s = 0; s < 8; ++s) wv[dt][s] = 0.f;
         }
       }
-      float vr[RS][NDT];
-#pragma unroll
-      for (int s = 0; s < RS; ++s) {
-        const int row = 4 * s + gi;
-#pragma unroll
-        for (int dt = 0; dt < NDT; ++dt)
-          vr[s][dt] = row < R ? T::load1(rv_base, static_cast<int64_t>(row) * D + dbase + 16 * dt + hl) : 0.f;
-      }
       float rmax = NEG_INF;
-      if (16 * wave < R) {
-        const int r = min(16 * wave + hl, R - 1);
-        const char* kr = rk_base + static_cast<int64_t>(r) * D * E;
+      if (krows) {
         floatx4 sc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int s = 0; s < KLD; ++s) sc = QkMfma<T>::step(load16(kr + k_elem_offset<T>(lane, s) * E), qop[s], sc);
+        for (int s = 0; s < KLD; ++s) sc = QkMfma<T>::step(kv[s], qop[s], sc);
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
           const int row = 16 * wave + 4 * gi + v;
@@ -426,14 +448,24 @@ __global__ __launch_bounds__(256) void dkv_attend_kernel(DkvDecodeArgs a) {
       const int d = (o - h * (D / 4)) * 4;
       const int64_t hq = static_cast<int64_t>(b) * a.Hq + g * G + h;
       float4 num = make_float4(0.f, 0.f, 0.f, 0.f);
-#pragma unroll 8
-      for (int cc = 0; cc < n_act; ++cc) {
-        const float w = merge_w[h][cc];
-        const float4 p = load_coherent4(prs, static_cast<uint32_t>(((cc * 16 + h) * D + d) * sizeof(float)));
-        num.x += w * p.x;
-        num.y += w * p.y;
-        num.z += w * p.z;
-        num.w += w * p.w;
+      // All of a batch's loads are in flight together (one round trip per
+      // batch). Chunk indices past n_act are clamped to the last chunk;
+      // their weights merge_w[h][cc] are 0 (n_act <= S <= kWave).
+      for (int c0 = 0; c0 < n_act; c0 += kMergeBatch) {
+        float4 p[kMergeBatch];
+#pragma unroll
+        for (int u = 0; u < kMergeBatch; ++u) {
+          const int cc = min(c0 + u, n_act - 1);
+          p[u] = load_coherent4(prs, static_cast<uint32_t>(((cc * 16 + h) * D + d) * sizeof(float)));
+        }
+#pragma unroll
+        for (int u = 0; u < kMergeBatch; ++u) {
+          const float w = merge_w[h][min(c0 + u, kWave - 1)];
+          num.x += w * p[u].x;
+          num.y += w * p[u].y;
+          num.z += w * p[u].z;
+          num.w += w * p[u].w;
+        }
       }
       const float Ls = merge_h[h][0];
       float4 o4 = make_float4(0.f, 0.f, 0.f, 0.f);
