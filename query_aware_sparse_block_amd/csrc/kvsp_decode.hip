@@ -85,11 +85,21 @@ struct SeqWork {
 // `quantum` tokens (one sub-tile per wavefront), at most max_chunks of them.
 __device__ __forceinline__ SeqWork seq_work(const DecodeArgs& a, int b, int quantum) {
   SeqWork w;
+  // The three loads do not depend on each other and are issued together (one
+  // round trip). None sits behind a branch, where it would be waited for
+  // alone: an absent array is replaced by context_lens for the load and its
+  // value masked afterwards.
+  const bool has_flag = a.use_dense != nullptr;
+  const bool has_nsel = a.num_selected != nullptr;
   w.L = a.context_lens[b];
+  const int flag_v = (has_flag ? a.use_dense : a.context_lens)[b];
+  const int nsel_v = (has_nsel ? a.num_selected : a.context_lens)[b];
+  const int flag = has_flag ? flag_v : 0;
+  const int nsel = has_nsel ? nsel_v : 0;
   const int n = (w.L + a.P - 1) / a.P;
   w.Cw = window_start_block(w.L, a.P, a.recent_window);
-  w.dense = a.all_dense || (a.use_dense != nullptr && a.use_dense[b] != 0);
-  w.k = (w.dense || a.num_selected == nullptr) ? 0 : a.num_selected[b];
+  w.dense = a.all_dense || flag != 0;
+  w.k = w.dense ? 0 : nsel;
   w.A = w.dense ? n : w.k + (n - w.Cw);
   w.T = w.dense ? w.L : w.k * a.P + (w.L - w.Cw * a.P);
   if (w.T > 0) {
