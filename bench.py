@@ -271,6 +271,60 @@ def bench_dkv(args, capture, timed):
     }
 
 
+def bench_budget(case, dc):
+    """The budget controller (SparPR, "Dynamic budget control") on this machine:
+    the pinned host-to-device copy bandwidth and the throughput of one block's
+    K and V projection GEMM ([P x hidden] x [hidden x 2 Hkv D], hidden = Hq D),
+    both measured here, priced by kvsp_budget_keep_ratio for the workload."""
+    import torch
+
+    from query_aware_sparse_block_amd import kvsp
+
+    hidden = case.Hq * case.D
+    n = 256 << 20
+    host = torch.empty(n, dtype=torch.uint8, pin_memory=True)
+    devbuf = torch.empty(n, dtype=torch.uint8, device="cuda")
+    devbuf.copy_(host, non_blocking=True)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    reps = 5
+    e0.record()
+    for _ in range(reps):
+        devbuf.copy_(host, non_blocking=True)
+    e1.record()
+    torch.cuda.synchronize()
+    h2d = reps * n / (e0.elapsed_time(e1) * 1e-3)
+    del host, devbuf
+
+    tdt = {"fp32": torch.float32, "fp16": torch.float16, "bf16": torch.bfloat16}[case.dtype]
+    x = torch.randn(case.P, hidden, device="cuda").to(tdt)
+    w = torch.randn(hidden, 2 * case.Hkv * case.D, device="cuda").to(tdt).contiguous()
+    for _ in range(10):
+        torch.matmul(x, w)
+    torch.cuda.synchronize()
+    reps = 200
+    e0.record()
+    for _ in range(reps):
+        torch.matmul(x, w)
+    e1.record()
+    torch.cuda.synchronize()
+    gemm_s = e0.elapsed_time(e1) * 1e-3 / reps
+    flops = 2.0 * case.P * hidden * 2 * case.Hkv * case.D / gemm_s
+    del x, w
+
+    den = 1024
+    num, copy_s, rec_s = kvsp.kvsp_budget_keep_ratio(dc.layout, kvsp.BudgetModel(h2d, flops, hidden),
+                                                     den)
+    Cs = [max(0, int(L) - case.recent_window) // case.P for L in case.ctx_lens]
+    ks = [min(C, max(case.keep_floor, -(-C * num // den))) for C in Cs]
+    return {"h2d_gbps": h2d / 1e9, "proj_tflops": flops / 1e12, "hidden": hidden,
+            "copy_us_per_block": copy_s * 1e6, "recompute_us_per_block": rec_s * 1e6,
+            "keep": f"{num}/{den}", "keep_ratio": num / den, "kept_blocks_per_seq": sorted(set(ks)),
+            "note": "kvsp_budget_keep_ratio with the measured copy bandwidth (256 MiB pinned "
+                    "copies) and projection throughput (torch.matmul of one block's K|V "
+                    "projection); reported only, the timed step keeps the workload's keep ratio"}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -285,6 +339,8 @@ def main():
                     help="also time the decode over a host-resident (pinned, mapped) pool")
     ap.add_argument("--no-dkv", action="store_true",
                     help="skip the DKV codec and decode on the 256-token-block workload")
+    ap.add_argument("--no-budget", action="store_true",
+                    help="skip measuring the budget controller's copy and recompute prices")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the library has "
@@ -427,6 +483,7 @@ def main():
             cpu["openmp"] = {k: mt[k] for k in ("value", "unit", "cores", "sample")}
 
     dkv = None if args.no_dkv else bench_dkv(args, capture, timed)
+    budget = None if args.no_budget else bench_budget(case, reps[0])
 
     E = {"fp32": 4, "fp16": 2, "bf16": 2}[case.dtype]
     rec = {
@@ -494,6 +551,7 @@ def main():
                       "gbps": summary_bytes(case) / (build_us * 1e-6) / 1e9,
                       "note": "kvsp_build_summaries over every full block, median over replicas"},
         "dkv": dkv,
+        "budget": budget,
         "cpu_baseline": cpu,
     }
     print(json.dumps(rec), flush=True)

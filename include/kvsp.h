@@ -130,6 +130,41 @@ typedef struct {
  * one workspace must not overlap in time. */
 size_t kvsp_workspace_bytes(const kvsp_layout* layout, const kvsp_select_params* params);
 
+/* Dynamic budget control (SparPR, "Dynamic budget control"): the keep ratio
+ * of the selection from the two prices of one block (one KV head group of
+ * block_size tokens across all num_kv_heads heads):
+ *   copy_s      = 2 * block_size * num_kv_heads * head_dim * E / h2d_bytes_per_s
+ *                 (its data volume over host-to-device bandwidth, x2 for K and V;
+ *                 E = element size of layout->dtype);
+ *   recompute_s = 4 * block_size * hidden * num_kv_heads * head_dim / proj_flops_per_s
+ *                 (rebuilding K and V from the block's hidden states through the
+ *                 two attention projections only: two products of a
+ *                 block_size x hidden matrix by a hidden x (num_kv_heads *
+ *                 head_dim) one, 2 flops per multiply-add; with multi-head
+ *                 attention num_kv_heads * head_dim = hidden, so the price
+ *                 scales with block length times hidden squared).
+ * The page leaves open how the ratio of the two prices becomes a keep ratio.
+ * Reading taken: ratio = min(1, recompute_s / copy_s) — every candidate block
+ * is kept while fetching it costs no more than rebuilding it, and the share
+ * falls in proportion as the fetch grows dearer. It is returned as
+ *   *keep_num = min(keep_den, ceil(ratio * keep_den))   (>= 1, never rounded down)
+ * for kvsp_select_params.keep_num with keep_den as given; the selection's
+ * keep_floor then bounds k from below (the page's Minimum Keep Floor).
+ * copy_s and recompute_s may be NULL. Host arithmetic only (no device access,
+ * no stream). Errors: a layout the other entry points reject gives the same
+ * status; KVSP_ERR_INVALID_ARG for NULL model or keep_num, a non-finite or
+ * non-positive bandwidth or throughput, hidden <= 0, or keep_den <= 0. Nothing
+ * is written on error. */
+typedef struct {
+  double h2d_bytes_per_s;  /* measured host-to-device copy bandwidth, bytes/s */
+  double proj_flops_per_s; /* measured throughput of the K/V projection GEMM, flop/s */
+  int32_t hidden;          /* model hidden size: the projections' input width */
+} kvsp_budget_model;
+
+kvsp_status kvsp_budget_keep_ratio(const kvsp_layout* layout, const kvsp_budget_model* model,
+                                   int32_t keep_den, double* copy_s, double* recompute_s,
+                                   int32_t* keep_num);
+
 /* Step 1 (SparPR, "Query-Aware key-block selection"): for every sequence b
  * and every full logical block j < floor(context_lens[b] / P), write
  *   summaries[block_table[b][j]][g][d] = (1/P) * sum_t K[block_table[b][j]][g][t][d]

@@ -4,6 +4,7 @@
 
 #include <stddef.h>
 #include <algorithm>
+#include <cmath>
 #include <stdint.h>
 
 #include "kvsp.h"
@@ -311,6 +312,35 @@ size_t kvsp_workspace_bytes(const kvsp_layout* layout, const kvsp_select_params*
   (void)params;
   if (check_layout(layout) != KVSP_OK) return 0;
   return workspace_layout(*layout).total;
+}
+
+// SparPR, "Dynamic budget control": the copy price of a block (its bytes over
+// the host-to-device bandwidth, twice for K and V) against its recompute price
+// (the K and V projections of its hidden states), the ratio read as the keep
+// ratio (capped at 1) in units of 1/keep_den, rounded up.
+kvsp_status kvsp_budget_keep_ratio(const kvsp_layout* layout, const kvsp_budget_model* model,
+                                   int32_t keep_den, double* copy_s, double* recompute_s,
+                                   int32_t* keep_num) {
+  const kvsp_status st = check_layout(layout);
+  if (st != KVSP_OK) return st;
+  if (model == nullptr || keep_num == nullptr || keep_den <= 0) return KVSP_ERR_INVALID_ARG;
+  const double bandwidth = model->h2d_bytes_per_s;
+  const double throughput = model->proj_flops_per_s;
+  if (!std::isfinite(bandwidth) || !(bandwidth > 0.0) || !std::isfinite(throughput) ||
+      !(throughput > 0.0) || model->hidden <= 0)
+    return KVSP_ERR_INVALID_ARG;
+  const double tokens = layout->block_size;
+  const double kv_width = static_cast<double>(layout->num_kv_heads) * layout->head_dim;
+  const double copy = 2.0 * tokens * kv_width * elem_bytes(layout->dtype) / bandwidth;
+  const double recompute = 4.0 * tokens * static_cast<double>(model->hidden) * kv_width / throughput;
+  const double ratio = std::min(1.0, recompute / copy);
+  const double units = std::ceil(ratio * keep_den);
+  int32_t num = keep_den;
+  if (units < static_cast<double>(keep_den)) num = units < 1.0 ? 1 : static_cast<int32_t>(units);
+  if (copy_s != nullptr) *copy_s = copy;
+  if (recompute_s != nullptr) *recompute_s = recompute;
+  *keep_num = num;
+  return KVSP_OK;
 }
 
 kvsp_status kvsp_append_kv(const kvsp_layout* layout, const void* k_new, const void* v_new,

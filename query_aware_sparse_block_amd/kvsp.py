@@ -46,6 +46,11 @@ class kvsp_dkv_params(ctypes.Structure):
                 ("power_iters", ctypes.c_int32)]
 
 
+class kvsp_budget_model(ctypes.Structure):
+    _fields_ = [("h2d_bytes_per_s", ctypes.c_double), ("proj_flops_per_s", ctypes.c_double),
+                ("hidden", ctypes.c_int32)]
+
+
 class KvspError(RuntimeError):
     def __init__(self, fn: str, status: int):
         super().__init__(f"{fn} returned {STATUS_NAMES.get(status, status)} "
@@ -92,6 +97,11 @@ def library() -> ctypes.CDLL:
         L.kvsp_dkv_decode.restype = ctypes.c_int
         L.kvsp_dkv_decode.argtypes = [LP, SP, DP, P, P, P, P, P, P, P, P, ctypes.c_float, P, P,
                                       P, sz, P]
+        BP = ctypes.POINTER(kvsp_budget_model)
+        L.kvsp_budget_keep_ratio.restype = ctypes.c_int
+        L.kvsp_budget_keep_ratio.argtypes = [LP, BP, i32, ctypes.POINTER(ctypes.c_double),
+                                             ctypes.POINTER(ctypes.c_double),
+                                             ctypes.POINTER(ctypes.c_int32)]
         _lib = L
     return _lib
 
@@ -260,6 +270,29 @@ def kvsp_dense_decode(layout, q, k_pool, v_pool, block_table, context_lens, scal
         _ptr(context_lens, "context_lens", z.per_seq, I32), ctypes.c_float(scale),
         _ptr(out, "out", z.out, F32), _ptr(lse, "lse", z.lse, F32), _ptr(workspace, "workspace"),
         workspace.numel(), _stream(stream)))
+
+
+@dataclass
+class BudgetModel:
+    h2d_bytes_per_s: float
+    proj_flops_per_s: float
+    hidden: int
+
+    def c(self) -> kvsp_budget_model:
+        return kvsp_budget_model(float(self.h2d_bytes_per_s), float(self.proj_flops_per_s),
+                                 int(self.hidden))
+
+
+def kvsp_budget_keep_ratio(layout: kvsp_layout, model: BudgetModel, keep_den: int):
+    """(keep_num, copy_s, recompute_s) of the budget controller; keep_num / keep_den
+    is the keep ratio for SelectParams."""
+    m = model.c()
+    num = ctypes.c_int32(-1)
+    copy_s, rec_s = ctypes.c_double(0.0), ctypes.c_double(0.0)
+    _check("kvsp_budget_keep_ratio", library().kvsp_budget_keep_ratio(
+        ctypes.byref(layout), ctypes.byref(m), int(keep_den), ctypes.byref(copy_s),
+        ctypes.byref(rec_s), ctypes.byref(num)))
+    return int(num.value), float(copy_s.value), float(rec_s.value)
 
 
 @dataclass

@@ -236,3 +236,39 @@ def test_binding_rejects_host_tensors_and_short_buffers():
     with pytest.raises(ValueError):
         kvsp.kvsp_build_summaries(lay, torch.zeros(4), torch.zeros(4, dtype=torch.int32),
                                   torch.zeros(2, dtype=torch.int32), torch.zeros(4))
+
+
+def test_budget_controller_rejects_bad_arguments_and_writes_nothing():
+    lib = kvsp.library()
+    num = ctypes.c_int32(-7)
+    c, r = ctypes.c_double(-1.0), ctypes.c_double(-1.0)
+    good = kvsp.kvsp_budget_model(25e9, 1e14, 4096)
+
+    def call(layout, model, den, out=True):
+        return lib.kvsp_budget_keep_ratio(
+            ctypes.byref(layout) if layout is not None else None,
+            ctypes.byref(model) if model is not None else None, den, ctypes.byref(c),
+            ctypes.byref(r), ctypes.byref(num) if out else None)
+
+    assert call(_layout(), good, 1024) == 0 and 1 <= num.value <= 1024
+    num.value, c.value, r.value = -7, -1.0, -1.0
+    bad_models = [kvsp.kvsp_budget_model(0.0, 1e14, 4096), kvsp.kvsp_budget_model(-1.0, 1e14, 4096),
+                  kvsp.kvsp_budget_model(float("inf"), 1e14, 4096),
+                  kvsp.kvsp_budget_model(float("nan"), 1e14, 4096),
+                  kvsp.kvsp_budget_model(25e9, 0.0, 4096), kvsp.kvsp_budget_model(25e9, float("nan"), 4096),
+                  kvsp.kvsp_budget_model(25e9, 1e14, 0), kvsp.kvsp_budget_model(25e9, 1e14, -5)]
+    for m in bad_models:
+        assert call(_layout(), m, 1024) == -1
+    assert call(_layout(), None, 1024) == -1
+    assert call(_layout(), good, 0) == -1
+    assert call(_layout(), good, -3) == -1
+    assert call(_layout(), good, 1024, out=False) == -1
+    assert call(None, good, 1024) == -1
+    assert call(_layout(head_dim=96), good, 1024) == -2
+    assert call(_layout(batch=0), good, 1024) == -1
+    assert (num.value, c.value, r.value) == (-7, -1.0, -1.0)
+    # the outputs for the prices may be NULL
+    assert lib.kvsp_budget_keep_ratio(ctypes.byref(_layout()), ctypes.byref(good), 1024, None,
+                                      None, ctypes.byref(num)) == 0
+    with pytest.raises(kvsp.KvspError):
+        kvsp.kvsp_budget_keep_ratio(_layout(), kvsp.BudgetModel(0.0, 1e14, 4096), 1024)

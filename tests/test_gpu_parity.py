@@ -321,3 +321,24 @@ def test_optional_outputs_may_be_null():
                          None, ws)
     torch.cuda.synchronize()
     assert torch.equal(out4, buf.out)
+
+
+@pytest.mark.parametrize("bw,floor", [(2e9, 1), (0.5e9, 12), (1e12, 1)])
+def test_budget_controller_drives_the_selection(bw, floor):
+    # SparPR, "Dynamic budget control": the keep ratio the controller derives
+    # for an OPT-like fp16 block (64 tokens, 16 heads x 128, hidden 2048) from
+    # a slow, a very slow and a fast host link feeds kvsp_score_topk; the step
+    # then meets every parity bar against the oracle run with the same ratio
+    # and keep floor
+    from query_aware_sparse_block_amd import kvsp
+    B, NH, D, P, L = 3, 16, 128, 64, 4096
+    layout = kvsp.kvsp_layout(B, NH, NH, D, P, B * L // P, L // P, 1)
+    num, copy_s, rec_s = kvsp.kvsp_budget_keep_ratio(layout, kvsp.BudgetModel(bw, 100e12, NH * D), 1024)
+    H.note(f"[budget] bw={bw:g} copy={copy_s:.3g}s recompute={rec_s:.3g}s keep={num}/1024 floor={floor}")
+    case = wl.make_case(f"budget-bw{bw:g}", seed=7100 + floor, B=B, Hq=NH, Hkv=NH, D=D, P=P,
+                        dtype="fp16", ctx_lens=[L, L - 100, 1000], values="needle",
+                        keep_num=num, keep_den=1024, keep_floor=floor, recent_window=128)
+    gpu, r_or = H.full_parity(case)
+    for b in range(B):
+        p = oracle.plan(int(case.ctx_lens[b]), P, 128, keep_num=num, keep_den=1024, keep_floor=floor)
+        assert int(gpu["num_selected"][b]) == p["k_eff"]
