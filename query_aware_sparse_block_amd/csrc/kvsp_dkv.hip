@@ -44,12 +44,34 @@ namespace {
 constexpr int kRank = 32;
 constexpr int kMaxResid = 64;
 constexpr int kCRow = 36;  // LDS row stride (floats) of staged coefficient rows
-constexpr int kQRow = 33;  // LDS row stride of per-head rank vectors
+// LDS row stride of per-head rank vectors: 16-byte aligned, and rows 36
+// floats apart put the 16 heads' 16-byte reads on distinct banks.
+constexpr int kQRow = 36;
+constexpr int kQaRow = 20;  // per-head anchor partials (16 used), same reasoning
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.69314718055994531f;
 
 __device__ __forceinline__ floatx4 mfma4(float a, float b, floatx4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+// out[s] = (p[0][hl][j] + p[1][hl][j]) + (p[2][hl][j] + p[3][hl][j]) for
+// j = 8 gi + s: the four waves' partials of head hl, ranks 8 gi .. 8 gi + 7,
+// read as 16-byte vectors.
+__device__ __forceinline__ void sum_wave_partials(const float (&p)[4][16][kQRow], int hl, int gi,
+                                                  float (&out)[8]) {
+  float4 v[4][2];
+#pragma unroll
+  for (int w = 0; w < 4; ++w)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) v[w][h] = *reinterpret_cast<const float4*>(&p[w][hl][8 * gi + 4 * h]);
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    out[4 * h + 0] = (v[0][h].x + v[1][h].x) + (v[2][h].x + v[3][h].x);
+    out[4 * h + 1] = (v[0][h].y + v[1][h].y) + (v[2][h].y + v[3][h].y);
+    out[4 * h + 2] = (v[0][h].z + v[1][h].z) + (v[2][h].z + v[3][h].z);
+    out[4 * h + 3] = (v[0][h].w + v[1][h].w) + (v[2][h].w + v[3][h].w);
+  }
 }
 
 constexpr int kMergeBatch = 32;  // chunk partials requested together in the merge
@@ -65,13 +87,14 @@ __global__ __launch_bounds__(256) void dkv_attend_kernel(DkvDecodeArgs a) {
   constexpr int RS = kMaxResid / 4;  // residual PV steps (4 rows each)
 
   __shared__ __align__(16) float c_lds[4][TOKW * kCRow];
-  __shared__ float qt_part[4][16][kQRow];
-  __shared__ float qa_part[4][4][16];
-  __shared__ float cb_part[4][16][kQRow];
+  // Per-wave partials, read back as 16-byte vectors.
+  __shared__ __align__(16) float qt_part[4][16][kQRow];
+  __shared__ __align__(16) float qa_part[16][kQaRow];  // [head][4 * wave + lane group]
+  __shared__ __align__(16) float cb_part[4][16][kQRow];
   __shared__ float p_res[kMaxResid][16];
-  __shared__ float wmax[4][16];
-  __shared__ float wsum[4][16];
-  __shared__ float rsum[4][16];
+  __shared__ __align__(16) float wmax[16][4];  // [head][wave]
+  __shared__ __align__(16) float wsum[16][4];
+  __shared__ __align__(16) float rsum[16][4];
   __shared__ uint32_t res_mask[8];
   __shared__ int last_flag;
   __shared__ float merge_w[16][kWave];  // split-KV merge: chunk weights per head
@@ -243,7 +266,7 @@ __global__ __launch_bounds__(256) void dkv_attend_kernel(DkvDecodeArgs a) {
         for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
           for (int v = 0; v < 4; ++v) qt_part[wave][4 * gi + v][16 * nt + hl] = qt[nt][v];
-        qa_part[wave][gi][hl] = qa;
+        qa_part[hl][4 * wave + gi] = qa;
       } else {
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt) {
@@ -272,16 +295,16 @@ __global__ __launch_bounds__(256) void dkv_attend_kernel(DkvDecodeArgs a) {
       float lmax = NEG_INF;
       if (!win) {
         float qtb[8];
-#pragma unroll
-        for (int s = 0; s < 8; ++s) {
-          const int j = gi * 8 + s;
-          qtb[s] = (qt_part[0][hl][j] + qt_part[1][hl][j]) + (qt_part[2][hl][j] + qt_part[3][hl][j]);
-        }
+        sum_wave_partials(qt_part, hl, gi, qtb);
         float qa_h = 0.f;
 #pragma unroll
-        for (int w = 0; w < 4; ++w)
-#pragma unroll
-          for (int q = 0; q < 4; ++q) qa_h += qa_part[w][q][hl];
+        for (int w = 0; w < 4; ++w) {
+          const float4 qa4 = *reinterpret_cast<const float4*>(&qa_part[hl][4 * w]);
+          qa_h += qa4.x;
+          qa_h += qa4.y;
+          qa_h += qa4.z;
+          qa_h += qa4.w;
+        }
 #pragma unroll
         for (int mt = 0; mt < TPW; ++mt) {
           const float* crow = &c_lds[wave][(16 * mt + hl) * kCRow + gi * 8];
@@ -306,12 +329,13 @@ __global__ __launch_bounds__(256) void dkv_attend_kernel(DkvDecodeArgs a) {
           for (int v = 0; v < 4; ++v) s2[mt][v] = NEG_INF;
       }
       lmax = fold_max<16>(fmaxf(lmax, rmax));
-      if (gi == 0) wmax[wave][hl] = lmax;
+      if (gi == 0) wmax[hl][wave] = lmax;
       __syncthreads();
 
       // ---- C: probabilities, p^T C, residual probabilities ------------------
       if (wave == 0 && lane < 8) res_mask[lane] = 0;  // every read of it is done
-      const float mb = fmaxf(fmaxf(wmax[0][hl], wmax[1][hl]), fmaxf(wmax[2][hl], wmax[3][hl]));
+      const float4 wm = *reinterpret_cast<const float4*>(wmax[hl]);
+      const float mb = fmaxf(fmaxf(wm.x, wm.y), fmaxf(wm.z, wm.w));
       float ls = 0.f;
 #pragma unroll
       for (int mt = 0; mt < TPW; ++mt)
@@ -336,7 +360,7 @@ __global__ __launch_bounds__(256) void dkv_attend_kernel(DkvDecodeArgs a) {
           for (int v = 0; v < 4; ++v) cb_part[wave][4 * gi + v][16 * nt + hl] = cb[nt][v];
       }
       ls = fold_sum<16>(ls);
-      if (gi == 0) wsum[wave][hl] = ls;
+      if (gi == 0) wsum[hl][wave] = ls;
       float rs = 0.f;
       if (16 * wave < R) {
 #pragma unroll
@@ -348,7 +372,7 @@ __global__ __launch_bounds__(256) void dkv_attend_kernel(DkvDecodeArgs a) {
         }
       }
       rs = fold_sum<16>(rs);
-      if (gi == 0) rsum[wave][hl] = rs;
+      if (gi == 0) rsum[hl][wave] = rs;
       __syncthreads();
 
       // ---- D: output channels of this wave -----------------------------------
@@ -356,9 +380,12 @@ __global__ __launch_bounds__(256) void dkv_attend_kernel(DkvDecodeArgs a) {
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
         const int h = 4 * gi + v;
-        const float mbh = fmaxf(fmaxf(wmax[0][h], wmax[1][h]), fmaxf(wmax[2][h], wmax[3][h]));
-        llr[v] = (wsum[0][h] + wsum[1][h]) + (wsum[2][h] + wsum[3][h]);
-        const float lb = llr[v] + ((rsum[0][h] + rsum[1][h]) + (rsum[2][h] + rsum[3][h]));
+        const float4 wm = *reinterpret_cast<const float4*>(wmax[h]);
+        const float4 ws = *reinterpret_cast<const float4*>(wsum[h]);
+        const float4 rs4 = *reinterpret_cast<const float4*>(rsum[h]);
+        const float mbh = fmaxf(fmaxf(wm.x, wm.y), fmaxf(wm.z, wm.w));
+        llr[v] = (ws.x + ws.y) + (ws.z + ws.w);
+        const float lb = llr[v] + ((rs4.x + rs4.y) + (rs4.z + rs4.w));
         const float mn = fmaxf(m_run[v], mbh);
         alpha[v] = __builtin_amdgcn_exp2f(m_run[v] - mn);
         beta[v] = __builtin_amdgcn_exp2f(mbh - mn);
@@ -366,23 +393,33 @@ __global__ __launch_bounds__(256) void dkv_attend_kernel(DkvDecodeArgs a) {
         m_run[v] = mn;
       }
       float ca[8];
+      if (win) {
 #pragma unroll
-      for (int s = 0; s < 8; ++s) {
-        const int j = gi * 8 + s;
-        ca[s] = win ? 0.f : (cb_part[0][hl][j] + cb_part[1][hl][j]) + (cb_part[2][hl][j] + cb_part[3][hl][j]);
+        for (int s = 0; s < 8; ++s) ca[s] = 0.f;
+      } else {
+        sum_wave_partials(cb_part, hl, gi, ca);
       }
+      // The residual probabilities, all read before the first product (rows
+      // past R in the last step are 0; later steps are skipped).
+      float pr[RS];
+#pragma unroll
+      for (int s = 0; s < RS; ++s) pr[s] = p_res[4 * s + gi][hl];
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt) {
+        // separate accumulators for the low-rank and the residual values, so
+        // the two MFMA chains run side by side
         floatx4 t = {0.f, 0.f, 0.f, 0.f};
+        floatx4 tr = {0.f, 0.f, 0.f, 0.f};
         if (!win) {
 #pragma unroll
           for (int s = 0; s < 8; ++s) t = mfma4(ca[s], wv[dt][s], t);
         }
 #pragma unroll
         for (int s = 0; s < RS; ++s)
-          if (4 * s < R) t = mfma4(p_res[4 * s + gi][hl], vr[s][dt], t);
+          if (4 * s < R) tr = mfma4(pr[s], vr[s][dt], tr);
 #pragma unroll
-        for (int v = 0; v < 4; ++v) acc[dt][v] = acc[dt][v] * alpha[v] + beta[v] * (t[v] + llr[v] * va[dt]);
+        for (int v = 0; v < 4; ++v)
+          acc[dt][v] = acc[dt][v] * alpha[v] + beta[v] * ((t[v] + tr[v]) + llr[v] * va[dt]);
       }
       __syncthreads();  // LDS is reused by the next block
     }
