@@ -54,3 +54,29 @@ def test_dense_decode_from_host_pool():
     a = _run(dc, dense_api=True)
     b = _run(dev.with_host_pool(dc), dense_api=True)
     assert np.array_equal(a["out"], b["out"]) and np.array_equal(a["lse"], b["lse"])
+
+
+def test_dkv_codec_and_decode_from_host_pool():
+    # the DKV variant over a pool in host RAM: the codec reads the older blocks
+    # and the decode the window rows across PCIe; records and outputs must be
+    # bit-identical to those of the device-resident pool
+    from query_aware_sparse_block_amd import kvsp
+    case = wl.c4_dkv(L=8192, n_resid=8)
+    H.note("[host pool] dkv compress + decode, qwen-like 8192")
+    dkv = kvsp.DkvParams(n_resid=8)
+    got = {}
+    for where, dc in (("device", dev.upload(case)), ("host", None)):
+        if dc is None:
+            dc = dev.with_host_pool(dev.upload(case))
+        buf = dev.alloc_buffers(dc)
+        dev.build_summaries(dc, buf)
+        recs = dev.alloc_dkv_records(dc, dkv)
+        ws = kvsp.alloc_dkv_workspace(dc.layout, dkv)
+        dev.dkv_compress(dc, dkv, recs)
+        dev.score_topk(dc, buf)
+        dev.dkv_decode(dc, buf, dkv, recs, ws)
+        torch.cuda.synchronize()
+        got[where] = (recs.cpu().numpy(), buf.selected.cpu().numpy(), buf.out.cpu().numpy(),
+                      buf.lse.cpu().numpy())
+    for a, b, name in zip(got["device"], got["host"], ("records", "selected", "out", "lse")):
+        assert np.array_equal(a, b), name
