@@ -16,7 +16,7 @@ control". One block is priced two ways:
 The ratio of the two prices sets the keep ratio, which the Minimum Keep Floor
 then bounds from below.
 
-Readings where the page is silent (each listed in the design notes):
+Readings where the page is silent:
 - the volume is that of one KV tensor of the block over all KV heads
   (block_size x num_kv_heads x head_dim elements), so the copy price is
   2 x that volume / bandwidth;

@@ -15,7 +15,7 @@ Long-Context Inference", abstract. In short:
   tokens through the low-rank factors and the residual and recent tokens
   exactly, and merges the two halves by log-sum-exp.
 
-Readings taken where the abstract is silent (each listed in the design notes):
+Readings taken where the abstract is silent:
 - the anchor is the block's first token;
 - the SVD is taken of X = [K - k_anchor | V - v_anchor] (P x 2D), without
   further centring or scaling;
