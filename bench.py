@@ -180,6 +180,7 @@ def bench_dkv(args, capture, timed):
 
     from query_aware_sparse_block_amd import device as dev
     from query_aware_sparse_block_amd import kvsp
+    from query_aware_sparse_block_amd import profiling
     from query_aware_sparse_block_amd import workloads as wl
 
     n_resid = 16
@@ -258,6 +259,11 @@ def bench_dkv(args, capture, timed):
         "window_tokens": window, "pool_replicas": R,
         "record_payload_bytes": payload, "exact_block_bytes": exact_block,
         "block_size_ratio": exact_block / payload,
+        "decode_traffic": profiling.recorded_traffic(DKV_WORKLOAD, profiling.DKV_TRAFFIC_FILE,
+                                                     profiling.DKV_SOURCES),
+        "decode_traffic_source": "profiles/dkv_attend_traffic.txt (rocprofv3 FETCH_SIZE and "
+                                 "WRITE_SIZE per dkv_attend_kernel launch, scaled as the roofline "
+                                 "traffic; null if the DKV decode sources changed)",
         "compress": {"us_per_launch": comp_us, "records": case.B * C * case.Hkv,
                      "us_per_record": comp_us / (case.B * C * case.Hkv)},
         "step_us": dkv_s / steps * 1e6,

@@ -10,6 +10,9 @@ plain-copy reference the counters are scaled by.
           COPY_FETCH_CSV COPY_WRITE_CSV OUT_TXT "COMMANDS"
       Per-launch HBM bytes of the decode kernel from two --pmc runs, scaled by
       the copy reference, stamped with the digest of the decode sources.
+  python -m query_aware_sparse_block_amd.profiling dkv-traffic WORKLOAD FETCH_CSV WRITE_CSV \
+          COPY_FETCH_CSV COPY_WRITE_CSV OUT_TXT "COMMANDS"
+      The same for the DKV decode kernel (dkv_attend_kernel) and its sources.
 """
 
 from __future__ import annotations
@@ -24,19 +27,29 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(_PKG)
 PROFILES = os.path.join(ROOT, "profiles")
 TRAFFIC_FILE = os.path.join(PROFILES, "attend_traffic.txt")
+DKV_TRAFFIC_FILE = os.path.join(PROFILES, "dkv_attend_traffic.txt")
 DECODE_SOURCES = ["csrc/kvsp_decode.hip", "csrc/kvsp_device.h", "csrc/kvsp_api.hip",
                   "csrc/kvsp_internal.h"]
+DKV_SOURCES = ["csrc/kvsp_dkv.hip", "csrc/kvsp_device.h", "csrc/kvsp_api.hip",
+               "csrc/kvsp_internal.h"]
 COPY_BYTES = 1 << 30
-DECODE_KERNEL = "attend_kernel"
+# Kernel-name prefixes as rocprofv3 prints them (the DKV kernel's name also
+# contains "attend_kernel", so the main one is matched with its namespace).
+DECODE_KERNEL = "kvsp::attend_kernel<"
+DKV_KERNEL = "dkv_attend_kernel<"
 COPY_KERNEL = "__amd_rocclr_copyBuffer"
 
 
-def decode_source_digest() -> str:
+def source_digest(sources) -> str:
     h = hashlib.sha256()
-    for rel in DECODE_SOURCES:
+    for rel in sources:
         with open(os.path.join(_PKG, rel), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
+
+
+def decode_source_digest() -> str:
+    return source_digest(DECODE_SOURCES)
 
 
 def copy_probe():
@@ -71,18 +84,21 @@ def copy_scale(copy_csv, counter):
 
 
 def write_traffic(workload, fetch_csv, write_csv, copy_fetch_csv, copy_write_csv, out_txt,
-                  commands):
-    fetch = counter_per_dispatch(fetch_csv, DECODE_KERNEL, "FETCH_SIZE")
-    write = counter_per_dispatch(write_csv, DECODE_KERNEL, "WRITE_SIZE")
+                  commands, kernel=DECODE_KERNEL, sources=DECODE_SOURCES,
+                  title="the decode kernel (attend_kernel)"):
+    fetch = counter_per_dispatch(fetch_csv, kernel, "FETCH_SIZE")
+    write = counter_per_dispatch(write_csv, kernel, "WRITE_SIZE")
+    if not fetch or not write:
+        raise RuntimeError(f"no {kernel} dispatch in {fetch_csv} / {write_csv}")
     fs = copy_scale(copy_fetch_csv, "FETCH_SIZE")
     ws = copy_scale(copy_write_csv, "WRITE_SIZE")
     f_med = statistics.median(fetch)
     w_med = statistics.median(write)
     traffic = f_med * fs + w_med * ws
     lines = [
-        "# HBM traffic of the decode kernel (attend_kernel), per launch",
+        f"# HBM traffic of {title}, per launch",
         f"workload = {workload}",
-        f"decode_source_digest = {decode_source_digest()}",
+        f"decode_source_digest = {source_digest(sources)}",
         f"fetch_size_median = {f_med:.1f}",
         f"write_size_median = {w_med:.1f}",
         f"dispatches = {len(fetch)} / {len(write)}",
@@ -96,9 +112,9 @@ def write_traffic(workload, fetch_csv, write_csv, copy_fetch_csv, copy_write_csv
     print("\n".join(lines))
 
 
-def recorded_traffic(workload, path=TRAFFIC_FILE):
+def recorded_traffic(workload, path=TRAFFIC_FILE, sources=DECODE_SOURCES):
     """Traffic bytes recorded for `workload`, or None when absent or when the
-    decode sources changed since the counters were taken."""
+    kernel's sources changed since the counters were taken."""
     if not os.path.exists(path):
         return None
     kv = {}
@@ -106,7 +122,7 @@ def recorded_traffic(workload, path=TRAFFIC_FILE):
         if "=" in line and not line.startswith("#"):
             k, v = line.split("=", 1)
             kv[k.strip()] = v.strip()
-    if kv.get("workload") != workload or kv.get("decode_source_digest") != decode_source_digest():
+    if kv.get("workload") != workload or kv.get("decode_source_digest") != source_digest(sources):
         return None
     return float(kv["traffic_bytes"])
 
@@ -139,6 +155,9 @@ def main(argv):
         write_stats(argv[1], argv[2], argv[3])
     elif cmd == "traffic":
         write_traffic(*argv[1:8])
+    elif cmd == "dkv-traffic":
+        write_traffic(*argv[1:8], kernel=DKV_KERNEL, sources=DKV_SOURCES,
+                      title="the DKV decode kernel (dkv_attend_kernel)")
     else:
         print(__doc__)
         return 2
