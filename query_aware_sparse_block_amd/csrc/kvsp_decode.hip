@@ -136,6 +136,12 @@ __global__ __launch_bounds__(256) void attend_kernel(DecodeArgs a) {
   constexpr int E = S::E;
   constexpr int QUANTUM = kDecodeWaves * S::SUB;
   __shared__ float p_lds[kDecodeWaves][S::SUB * S::PROW];
+  // One-head items keep the physical ids of 64 consecutive attended blocks in
+  // LDS, a row per wave, rather than in a register read with readlane: a
+  // refresh load behind a branch makes every later readlane wait at the join
+  // for all loads in flight (the prefetched tile included); an LDS read waits
+  // for none. (Head-group items measured faster with the register.)
+  __shared__ int32_t phys_lds[kDecodeWaves][GP == 1 ? kWave : 1];
   __shared__ float alpha_lds[kDecodeWaves][16];
   __shared__ float ml_lds[kDecodeWaves][2][16];
   __shared__ float xacc[kDecodeWaves - 1][GP * D];
@@ -203,7 +209,13 @@ __global__ __launch_bounds__(256) void attend_kernel(DecodeArgs a) {
     int phys_v = 0;
     {
       const int ab = gbase + lane;
-      if (ab < w.A) phys_v = attended_phys(a, b, w, ab);
+      const int32_t p0 = ab < w.A ? attended_phys(a, b, w, ab) : 0;
+      if constexpr (GP == 1) {
+        phys_lds[wave][lane] = p0;
+        wave_lds_sync();
+      } else {
+        phys_v = p0;
+      }
     }
 
     const char* kbase = static_cast<const char*>(a.k_pool);
@@ -234,14 +246,25 @@ __global__ __launch_bounds__(256) void attend_kernel(DecodeArgs a) {
       if (a_last - gbase >= kWave) {
         gbase = i0 / a.P;
         const int ab = gbase + lane;
-        phys_v = ab < w.A ? attended_phys(a, b, w, ab) : 0;
+        const int32_t p1 = ab < w.A ? attended_phys(a, b, w, ab) : 0;
+        if constexpr (GP == 1) {
+          phys_lds[wave][lane] = p1;
+          wave_lds_sync();
+        } else {
+          phys_v = p1;
+        }
       }
       int64_t tile_byte0[S::TILES];  // byte offset of the tile's first row in the pool
 #pragma unroll
       for (int t = 0; t < S::TILES; ++t) {
         const int ti = i0 + 16 * t;
         const int ab = min(ti, end - 1) / a.P;
-        const int64_t phys = __builtin_amdgcn_readlane(phys_v, ab - gbase);
+        int64_t phys;
+        if constexpr (GP == 1) {
+          phys = phys_lds[wave][ab - gbase];
+        } else {
+          phys = __builtin_amdgcn_readlane(phys_v, ab - gbase);
+        }
         tile_byte0[t] = ((phys * a.Hkv + g) * a.P + (ti % a.P)) * static_cast<int64_t>(D * E);
       }
       // Rows past `end` still lie inside a valid physical block (tiles are
@@ -330,15 +353,33 @@ __global__ __launch_bounds__(256) void attend_kernel(DecodeArgs a) {
     int i0 = first_tok;
     if (i0 < end) issue(i0, buf0);
     if constexpr (GP <= KVSP_PIPELINE_MAX_GP) {
-      while (i0 < end) {
-        int i1 = i0 + STRIDE;
-        if (i1 < end) issue(i1, buf1);
-        consume(i0, buf0);
-        if (i1 >= end) break;
-        const int i2 = i1 + STRIDE;
-        if (i2 < end) issue(i2, buf0);
-        consume(i1, buf1);
-        i0 = i2;
+      if constexpr (GP == 1) {
+        // One-head items: every step issues a tile, so that every path has
+        // the same loads in flight and a tile's use waits for that tile alone
+        // (with a conditional issue the wait also covers the first load of
+        // the tile just requested). Past the end the current tile is
+        // requested again (valid addresses; the data is not used).
+        while (i0 < end) {
+          const int i1 = i0 + STRIDE;
+          issue(i1 < end ? i1 : i0, buf1);
+          consume(i0, buf0);
+          if (i1 >= end) break;
+          const int i2 = i1 + STRIDE;
+          issue(i2 < end ? i2 : i1, buf0);
+          consume(i1, buf1);
+          i0 = i2;
+        }
+      } else {
+        while (i0 < end) {
+          const int i1 = i0 + STRIDE;
+          if (i1 < end) issue(i1, buf1);
+          consume(i0, buf0);
+          if (i1 >= end) break;
+          const int i2 = i1 + STRIDE;
+          if (i2 < end) issue(i2, buf0);
+          consume(i1, buf1);
+          i0 = i2;
+        }
       }
     } else {
       while (i0 < end) {

@@ -203,11 +203,18 @@ __device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x) {
 }
 
 // Orders LDS traffic between lanes of one wavefront (no workgroup barrier:
-// the waves of a workgroup run independent work items).
+// the waves of a workgroup run independent work items). A wavefront's LDS
+// operations execute in order, so wavefront-scope fences (which keep the
+// compiler from moving memory operations across them and emit no wait) are
+// enough. Workgroup scope would also wait for the wave's outstanding global
+// loads, i.e. drain the next tile's prefetch at every call.
+#ifndef KVSP_WAVE_SYNC_SCOPE
+#define KVSP_WAVE_SYNC_SCOPE "wavefront"
+#endif
 __device__ __forceinline__ void wave_lds_sync() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, KVSP_WAVE_SYNC_SCOPE);
   __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, KVSP_WAVE_SYNC_SCOPE);
 }
 
 // ---- device-coherent accesses ------------------------------------------------------
