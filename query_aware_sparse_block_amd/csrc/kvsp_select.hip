@@ -36,7 +36,9 @@ namespace kvsp {
 // returns C (the sequence's candidate count). COHERENT stores make the scores
 // visible to other workgroups of the same launch.
 
-template <typename T, int LG, int VPL, bool COHERENT>
+// STREAM (a.stream_rows as a template parameter) reads the summary rows with
+// non-temporal loads and runs the passes as a branch-free pipeline.
+template <typename T, int LG, int VPL, bool COHERENT, bool STREAM>
 __device__ __forceinline__ int score_blocks(const ScoreArgs& a, double* qbar, int b) {
   const int lane = threadIdx.x % kWave;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
@@ -101,10 +103,22 @@ __device__ __forceinline__ int score_blocks(const ScoreArgs& a, double* qbar, in
   // (a.stream_rows, uniform); small ones may stay cached between calls.
   auto issue = [&](int jb, float4 (&sv)[VPL], bool direct) {
     const int j = jb + slot;
+    if (STREAM && !direct) {
+      // Later streamed passes: no load behind a per-lane branch (such a load
+      // is waited for alone, and the next pass's loads could not stay in
+      // flight). A row past j1 reads the last live row of the range and a
+      // vector past the row's end the row's last vector; consume masks both.
+      const int64_t phys = phys_lds[min(j, j1 - 1) - first];
+      const float4* srow = reinterpret_cast<const float4*>(a.summaries + phys * row);
+#pragma unroll
+      for (int v = 0; v < VPL; ++v)
+        sv[v] = __builtin_bit_cast(float4, load16_stream(srow + min(gl + LG * v, nvec - 1)));
+      return;
+    }
     int64_t phys = 0;
     if (j < j1) phys = direct ? a.block_table[trow + j] : phys_lds[j - first];
     const float4* srow = reinterpret_cast<const float4*>(a.summaries + phys * row);
-    if (a.stream_rows) {
+    if constexpr (STREAM) {
 #pragma unroll
       for (int v = 0; v < VPL; ++v)
         sv[v] = (j < j1 && gl + LG * v < nvec) ? __builtin_bit_cast(float4, load16_stream(srow + gl + LG * v))
@@ -117,14 +131,30 @@ __device__ __forceinline__ int score_blocks(const ScoreArgs& a, double* qbar, in
   };
   auto consume = [&](int jb, const float4 (&sv)[VPL]) {
     double acc = 0.0;
+    if constexpr (STREAM) {
+      // Straight-line: a per-lane conditional here becomes a branch around
+      // the LDS reads, and every such branch waits for all loads in flight.
+      // A vector past the row's end is weighted by 0.0 and adds a zero (the
+      // sum starts at +0.0, so its bits are those of the sum over the row).
 #pragma unroll
-    for (int v = 0; v < VPL; ++v) {
-      if (gl + LG * v < nvec) {
-        const double* qv = qbar + 4 * (gl + LG * v);
-        acc += qv[0] * static_cast<double>(sv[v].x);
-        acc += qv[1] * static_cast<double>(sv[v].y);
-        acc += qv[2] * static_cast<double>(sv[v].z);
-        acc += qv[3] * static_cast<double>(sv[v].w);
+      for (int v = 0; v < VPL; ++v) {
+        const double in = gl + LG * v < nvec ? 1.0 : 0.0;
+        const double* qv = qbar + 4 * min(gl + LG * v, nvec - 1);
+        acc += (qv[0] * in) * static_cast<double>(sv[v].x);
+        acc += (qv[1] * in) * static_cast<double>(sv[v].y);
+        acc += (qv[2] * in) * static_cast<double>(sv[v].z);
+        acc += (qv[3] * in) * static_cast<double>(sv[v].w);
+      }
+    } else {
+#pragma unroll
+      for (int v = 0; v < VPL; ++v) {
+        if (gl + LG * v < nvec) {
+          const double* qv = qbar + 4 * (gl + LG * v);
+          acc += qv[0] * static_cast<double>(sv[v].x);
+          acc += qv[1] * static_cast<double>(sv[v].y);
+          acc += qv[2] * static_cast<double>(sv[v].z);
+          acc += qv[3] * static_cast<double>(sv[v].w);
+        }
       }
     }
     acc = group_sum<LG>(acc);
@@ -144,15 +174,34 @@ __device__ __forceinline__ int score_blocks(const ScoreArgs& a, double* qbar, in
     if (jb < j1) issue(jb, buf0, true);
     __syncthreads();  // qbar and the staged table entries
     if (first >= C) return C;  // uniform over the workgroup
-    while (jb < j1) {
-      const int jn = jb + BPP;
-      if (jn < j1) issue(jn, buf1, false);
-      consume(jb, buf0);
-      if (jn >= j1) break;
-      const int jn2 = jn + BPP;
-      if (jn2 < j1) issue(jn2, buf0, false);
-      consume(jn, buf1);
-      jb = jn2;
+    if constexpr (STREAM) {
+      // Every pass issues one, so that a pass's use waits for that pass alone
+      // (past the end the current pass is requested again; its data is not
+      // used). The scheduling barriers keep the next pass's loads ahead of
+      // this pass's arithmetic, which would otherwise be hoisted above them.
+      while (jb < j1) {
+        const int jn = jb + BPP;
+        issue(jn < j1 ? jn : jb, buf1, false);
+        __builtin_amdgcn_sched_barrier(0);
+        consume(jb, buf0);
+        if (jn >= j1) break;
+        const int jn2 = jn + BPP;
+        issue(jn2 < j1 ? jn2 : jn, buf0, false);
+        __builtin_amdgcn_sched_barrier(0);
+        consume(jn, buf1);
+        jb = jn2;
+      }
+    } else {
+      while (jb < j1) {
+        const int jn = jb + BPP;
+        if (jn < j1) issue(jn, buf1, false);
+        consume(jb, buf0);
+        if (jn >= j1) break;
+        const int jn2 = jn + BPP;
+        if (jn2 < j1) issue(jn2, buf0, false);
+        consume(jn, buf1);
+        jb = jn2;
+      }
     }
   } else {
     // The longest rows: one buffer already holds 32 vectors per lane.
@@ -168,10 +217,10 @@ __device__ __forceinline__ int score_blocks(const ScoreArgs& a, double* qbar, in
   return C;
 }
 
-template <typename T, int LG, int VPL>
+template <typename T, int LG, int VPL, bool STREAM>
 __global__ __launch_bounds__(256) void score_kernel(ScoreArgs a) {
   extern __shared__ double qbar[];  // [Hkv * D] group-summed queries, then [4 * bpw] ints
-  score_blocks<T, LG, VPL, false>(a, qbar, blockIdx.y);
+  score_blocks<T, LG, VPL, false, STREAM>(a, qbar, blockIdx.y);
 }
 
 template <typename T, int LG, int VPL>
@@ -179,7 +228,10 @@ static hipError_t launch_score_v(const ScoreArgs& a, hipStream_t stream) {
   const int per_wg = 4 * a.blocks_per_wave;
   dim3 grid((a.max_blocks + per_wg - 1) / per_wg, a.B);
   const size_t lds = static_cast<size_t>(a.Hkv) * a.D * sizeof(double) + per_wg * sizeof(int32_t);
-  hipLaunchKernelGGL((score_kernel<T, LG, VPL>), grid, dim3(256), lds, stream, a);
+  if (a.stream_rows)
+    hipLaunchKernelGGL((score_kernel<T, LG, VPL, true>), grid, dim3(256), lds, stream, a);
+  else
+    hipLaunchKernelGGL((score_kernel<T, LG, VPL, false>), grid, dim3(256), lds, stream, a);
   return hipGetLastError();
 }
 
@@ -514,12 +566,12 @@ static hipError_t launch_topk_w(const TopkArgs& a, hipStream_t stream) {
 // device-scope atomic) runs that sequence's Top-k on the scores the others
 // published. Workgroup 0 of every sequence takes part even with no
 // candidates, so every sequence gets its counts and spans.
-template <typename T, int LG, int VPL>
+template <typename T, int LG, int VPL, bool STREAM>
 __global__ __launch_bounds__(256) void score_select_kernel(ScoreArgs sa, TopkArgs ta,
                                                            int32_t* counters) {
   extern __shared__ double lds[];
   const int b = blockIdx.y;
-  const int C = score_blocks<T, LG, VPL, true>(sa, lds, b);
+  const int C = score_blocks<T, LG, VPL, true, STREAM>(sa, lds, b);
   const int per_wg = 4 * sa.blocks_per_wave;
   const int first = blockIdx.x * per_wg;
   if (first >= C && blockIdx.x != 0) return;  // uniform: no blocks, not the anchor
@@ -548,8 +600,12 @@ static hipError_t launch_fused_v(const ScoreArgs& sa, const TopkArgs& ta, int32_
   const size_t score_lds = static_cast<size_t>(sa.Hkv) * sa.D * sizeof(double) + per_wg * sizeof(int32_t);
   const size_t topk_lds = sizeof(TopkShared);
   const size_t lds = (score_lds > topk_lds ? score_lds : topk_lds + 7) / 8 * 8;
-  hipLaunchKernelGGL((score_select_kernel<T, LG, VPL>), grid, dim3(256), lds, stream, sa, ta,
-                     counters);
+  if (sa.stream_rows)
+    hipLaunchKernelGGL((score_select_kernel<T, LG, VPL, true>), grid, dim3(256), lds, stream, sa, ta,
+                       counters);
+  else
+    hipLaunchKernelGGL((score_select_kernel<T, LG, VPL, false>), grid, dim3(256), lds, stream, sa,
+                       ta, counters);
   return hipGetLastError();
 }
 
