@@ -241,7 +241,13 @@ __global__ __launch_bounds__(256) void attend_kernel(DecodeArgs a) {
     };
     // Enqueue the K and V loads of the sub-tile starting at attended token i0.
     // Tile bases are wave-uniform, so every load is base + lane offset.
-    auto issue = [&](int i0, SubTile& st) {
+    // A repeat (repeat == true, the one-head pipeline past the end) keeps
+    // the instruction count, which the waits depend on, but points every
+    // lane at the tile's first 16 bytes: one line per load instead of the
+    // tile, whose data would not be used.
+    auto issue = [&](int i0, SubTile& st, bool repeat = false) {
+      const uint32_t k_off = repeat ? 0u : k_lane_off;
+      const uint32_t v_off = repeat ? 0u : v_lane_off;
       const int a_last = (min(i0 + S::SUB, end) - 1) / a.P;
       if (a_last - gbase >= kWave) {
         gbase = i0 / a.P;
@@ -274,13 +280,13 @@ __global__ __launch_bounds__(256) void attend_kernel(DecodeArgs a) {
       for (int t = 0; t < S::TILES; ++t) {
         const char* tk = kbase + tile_byte0[t];
 #pragma unroll
-        for (int s = 0; s < S::KLD; ++s) st.kv[t][s] = kv_load(tk + k_lane_off + 64 * s);
+        for (int s = 0; s < S::KLD; ++s) st.kv[t][s] = kv_load(tk + k_off + (repeat ? 0 : 64 * s));
       }
 #pragma unroll
       for (int r = 0; r < S::VLD; ++r) {
         const int t = (r * S::RPL) / 16;
         const char* tv = vbase + tile_byte0[t] + (r * S::RPL - 16 * t) * D * E;
-        st.vv[r] = kv_load(tv + v_lane_off);
+        st.vv[r] = kv_load(tv + v_off);
       }
     };
 
@@ -361,11 +367,11 @@ __global__ __launch_bounds__(256) void attend_kernel(DecodeArgs a) {
         // requested again (valid addresses; the data is not used).
         while (i0 < end) {
           const int i1 = i0 + STRIDE;
-          issue(i1 < end ? i1 : i0, buf1);
+          issue(i1 < end ? i1 : i0, buf1, i1 >= end);
           consume(i0, buf0);
           if (i1 >= end) break;
           const int i2 = i1 + STRIDE;
-          issue(i2 < end ? i2 : i1, buf0);
+          issue(i2 < end ? i2 : i1, buf0, i2 >= end);
           consume(i1, buf1);
           i0 = i2;
         }
