@@ -342,3 +342,24 @@ def test_budget_controller_drives_the_selection(bw, floor):
     for b in range(B):
         p = oracle.plan(int(case.ctx_lens[b]), P, 128, keep_num=num, keep_den=1024, keep_floor=floor)
         assert int(gpu["num_selected"][b]) == p["k_eff"]
+
+
+@pytest.mark.parametrize("keep", ["1/2", "dense"])
+def test_one_head_items_longer_than_the_id_window(keep):
+    # one-head (MHA) items that attend more than 64 blocks: 64 sequences x 4
+    # KV heads make 256 groups, so every group is a single chunk, and 16-token
+    # blocks over 2048 tokens give 128 blocks per item; the per-wave window of
+    # physical block ids is refreshed inside the streaming loop
+    B, NH, P, L = 64, 4, 16, 2048
+    params = dict(keep_num=1, keep_den=2) if keep == "1/2" else dict(keep_num=1, keep_den=1)
+    case = wl.make_case(f"mha-long-items-{keep.replace('/', '_')}", seed=9300, B=B, Hq=NH, Hkv=NH,
+                        D=128, P=P, dtype="fp16", ctx_lens=[L] * B, keep_floor=1,
+                        recent_window=64, **params)
+    H.note(f"[long items] keep={keep}")
+    H.full_parity(case, check_all_summaries=False)
+    if keep == "dense":
+        gpu, dc, buf = H.run_gpu(case, dense_api=True)
+        for b in (0, 17, 63):
+            outs, _ = H.oracle_attention_on(case, b, [], True)
+            for h, o in outs.items():
+                assert np.max(np.abs(gpu["out"][b, h] - o)) <= 2e-3, (b, h)
