@@ -131,6 +131,17 @@ def summaries(dtype, k_pool, block_table, ctx_lens, Hkv, P, D):
     return out
 
 
+def stored_summaries(summ: np.ndarray) -> np.ndarray:
+    """The summaries as the GPU keeps them resident: each double mean rounded
+    to the nearest float32, ties to even (the compact per-block summary is
+    held in float32 [SparPR ¶Query-Aware key-block selection: summaries stay
+    resident on the GPU and scoring reads only them]). Scores are computed
+    from these stored values. NaN entries (no full block) stay NaN. The
+    rounding is numpy's float64 -> float32 cast, which is IEEE
+    round-to-nearest-even."""
+    return np.asarray(summ, np.float64).astype(np.float32).astype(np.float64)
+
+
 def append(dtype, k_pool, v_pool, k_new, v_new, block_table, positions, *, Hkv, P, D):
     """Decode-time append [SparPR opening paragraphs; ¶Query-Aware key-block
     selection]: writes each sequence's new K/V row at token positions[b]

@@ -19,6 +19,8 @@
 // remaining places (ties go to the lower block index). Block-wide scans then
 // emit the kept ids in ascending order and the span boundaries.
 
+#include <algorithm>
+
 #include "kvsp_device.h"
 #include "kvsp_internal.h"
 
@@ -599,7 +601,7 @@ static hipError_t launch_fused_v(const ScoreArgs& sa, const TopkArgs& ta, int32_
   dim3 grid((sa.max_blocks + per_wg - 1) / per_wg, sa.B);
   const size_t score_lds = static_cast<size_t>(sa.Hkv) * sa.D * sizeof(double) + per_wg * sizeof(int32_t);
   const size_t topk_lds = sizeof(TopkShared);
-  const size_t lds = (score_lds > topk_lds ? score_lds : topk_lds + 7) / 8 * 8;
+  const size_t lds = (std::max(score_lds, topk_lds) + 7) / 8 * 8;
   if (sa.stream_rows)
     hipLaunchKernelGGL((score_select_kernel<T, LG, VPL, true>), grid, dim3(256), lds, stream, sa, ta,
                        counters);

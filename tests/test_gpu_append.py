@@ -86,9 +86,10 @@ def test_decode_loop_appends_match_oracle(dtype, Hq, Hkv, D, P):
     summ = H.oracle_summaries(grown)
     r_or = oracle.decode_step(dtype, grown.q, k_host, v_host, grown.block_table, ctx, summ,
                               Hkv=Hkv, P=P, **grown.select_params)
-    H.check_scores(grown, r_or, gpu)
+    T = H.term_sums(grown, summ)
+    H.check_scores(grown, r_or, gpu, T)
     for b in range(B):
-        sel = H.check_selection(grown, r_or, gpu, b)
+        sel = H.check_selection(grown, r_or, gpu, b, T)
         H.check_outputs(grown, r_or, gpu, b, sel)
 
 

@@ -1,16 +1,15 @@
 """GPU parity at the workloads' full sizes, in the launch configuration the
 benchmark times (same entry points, same layouts).
 
-The OPT-like, MiniCPM-like and Qwen-like families are checked completely
-(every score, selection, span, output and lse). The batched serving shape
-(64 sequences of 32768 tokens, an 8 GiB pool) is checked completely for
-summaries, scores and selection, and on a seeded sample of (sequence, head)
-outputs that the oracle recomputes one by one; its dense-fallback variant
-(keep 7/10 > gamma 3/5) likewise."""
+Every family is checked completely: every summary, score, selection, span,
+output and lse. That includes the batched serving shape (64 sequences of
+32768 tokens in an 8 GiB pool, 2048 (sequence, head) outputs) at keep 1/32
+and in its dense-fallback variant (keep 7/10 > gamma 3/5, every token of every
+sequence attended); the oracle runs its (sequence, head) attentions on the
+host's thread share."""
 
 import dataclasses
 
-import numpy as np
 import pytest
 
 from query_aware_sparse_block_amd import workloads as wl
@@ -46,25 +45,19 @@ def test_qwen_like_full(L):
 @pytest.fixture(scope="module")
 def serving_case():
     H.note("[fullsize] generating the batched serving workload (8 GiB pool)")
-    return wl.c5(keep="1/32")
-
-
-def _sample_mask(case, n, seed):
-    rng = np.random.default_rng(seed)
-    mask = np.zeros((case.B, case.Hq), np.uint8)
-    while int(mask.sum()) < n:
-        mask[rng.integers(case.B), rng.integers(case.Hq)] = 1
-    mask[0, 0] = mask[case.B - 1, case.Hq - 1] = 1   # first and last head always
-    return mask
+    case = wl.c5(keep="1/32")
+    H.note("[fullsize] oracle summaries of the serving workload")
+    return case, H.oracle_summaries(case)
 
 
 def test_serving_full_sparse(serving_case):
-    gpu, r_or = H.full_parity(serving_case, head_mask=_sample_mask(serving_case, 24, 1))
+    case, summ = serving_case
+    gpu, r_or = H.full_parity(case, summ=summ)
     assert (gpu["num_selected"] == 16).all() and not gpu["use_dense"].any()
 
 
 def test_serving_full_dense_fallback(serving_case):
-    case = dataclasses.replace(serving_case, name="c5-keep7/10", keep_num=7, keep_den=10)
-    gpu, r_or = H.full_parity(case, head_mask=_sample_mask(case, 8, 2),
-                              check_all_summaries=False)
+    base, summ = serving_case
+    case = dataclasses.replace(base, name="c5-keep7/10", keep_num=7, keep_den=10)
+    gpu, r_or = H.full_parity(case, summ=summ)
     assert (gpu["num_selected"] == 359).all() and gpu["use_dense"].all()

@@ -29,6 +29,7 @@ def test_streamed_scoring_with_partial_rows_matches_oracle():
     H.check_summaries(case, gpu["summaries"], summ)
     r_or = oracle.decode_step(case.dtype, case.q, case.k_pool, case.v_pool, case.block_table,
                               case.ctx_lens, summ, Hkv=case.Hkv, P=case.P, **case.select_params)
-    H.check_scores(case, r_or, gpu)
+    T = H.term_sums(case, summ)
+    H.check_scores(case, r_or, gpu, T)
     for b in range(B):
-        H.check_selection(case, r_or, gpu, b)
+        H.check_selection(case, r_or, gpu, b, T)

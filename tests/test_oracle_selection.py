@@ -259,3 +259,34 @@ def test_attended_tokens_sparse_and_dense():
     toks = oracle.attended_tokens(L=70, P=16, C=2, sel=np.array([1]), use_dense=1)
     assert toks.tolist() == list(range(70))
     assert math.isclose(len(oracle.attended_tokens(1024, 16, 62, np.arange(8), 0)), 160)
+
+
+# ---- stored (float32) summaries --------------------------------------------------
+
+@pytest.mark.parametrize("keys,expect", [
+    # P = 2: the mean falls exactly halfway between two float32 values and
+    # rounds to the one with an even last mantissa bit
+    ([1.0, 1.0 + 2.0 ** -23], 1.0),
+    ([1.0 + 2.0 ** -23, 1.0 + 2.0 ** -22], 1.0 + 2.0 ** -22),
+    ([1.0, 1.0 + 3 * 2.0 ** -23], 1.0 + 2.0 ** -22),
+    ([-1.0, -(1.0 + 2.0 ** -23)], -1.0),
+    # P = 4: below and above the halfway point
+    ([1.0, 1.0, 1.0, 1.0 + 2.0 ** -23], 1.0),
+    ([1.0 + 2.0 ** -23, 1.0 + 2.0 ** -23, 1.0 + 2.0 ** -23, 1.0], 1.0 + 2.0 ** -23),
+    # exactly representable means are unchanged
+    ([0.5, 0.25], 0.375),
+])
+def test_stored_summary_is_the_mean_rounded_to_nearest_even_float32(keys, expect):
+    P = len(keys)
+    pool = np.asarray(keys, np.float32).reshape(1, 1, P, 1)
+    bt = np.zeros((1, 1), np.int32)
+    s = oracle.summaries("fp32", pool, bt, np.array([P], np.int32), 1, P, 1)
+    assert s[0, 0, 0, 0] == np.mean(np.asarray(keys, np.float64))  # the exact double mean
+    stored = oracle.stored_summaries(s)
+    assert stored[0, 0, 0, 0] == expect
+
+
+def test_stored_summaries_keep_missing_blocks_missing():
+    s = np.array([[[[np.nan, 1.0 / 3.0]]]])
+    out = oracle.stored_summaries(s)
+    assert np.isnan(out[0, 0, 0, 0]) and out[0, 0, 0, 1] == float(np.float32(1.0 / 3.0))
