@@ -226,19 +226,29 @@ kvsp_status kvsp_score_topk(const kvsp_layout* layout, const kvsp_select_params*
 
 /* Steps 4-5 (DKV abstract: attention over the routed blocks and the exact
  * recency window, partial softmaxes merged by a flash-style log-sum-exp;
- * SparPR, "On-demand local recomputation with cost-aware fallback": the
- * dense path). For every sequence b and query head h, attends over
- *   tokens of selected[b][0..num_selected[b]) followed by tokens [C*P, L)
- * or, if use_dense is non-NULL and use_dense[b] != 0, over all tokens
- * [0, L), with logits scale * <q, K> (scale <= 0 means 1/sqrt(head_dim)),
- * accumulating in float32, and writes the normalised output and its
- * log-sum-exp. `selected` holds ascending candidate ids < C as written by
- * kvsp_score_topk; params supplies recent_window (C depends on it). A
- * sequence with no cached token attends nothing: its out is 0 and its lse
- * -inf. */
+ * SparPR, "On-demand local recomputation with cost-aware fallback": kept
+ * blocks recovered as contiguous spans, and the dense path). For every
+ * sequence b and query head h, attends over the kept blocks, given in one
+ * of two forms (exactly one pair is non-NULL, else KVSP_ERR_INVALID_ARG):
+ *   spans, num_spans        the span list kvsp_score_topk writes: the tokens
+ *                           of logical blocks [start, end) of spans[b][0..
+ *                           num_spans[b]), ascending, the window run last;
+ *                           or
+ *   selected, num_selected  the tokens of selected[b][0..num_selected[b])
+ *                           (ascending candidate ids < C) followed by the
+ *                           window tokens [C*P, L);
+ * both describe the same tokens in the same order and give bit-identical
+ * results. If use_dense is non-NULL and use_dense[b] != 0 the sequence
+ * attends all tokens [0, L) instead. Logits are scale * <q, K> (scale <= 0
+ * means 1/sqrt(head_dim)), accumulated in float32; writes the normalised
+ * output and its log-sum-exp. params supplies recent_window (C depends on
+ * it). Spans must cover block ceil(L/P) - 1 whenever it is partial (the
+ * window always does). A sequence with no cached token attends nothing: its
+ * out is 0 and its lse -inf. */
 kvsp_status kvsp_sparse_decode(const kvsp_layout* layout, const kvsp_select_params* params,
                                const void* q, const void* k_pool, const void* v_pool,
                                const int32_t* block_table, const int32_t* context_lens,
+                               const int32_t* spans, const int32_t* num_spans,
                                const int32_t* selected, const int32_t* num_selected,
                                const int32_t* use_dense, float scale, float* out, float* lse,
                                void* workspace, size_t workspace_bytes, hipStream_t stream);
@@ -338,7 +348,7 @@ kvsp_status kvsp_dkv_decode(const kvsp_layout* layout, const kvsp_select_params*
 const char* kvsp_status_string(kvsp_status status);
 
 /* ABI version of this header (bumped on any incompatible change). */
-#define KVSP_ABI_VERSION 1
+#define KVSP_ABI_VERSION 2
 int32_t kvsp_abi_version(void);
 
 #ifdef __cplusplus

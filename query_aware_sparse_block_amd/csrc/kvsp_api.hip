@@ -125,21 +125,51 @@ WorkspaceLayout workspace_layout(const kvsp_layout& l) {
 
 kvsp_status from_hip(hipError_t e) { return e == hipSuccess ? KVSP_OK : KVSP_ERR_HIP; }
 
-kvsp_status run_decode(const kvsp_layout* layout, const kvsp_select_params* params, bool all_dense,
-                       const void* q, const void* k_pool, const void* v_pool,
-                       const int32_t* block_table, const int32_t* context_lens,
-                       const int32_t* selected, const int32_t* num_selected,
-                       const int32_t* use_dense, float scale, float* out, float* lse,
-                       void* workspace, size_t workspace_bytes, hipStream_t stream) {
+// Host checks shared by every decode entry point (no HIP call).
+kvsp_status check_decode(const kvsp_layout* layout, const kvsp_select_params* params, bool all_dense,
+                         const void* q, const void* k_pool, const void* v_pool,
+                         const int32_t* block_table, const int32_t* context_lens,
+                         const int32_t* spans, const int32_t* num_spans,
+                         const int32_t* selected, const int32_t* num_selected, const float* out) {
   kvsp_status st = check_layout(layout);
   if (st != KVSP_OK) return st;
   if (!all_dense && (st = check_params(params)) != KVSP_OK) return st;
   if (!q || !k_pool || !v_pool || !block_table || !context_lens || !out)
     return KVSP_ERR_INVALID_ARG;
-  if (!all_dense && (!selected || !num_selected)) return KVSP_ERR_INVALID_ARG;
-  const kvsp_layout& l = *layout;
+  if (!all_dense) {
+    // exactly one form of the kept blocks: the span list or the selected list
+    const bool by_spans = spans != nullptr || num_spans != nullptr;
+    const bool by_list = selected != nullptr || num_selected != nullptr;
+    if (by_spans == by_list) return KVSP_ERR_INVALID_ARG;
+    if (by_spans && (!spans || !num_spans)) return KVSP_ERR_INVALID_ARG;
+    if (by_list && (!selected || !num_selected)) return KVSP_ERR_INVALID_ARG;
+  }
+  return KVSP_OK;
+}
+
+// Where a decode keeps its completion counters and split-KV partials.
+struct DecodeScratch {
+  int32_t* counters;
+  float* part_acc;
+  float* part_ml;
+};
+
+DecodeScratch workspace_scratch(const kvsp_layout& l, void* workspace) {
   const WorkspaceLayout wl = workspace_layout(l);
-  if (workspace == nullptr || workspace_bytes < wl.total) return KVSP_ERR_WORKSPACE;
+  char* base = static_cast<char*>(workspace);
+  return {reinterpret_cast<int32_t*>(base + wl.counters), reinterpret_cast<float*>(base + wl.part_acc),
+          reinterpret_cast<float*>(base + wl.part_ml)};
+}
+
+// Launches the decode of checked arguments into `scr`.
+kvsp_status launch_checked_decode(const kvsp_layout& l, const kvsp_select_params* params,
+                                  bool all_dense, const void* q, const void* k_pool,
+                                  const void* v_pool, const int32_t* block_table,
+                                  const int32_t* context_lens, const int32_t* spans,
+                                  const int32_t* num_spans, const int32_t* selected,
+                                  const int32_t* num_selected, const int32_t* use_dense,
+                                  float scale, float* out, float* lse, const DecodeScratch& scr,
+                                  hipStream_t stream) {
   const DecodeGeometry g = decode_geometry(l);
   DecodeArgs a;
   a.q = q;
@@ -149,12 +179,14 @@ kvsp_status run_decode(const kvsp_layout* layout, const kvsp_select_params* para
   a.context_lens = context_lens;
   a.selected = all_dense ? nullptr : selected;
   a.num_selected = all_dense ? nullptr : num_selected;
+  a.spans = all_dense ? nullptr : spans;
+  a.num_spans = all_dense ? nullptr : num_spans;
   a.use_dense = all_dense ? nullptr : use_dense;
   a.out = out;
   a.lse = lse;
-  a.part_acc = reinterpret_cast<float*>(static_cast<char*>(workspace) + wl.part_acc);
-  a.part_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) + wl.part_ml);
-  a.counters = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + wl.counters);
+  a.part_acc = scr.part_acc;
+  a.part_ml = scr.part_ml;
+  a.counters = scr.counters;
   a.B = l.batch;
   a.Hq = l.num_q_heads;
   a.Hkv = l.num_kv_heads;
@@ -169,6 +201,23 @@ kvsp_status run_decode(const kvsp_layout* layout, const kvsp_select_params* para
   const float s = scale > 0.f ? scale : 1.0f / __builtin_sqrtf(static_cast<float>(l.head_dim));
   a.scale_log2 = s * 1.4426950408889634f;
   return from_hip(launch_decode(a, l.dtype, g.gp, g.num_wgs, stream));
+}
+
+kvsp_status run_decode(const kvsp_layout* layout, const kvsp_select_params* params, bool all_dense,
+                       const void* q, const void* k_pool, const void* v_pool,
+                       const int32_t* block_table, const int32_t* context_lens,
+                       const int32_t* spans, const int32_t* num_spans,
+                       const int32_t* selected, const int32_t* num_selected,
+                       const int32_t* use_dense, float scale, float* out, float* lse,
+                       void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  const kvsp_status st = check_decode(layout, params, all_dense, q, k_pool, v_pool, block_table,
+                                      context_lens, spans, num_spans, selected, num_selected, out);
+  if (st != KVSP_OK) return st;
+  const kvsp_layout& l = *layout;
+  if (workspace == nullptr || workspace_bytes < workspace_layout(l).total) return KVSP_ERR_WORKSPACE;
+  return launch_checked_decode(l, params, all_dense, q, k_pool, v_pool, block_table, context_lens,
+                               spans, num_spans, selected, num_selected, use_dense, scale, out,
+                               lse, workspace_scratch(l, workspace), stream);
 }
 
 // ---- DKV variant ------------------------------------------------------------------
@@ -443,11 +492,13 @@ kvsp_status kvsp_score_topk(const kvsp_layout* layout, const kvsp_select_params*
 kvsp_status kvsp_sparse_decode(const kvsp_layout* layout, const kvsp_select_params* params,
                                const void* q, const void* k_pool, const void* v_pool,
                                const int32_t* block_table, const int32_t* context_lens,
+                               const int32_t* spans, const int32_t* num_spans,
                                const int32_t* selected, const int32_t* num_selected,
                                const int32_t* use_dense, float scale, float* out, float* lse,
                                void* workspace, size_t workspace_bytes, hipStream_t stream) {
-  return run_decode(layout, params, false, q, k_pool, v_pool, block_table, context_lens, selected,
-                    num_selected, use_dense, scale, out, lse, workspace, workspace_bytes, stream);
+  return run_decode(layout, params, false, q, k_pool, v_pool, block_table, context_lens, spans,
+                    num_spans, selected, num_selected, use_dense, scale, out, lse, workspace,
+                    workspace_bytes, stream);
 }
 
 kvsp_status kvsp_dense_decode(const kvsp_layout* layout, const void* q, const void* k_pool,
@@ -455,7 +506,8 @@ kvsp_status kvsp_dense_decode(const kvsp_layout* layout, const void* q, const vo
                               const int32_t* context_lens, float scale, float* out, float* lse,
                               void* workspace, size_t workspace_bytes, hipStream_t stream) {
   return run_decode(layout, nullptr, true, q, k_pool, v_pool, block_table, context_lens, nullptr,
-                    nullptr, nullptr, scale, out, lse, workspace, workspace_bytes, stream);
+                    nullptr, nullptr, nullptr, nullptr, scale, out, lse, workspace, workspace_bytes,
+                    stream);
 }
 
 size_t kvsp_dkv_record_bytes(const kvsp_layout* layout, const kvsp_dkv_params* dkv) {

@@ -7,8 +7,10 @@
 //
 // Work decomposition. For sequence b the attended tokens form one ordered
 // sequence: the tokens of selected[b][0..k) followed by the window [C*P, L)
-// (or all of [0, L) when dense). Attended token i lives in attended block
-// i / P at offset i % P, because every attended block but the last is full.
+// (or all of [0, L) when dense). Given as spans, the same blocks are the
+// union of the spans in ascending order (the window run last). Attended
+// token i lives in attended block i / P at offset i % P, because every
+// attended block but the last is full.
 // That sequence is cut into at most max_chunks chunks of whole sub-tiles.
 // One workgroup handles one (sequence, KV head, head group, chunk) item: its
 // four wavefronts take the chunk's sub-tiles (SUB tokens: 4 KiB of keys and
@@ -81,27 +83,86 @@ struct SeqWork {
   int32_t L, Cw, k, dense, A, T, CT, nc;
 };
 
+// A span list's first 64 spans stay in registers from the prologue to the
+// first block-id window: per lane (span `lane`), its first logical block, the
+// attended blocks before it and its length (0 past the list). `carry` is the
+// attended-block count they cover. (Holding more rounds measured as register
+// pressure that cost GQA items their second wave per SIMD.) Later spans are
+// requested kSpanBatch rounds of 64 at a time.
+constexpr int kSpanBatch = 4;
+struct SpanRegs {
+  int32_t st, ex, ln;
+  int32_t n, carry;
+};
+
+// (start, end) of span s of sequence b; s must lie in [0, max_blocks].
+__device__ __forceinline__ int2 load_span(const DecodeArgs& a, int b, int s) {
+  const int64_t i = (static_cast<int64_t>(b) * (a.max_blocks + 1) + s) * 2;
+  return *reinterpret_cast<const int2*>(a.spans + i);
+}
+
 // Chunking of sequence b's attended tokens: chunks are whole multiples of
 // `quantum` tokens (one sub-tile per wavefront), at most max_chunks of them.
-__device__ __forceinline__ SeqWork seq_work(const DecodeArgs& a, int b, int quantum) {
+// Every lane of the wave calls it (span lists are scanned across the wave).
+template <bool SPANS>
+__device__ __forceinline__ SeqWork seq_work(const DecodeArgs& a, int b, int quantum,
+                                            SpanRegs& sr) {
   SeqWork w;
-  // The three loads do not depend on each other and are issued together (one
-  // round trip). None sits behind a branch, where it would be waited for
-  // alone: an absent array is replaced by context_lens for the load and its
-  // value masked afterwards.
+  const int lane = threadIdx.x % kWave;
+  // The plan's loads do not depend on each other and are issued together
+  // (one round trip). None sits behind a branch, where it would be waited
+  // for alone: an absent array is replaced by context_lens for the load and
+  // its value masked afterwards. A span list's first rounds are requested in
+  // the same trip (clamped to the row; entries past the count are masked).
   const bool has_flag = a.use_dense != nullptr;
-  const bool has_nsel = a.num_selected != nullptr;
+  constexpr bool by_spans = SPANS;
+  const int32_t* count = by_spans ? a.num_spans : a.num_selected;
+  const bool has_count = count != nullptr;
   w.L = a.context_lens[b];
   const int flag_v = (has_flag ? a.use_dense : a.context_lens)[b];
-  const int nsel_v = (has_nsel ? a.num_selected : a.context_lens)[b];
+  const int count_v = (has_count ? count : a.context_lens)[b];
+  int2 sp0 = make_int2(0, 0);
+  if constexpr (SPANS) sp0 = load_span(a, b, min(lane, a.max_blocks));
   const int flag = has_flag ? flag_v : 0;
-  const int nsel = has_nsel ? nsel_v : 0;
+  const int cnt = has_count ? count_v : 0;
   const int n = (w.L + a.P - 1) / a.P;
   w.Cw = window_start_block(w.L, a.P, a.recent_window);
   w.dense = a.all_dense || flag != 0;
-  w.k = w.dense ? 0 : nsel;
-  w.A = w.dense ? n : w.k + (n - w.Cw);
-  w.T = w.dense ? w.L : w.k * a.P + (w.L - w.Cw * a.P);
+  if (w.dense) {
+    w.k = 0;
+    w.A = n;
+    w.T = w.L;
+  } else if constexpr (SPANS) {
+    // A = total length of the spans; inclusive scans give each span the
+    // attended blocks before it.
+    sr.n = min(cnt, a.max_blocks + 1);
+    sr.ln = lane < sr.n ? sp0.y - sp0.x : 0;
+    const int incl = static_cast<int>(wave_incl_scan(static_cast<uint32_t>(sr.ln)));
+    sr.st = sp0.x;
+    sr.ex = incl - sr.ln;
+    int carry = __builtin_amdgcn_readlane(incl, kWave - 1);
+    sr.carry = carry;
+    for (int s0 = kWave; s0 < sr.n; s0 += kWave * kSpanBatch) {  // lists past 64 spans
+      int2 v[kSpanBatch];
+#pragma unroll
+      for (int i = 0; i < kSpanBatch; ++i) v[i] = load_span(a, b, min(s0 + kWave * i + lane, a.max_blocks));
+#pragma unroll
+      for (int i = 0; i < kSpanBatch; ++i) {
+        const int len = s0 + kWave * i + lane < sr.n ? v[i].y - v[i].x : 0;
+        carry += __builtin_amdgcn_readlane(static_cast<int>(wave_incl_scan(static_cast<uint32_t>(len))),
+                                           kWave - 1);
+      }
+    }
+    w.k = 0;
+    w.A = carry;
+    // every attended block is full except block n - 1, which the window
+    // always holds when it is partial
+    w.T = w.A > 0 ? w.A * a.P - (n * a.P - w.L) : 0;
+  } else {
+    w.k = cnt;
+    w.A = w.k + (n - w.Cw);
+    w.T = w.k * a.P + (w.L - w.Cw * a.P);
+  }
   if (w.T > 0) {
     const int per = (w.T + quantum * a.max_chunks - 1) / (quantum * a.max_chunks);
     w.CT = per * quantum;
@@ -113,7 +174,8 @@ __device__ __forceinline__ SeqWork seq_work(const DecodeArgs& a, int b, int quan
   return w;
 }
 
-// Physical block of attended block `ab` (caller guarantees ab < A).
+// Physical block of attended block `ab` from the selected list or, when
+// dense, the context itself (caller guarantees ab < A).
 __device__ __forceinline__ int32_t attended_phys(const DecodeArgs& a, int b, const SeqWork& w,
                                                  int ab) {
   int32_t logical;
@@ -127,10 +189,68 @@ __device__ __forceinline__ int32_t attended_phys(const DecodeArgs& a, int b, con
   return a.block_table[static_cast<int64_t>(b) * a.max_blocks + logical];
 }
 
+// Span lists: the logical block of attended block gbase + lane. Every span
+// that overlaps [gbase, gbase + 64) writes, into the wave's `marks` row at its
+// first position in that range, the offset between its logical and attended
+// indices; each lane then takes the nearest mark at or below its position.
+constexpr int32_t kNoMark = -2147483647 - 1;
+
+__device__ __forceinline__ void span_mark(int32_t* marks, int gbase, int st, int ex, int len) {
+  if (len > 0 && ex < gbase + kWave && ex + len > gbase) marks[max(ex - gbase, 0)] = st - ex;
+}
+
+// Marks the spans from number s0 on (the attended blocks before s0 are
+// `carry`), BATCH rounds of 64 at a time, until the range is covered, then
+// resolves every lane. Spans past the range mark nothing.
+template <int BATCH>
+__device__ __forceinline__ int span_logical_from(const DecodeArgs& a, int b, int n_spans, int s0,
+                                                 int carry, int gbase, int32_t* marks) {
+  const int lane = threadIdx.x % kWave;
+  for (; s0 < n_spans && carry < gbase + kWave; s0 += kWave * BATCH) {
+    int2 v[BATCH];
+#pragma unroll
+    for (int i = 0; i < BATCH; ++i) v[i] = load_span(a, b, min(s0 + kWave * i + lane, a.max_blocks));
+#pragma unroll
+    for (int i = 0; i < BATCH; ++i) {
+      const int len = s0 + kWave * i + lane < n_spans ? v[i].y - v[i].x : 0;
+      const int incl = static_cast<int>(wave_incl_scan(static_cast<uint32_t>(len)));
+      span_mark(marks, gbase, v[i].x, carry + incl - len, len);
+      carry += __builtin_amdgcn_readlane(incl, kWave - 1);
+    }
+  }
+  wave_lds_sync();
+  const uint64_t below = __ballot(marks[lane] != kNoMark) & (~0ull >> (kWave - 1 - lane));
+  const int src = kWave - 1 - __builtin_clzll(below | 1ull);  // lane 0 is marked while gbase < A
+  return gbase + lane + marks[src];
+}
+
+// First window of an item: span `lane` from registers, later ones in batches.
+__device__ __forceinline__ int span_logical_first(const DecodeArgs& a, int b, const SpanRegs& sr,
+                                                  int gbase, int32_t* marks) {
+  const int lane = threadIdx.x % kWave;
+  marks[lane] = kNoMark;
+  wave_lds_sync();
+  span_mark(marks, gbase, sr.st, sr.ex, sr.ln);
+  return span_logical_from<kSpanBatch>(a, b, sr.n, kWave, sr.carry, gbase, marks);
+}
+
+// A later window (rare: an item longer than 64 blocks): from the list again,
+// one round at a time (this runs inside the streaming loop, where registers
+// are scarce).
+__device__ __forceinline__ int span_logical_again(const DecodeArgs& a, int b, int n_spans,
+                                                  int gbase, int32_t* marks) {
+  const int lane = threadIdx.x % kWave;
+  wave_lds_sync();  // the previous window's marks have been read
+  marks[lane] = kNoMark;
+  wave_lds_sync();
+  return span_logical_from<1>(a, b, n_spans, 0, 0, gbase, marks);
+}
+
 // STREAM: read K/V with non-temporal loads. The launch picks it when every KV
 // head is read by one head group only (nothing to reuse from the caches);
 // when split head groups share a KV head, default loads let them reuse it.
-template <typename T, int D, int GP, bool STREAM>
+// SPANS: the kept blocks come as span lists (a.spans), else as selected lists.
+template <typename T, int D, int GP, bool STREAM, bool SPANS>
 __global__ __launch_bounds__(256) void attend_kernel(DecodeArgs a) {
   using S = DecodeShape<T, D>;
   constexpr int E = S::E;
@@ -142,6 +262,7 @@ __global__ __launch_bounds__(256) void attend_kernel(DecodeArgs a) {
   // for all loads in flight (the prefetched tile included); an LDS read waits
   // for none. (Head-group items measured faster with the register.)
   __shared__ int32_t phys_lds[kDecodeWaves][GP == 1 ? kWave : 1];
+  __shared__ int32_t mark_lds[kDecodeWaves][SPANS ? kWave : 1];  // per-wave window marks
   __shared__ float alpha_lds[kDecodeWaves][16];
   __shared__ float ml_lds[kDecodeWaves][2][16];
   __shared__ float xacc[kDecodeWaves - 1][GP * D];
@@ -191,7 +312,9 @@ __global__ __launch_bounds__(256) void attend_kernel(DecodeArgs a) {
         qop[s] = make_uint4(0, 0, 0, 0);
       }
     }
-    const SeqWork w = seq_work(a, b, QUANTUM);
+    SpanRegs sr;
+    const SeqWork w = seq_work<SPANS>(a, b, QUANTUM, sr);
+    const bool by_spans = SPANS && !w.dense;  // uniform
     if (c >= w.nc) continue;  // uniform over the workgroup
     const int start = c * w.CT;
     const int end = min(w.T, start + w.CT);
@@ -209,7 +332,13 @@ __global__ __launch_bounds__(256) void attend_kernel(DecodeArgs a) {
     int phys_v = 0;
     {
       const int ab = gbase + lane;
-      const int32_t p0 = ab < w.A ? attended_phys(a, b, w, ab) : 0;
+      int32_t p0;
+      if (SPANS && by_spans) {
+        const int logical = span_logical_first(a, b, sr, gbase, mark_lds[wave]);
+        p0 = ab < w.A ? a.block_table[static_cast<int64_t>(b) * a.max_blocks + logical] : 0;
+      } else {
+        p0 = ab < w.A ? attended_phys(a, b, w, ab) : 0;
+      }
       if constexpr (GP == 1) {
         phys_lds[wave][lane] = p0;
         wave_lds_sync();
@@ -252,7 +381,13 @@ __global__ __launch_bounds__(256) void attend_kernel(DecodeArgs a) {
       if (a_last - gbase >= kWave) {
         gbase = i0 / a.P;
         const int ab = gbase + lane;
-        const int32_t p1 = ab < w.A ? attended_phys(a, b, w, ab) : 0;
+        int32_t p1;
+        if (SPANS && by_spans) {
+          const int logical = span_logical_again(a, b, sr.n, gbase, mark_lds[wave]);
+          p1 = ab < w.A ? a.block_table[static_cast<int64_t>(b) * a.max_blocks + logical] : 0;
+        } else {
+          p1 = ab < w.A ? attended_phys(a, b, w, ab) : 0;
+        }
         if constexpr (GP == 1) {
           phys_lds[wave][lane] = p1;
           wave_lds_sync();
@@ -672,16 +807,22 @@ __global__ __launch_bounds__(256) void attend_kernel(DecodeArgs a) {
   }
 }
 
-template <typename T, int D, int GP>
-static hipError_t launch_decode_t(const DecodeArgs& a, int num_wgs, hipStream_t stream) {
+template <typename T, int D, int GP, bool SPANS>
+static hipError_t launch_decode_s(const DecodeArgs& a, int num_wgs, hipStream_t stream) {
   if (a.n_head_groups == 1) {
-    hipLaunchKernelGGL((attend_kernel<T, D, GP, true>), dim3(num_wgs), dim3(kDecodeWaves * kWave),
-                       0, stream, a);
+    hipLaunchKernelGGL((attend_kernel<T, D, GP, true, SPANS>), dim3(num_wgs),
+                       dim3(kDecodeWaves * kWave), 0, stream, a);
   } else {
-    hipLaunchKernelGGL((attend_kernel<T, D, GP, false>), dim3(num_wgs), dim3(kDecodeWaves * kWave),
-                       0, stream, a);
+    hipLaunchKernelGGL((attend_kernel<T, D, GP, false, SPANS>), dim3(num_wgs),
+                       dim3(kDecodeWaves * kWave), 0, stream, a);
   }
   return hipGetLastError();
+}
+
+template <typename T, int D, int GP>
+static hipError_t launch_decode_t(const DecodeArgs& a, int num_wgs, hipStream_t stream) {
+  return a.spans != nullptr ? launch_decode_s<T, D, GP, true>(a, num_wgs, stream)
+                            : launch_decode_s<T, D, GP, false>(a, num_wgs, stream);
 }
 
 template <typename T, int D>

@@ -64,8 +64,10 @@ struct DecodeArgs {
   const void* v_pool;
   const int32_t* block_table;
   const int32_t* context_lens;
-  const int32_t* selected;      // NULL when every sequence is dense
-  const int32_t* num_selected;  // NULL when every sequence is dense
+  const int32_t* selected;      // NULL when every sequence is dense or spans are given
+  const int32_t* num_selected;  // NULL when every sequence is dense or spans are given
+  const int32_t* spans;         // [B][max_blocks + 1][2]; NULL: use `selected`
+  const int32_t* num_spans;     // [B]; with `spans`
   const int32_t* use_dense;     // may be NULL
   float* out;
   float* lse;                   // may be NULL

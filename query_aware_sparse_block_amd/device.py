@@ -108,10 +108,21 @@ def score_topk(dc: DeviceCase, buf: StepBuffers, params=None, stream=None):
                          buf.num_spans, buf.use_dense, buf.workspace, stream)
 
 
-def sparse_decode(dc: DeviceCase, buf: StepBuffers, params=None, scale=0.0, stream=None):
+def sparse_decode(dc: DeviceCase, buf: StepBuffers, params=None, scale=0.0, stream=None,
+                  form="spans", out=None):
+    """Attention over the kept blocks of kvsp_score_topk's outputs in `buf`,
+    handed over as its span list (form="spans") or its selected list
+    (form="selected"); into buf.out / buf.lse unless `out` is given."""
+    if form == "spans":
+        kept = (buf.spans, buf.num_spans, None, None)
+    elif form == "selected":
+        kept = (None, None, buf.selected, buf.num_selected)
+    else:
+        raise ValueError(f"unknown form {form!r}")
     kvsp.kvsp_sparse_decode(dc.layout, params or dc.params, dc.q, dc.k_pool, dc.v_pool,
-                            dc.block_table, dc.ctx_lens, buf.selected, buf.num_selected,
-                            buf.use_dense, scale, buf.out, buf.lse, buf.workspace, stream)
+                            dc.block_table, dc.ctx_lens, *kept, buf.use_dense, scale,
+                            buf.out if out is None else out, buf.lse if out is None else None,
+                            buf.workspace, stream)
 
 
 def dense_decode(dc: DeviceCase, buf: StepBuffers, scale=0.0, stream=None):

@@ -83,8 +83,8 @@ def library() -> ctypes.CDLL:
         L.kvsp_score_topk.restype = ctypes.c_int
         L.kvsp_score_topk.argtypes = [LP, SP, P, P, P, P, P, P, P, P, P, P, P, sz, P]
         L.kvsp_sparse_decode.restype = ctypes.c_int
-        L.kvsp_sparse_decode.argtypes = [LP, SP, P, P, P, P, P, P, P, P, ctypes.c_float, P, P, P,
-                                         sz, P]
+        L.kvsp_sparse_decode.argtypes = [LP, SP, P, P, P, P, P, P, P, P, P, P, ctypes.c_float, P,
+                                         P, P, sz, P]
         L.kvsp_dense_decode.restype = ctypes.c_int
         L.kvsp_dense_decode.argtypes = [LP, P, P, P, P, P, ctypes.c_float, P, P, P, sz, P]
         DP = ctypes.POINTER(kvsp_dkv_params)
@@ -247,14 +247,18 @@ def kvsp_score_topk(layout, params: SelectParams, q, summaries, block_table, con
 
 
 def kvsp_sparse_decode(layout, params: SelectParams, q, k_pool, v_pool, block_table, context_lens,
-                       selected, num_selected, use_dense, scale, out, lse, workspace, stream=None):
+                       spans, num_spans, selected, num_selected, use_dense, scale, out, lse,
+                       workspace, stream=None):
+    """The kept blocks come as (spans, num_spans) or as (selected,
+    num_selected); pass None for the other pair."""
     p = params.c()
     z = _Sizes(layout)
     _check("kvsp_sparse_decode", library().kvsp_sparse_decode(
         ctypes.byref(layout), ctypes.byref(p), _ptr(q, "q", z.q, z.cache_dtype),
         _ptr(k_pool, "k_pool", z.pool, z.cache_dtype), _ptr(v_pool, "v_pool", z.pool, z.cache_dtype),
         _ptr(block_table, "block_table", z.table, I32),
-        _ptr(context_lens, "context_lens", z.per_seq, I32), _ptr(selected, "selected", z.row, I32),
+        _ptr(context_lens, "context_lens", z.per_seq, I32), _ptr(spans, "spans", z.spans, I32),
+        _ptr(num_spans, "num_spans", z.per_seq, I32), _ptr(selected, "selected", z.row, I32),
         _ptr(num_selected, "num_selected", z.per_seq, I32), _ptr(use_dense, "use_dense", z.per_seq, I32),
         ctypes.c_float(scale), _ptr(out, "out", z.out, F32), _ptr(lse, "lse", z.lse, F32),
         _ptr(workspace, "workspace"), workspace.numel(), _stream(stream)))

@@ -17,6 +17,8 @@ Bars (written here once, used by every parity test):
   * selection against the GPU's own float32 scores: exactly their k largest,
     equal scores (+0 and -0 alike) taken in ascending block order;
   * spans, counts and the dense flag: exact (spans of the GPU's own set);
+  * the decode given the span list and given the selected list: the same
+    outputs bit for bit (every sparse run does both);
   * outputs: max-abs error <= 2e-3 for fp16/bf16 caches and <= 1e-5 for fp32
     caches (float32 accumulation); lse within 1e-4.
 """
@@ -68,7 +70,12 @@ def run_gpu(case: wl.Case, *, dense_api=False, params=None):
     else:
         dev.score_topk(dc, buf, params)
         dev.sparse_decode(dc, buf, params)
+        # the same kept blocks handed over as the selected list: bit-identical
+        out_sel = torch.full_like(buf.out, float("nan"))
+        dev.sparse_decode(dc, buf, params, form="selected", out=out_sel)
     torch.cuda.synchronize()
+    if not dense_api:
+        assert torch.equal(out_sel, buf.out), "span and selected forms of the decode differ"
     res = {k: getattr(buf, k).cpu().numpy() for k in
            ("summaries", "scores", "selected", "num_selected", "spans", "num_spans", "use_dense",
             "out", "lse")}

@@ -39,7 +39,7 @@ def test_library_exports_every_declared_entry_point():
             "kvsp_abi_version"} <= set(names)
     for name in names:
         assert hasattr(lib, name), name
-    assert lib.kvsp_abi_version() == 1
+    assert lib.kvsp_abi_version() == 2
 
 
 def test_status_strings():
@@ -80,7 +80,7 @@ def test_bad_layout_rejected(over, code):
     assert lib.kvsp_build_summaries(ctypes.byref(lay), None, None, None, None, None) == code
     assert lib.kvsp_append_kv(ctypes.byref(lay), *([None] * 7), None) == code
     assert lib.kvsp_score_topk(ctypes.byref(lay), ctypes.byref(par), *nul, None, 0, None) == code
-    assert lib.kvsp_sparse_decode(ctypes.byref(lay), ctypes.byref(par), *([None] * 8),
+    assert lib.kvsp_sparse_decode(ctypes.byref(lay), ctypes.byref(par), *([None] * 10),
                                   ctypes.c_float(0), None, None, None, 0, None) == code
     assert lib.kvsp_dense_decode(ctypes.byref(lay), *([None] * 5), ctypes.c_float(0), None,
                                  None, None, 0, None) == code
@@ -95,8 +95,9 @@ def test_bad_params_rejected(over):
     lay, par = _layout(), _params(**over)
     assert lib.kvsp_score_topk(ctypes.byref(lay), ctypes.byref(par), *([FAKE] * 10), FAKE,
                                1 << 30, None) == -1
-    assert lib.kvsp_sparse_decode(ctypes.byref(lay), ctypes.byref(par), *([FAKE] * 8),
-                                  ctypes.c_float(0), FAKE, FAKE, FAKE, 1 << 30, None) == -1
+    assert lib.kvsp_sparse_decode(ctypes.byref(lay), ctypes.byref(par), *([FAKE] * 7),
+                                  None, None, FAKE, ctypes.c_float(0), FAKE, FAKE, FAKE, 1 << 30,
+                                  None) == -1
 
 
 def test_null_pointers_rejected():
@@ -112,8 +113,24 @@ def test_null_pointers_rejected():
     assert lib.kvsp_score_topk(ctypes.byref(lay), ctypes.byref(par), *args, FAKE, 1 << 30,
                                None) == -1
     assert lib.kvsp_sparse_decode(ctypes.byref(lay), ctypes.byref(par), FAKE, FAKE, None,
-                                  *([FAKE] * 5), ctypes.c_float(0), FAKE, FAKE, FAKE, 1 << 30,
-                                  None) == -1
+                                  *([FAKE] * 4), None, None, FAKE, ctypes.c_float(0), FAKE, FAKE,
+                                  FAKE, 1 << 30, None) == -1
+
+
+@pytest.mark.parametrize("kept", [
+    (FAKE, FAKE, FAKE, FAKE),   # both forms
+    (None, None, None, None),   # neither
+    (FAKE, None, None, None),   # a span list without its counts
+    (None, FAKE, None, None),
+    (None, None, FAKE, None),   # a selected list without its counts
+    (None, None, None, FAKE),
+    (FAKE, None, FAKE, None),
+])
+def test_sparse_decode_takes_exactly_one_form_of_the_kept_blocks(kept):
+    lib = kvsp.library()
+    lay, par = _layout(), _params()
+    assert lib.kvsp_sparse_decode(ctypes.byref(lay), ctypes.byref(par), *([FAKE] * 5), *kept,
+                                  FAKE, ctypes.c_float(0), FAKE, FAKE, FAKE, 1 << 30, None) == -1
     assert lib.kvsp_dense_decode(None, *([FAKE] * 5), ctypes.c_float(0), FAKE, FAKE, FAKE, 1 << 30,
                                  None) == -1
 
@@ -123,8 +140,9 @@ def test_small_workspace_rejected():
     lib = kvsp.library()
     lay, par = _layout(), _params()
     need = lib.kvsp_workspace_bytes(ctypes.byref(lay), ctypes.byref(par))
-    assert lib.kvsp_sparse_decode(ctypes.byref(lay), ctypes.byref(par), *([FAKE] * 8),
-                                  ctypes.c_float(0), FAKE, FAKE, FAKE, need - 1, None) == -3
+    assert lib.kvsp_sparse_decode(ctypes.byref(lay), ctypes.byref(par), *([FAKE] * 7),
+                                  None, None, FAKE, ctypes.c_float(0), FAKE, FAKE, FAKE, need - 1,
+                                  None) == -3
     assert lib.kvsp_dense_decode(ctypes.byref(lay), *([FAKE] * 5), ctypes.c_float(0), FAKE, FAKE,
                                  None, need, None) == -3
     # scores == NULL needs the workspace

@@ -293,7 +293,8 @@ def test_optional_outputs_may_be_null():
                          None, sel2, nsel2, spans2, nsp2, dense2, buf.workspace)
     out2 = torch.zeros_like(buf.out)
     kvsp.kvsp_sparse_decode(dc.layout, dc.params, dc.q, dc.k_pool, dc.v_pool, dc.block_table,
-                            dc.ctx_lens, sel2, nsel2, dense2, 0.0, out2, None, buf.workspace)
+                            dc.ctx_lens, spans2, nsp2, None, None, dense2, 0.0, out2, None,
+                            buf.workspace)
     torch.cuda.synchronize()
     assert torch.equal(sel2, buf.selected) and torch.equal(nsel2, buf.num_selected)
     assert torch.equal(spans2, buf.spans) and torch.equal(nsp2, buf.num_spans)
@@ -363,3 +364,18 @@ def test_one_head_items_longer_than_the_id_window(keep):
             outs, _ = H.oracle_attention_on(case, b, [], True)
             for h, o in outs.items():
                 assert np.max(np.abs(gpu["out"][b, h] - o)) <= 2e-3, (b, h)
+
+
+@pytest.mark.parametrize("Hq,Hkv", [(4, 4), (8, 4)])
+def test_long_span_lists_and_long_items(Hq, Hkv):
+    # keep 3/8 of 1535 candidates: about 360 spans per sequence, more than the
+    # 256 the decode keeps in registers, and 64 sequences x 4 KV heads make
+    # one chunk per group, so each item walks about 580 attended blocks and
+    # refreshes its window of block ids from the span list many times; the
+    # selected-list form must give the same bits (run_gpu checks it)
+    case = wl.make_case(f"long-spans-{Hq}-{Hkv}", seed=9400 + Hq, B=64, Hq=Hq, Hkv=Hkv, D=64,
+                        P=16, dtype="bf16", ctx_lens=[24576] * 64, shuffle=True,
+                        keep_num=3, keep_den=8, keep_floor=1, recent_window=16)
+    H.note(f"[long spans] Hq={Hq} Hkv={Hkv}")
+    gpu, r_or = H.full_parity(case, check_all_summaries=False)
+    assert int(gpu["num_spans"].min()) > 256
