@@ -84,7 +84,8 @@ typedef enum {
   KVSP_ERR_INVALID_ARG = -1,
   KVSP_ERR_UNSUPPORTED = -2,
   KVSP_ERR_WORKSPACE = -3,
-  KVSP_ERR_HIP = -4
+  KVSP_ERR_HIP = -4,
+  KVSP_ERR_TOO_LARGE = -5 /* beyond the static scratch of kvsp_sparse_decode_noalloc */
 } kvsp_status;
 
 typedef enum { KVSP_F32 = 0, KVSP_F16 = 1, KVSP_BF16 = 2 } kvsp_dtype;
@@ -252,6 +253,32 @@ kvsp_status kvsp_sparse_decode(const kvsp_layout* layout, const kvsp_select_para
                                const int32_t* selected, const int32_t* num_selected,
                                const int32_t* use_dense, float scale, float* out, float* lse,
                                void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* kvsp_sparse_decode for callers that cannot allocate or pass device memory
+ * of their own for scratch: code under HIP graph capture, tight serving
+ * loops, and harnesses that forbid allocation. Same arguments, results (bit
+ * for bit) and kernels as kvsp_sparse_decode, without the workspace: the
+ * completion counters and split-KV partials live in a static device array of
+ * the library (8 MiB per device that calls it, held until the process ends).
+ * It allocates nothing and never calls hipMalloc or hipFree. The first call
+ * on a device (the current device) looks the array up and zeroes its counter
+ * region with a fill kernel enqueued on `stream`; a first call under stream
+ * capture records that kernel in the graph and the next eager call enqueues
+ * it again. Every call leaves the counters at zero.
+ * Every call on one device shares that device's array, so calls that overlap
+ * in time on one device (on different streams, or concurrent replays of
+ * graphs holding this call) race and give undefined results; serialise them.
+ * Errors: as kvsp_sparse_decode (no workspace error), plus KVSP_ERR_TOO_LARGE
+ * when the layout has more than 16384 (sequence, KV head, head group)
+ * counters or its split-KV partials exceed the array; checked on the host
+ * before anything is enqueued. */
+kvsp_status kvsp_sparse_decode_noalloc(const kvsp_layout* layout, const kvsp_select_params* params,
+                                       const void* q, const void* k_pool, const void* v_pool,
+                                       const int32_t* block_table, const int32_t* context_lens,
+                                       const int32_t* spans, const int32_t* num_spans,
+                                       const int32_t* selected, const int32_t* num_selected,
+                                       const int32_t* use_dense, float scale, float* out,
+                                       float* lse, hipStream_t stream);
 
 /* Step 5 on its own ("KV cache offloading", "Why the cache leaves the GPU":
  * dense decode reads every key and value): attention of every query head

@@ -5,6 +5,7 @@
 #include <stddef.h>
 #include <algorithm>
 #include <cmath>
+#include <mutex>
 #include <stdint.h>
 
 #include "kvsp.h"
@@ -220,6 +221,78 @@ kvsp_status run_decode(const kvsp_layout* layout, const kvsp_select_params* para
                                lse, workspace_scratch(l, workspace), stream);
 }
 
+// ---- the decode for callers that cannot allocate --------------------------------
+// Its counters and partials live in `scratch`, a file-scope device array (one
+// copy per device, held until the process ends). The completion counters
+// have a fixed region at its start, so a later call's counters never overlap
+// an earlier call's partials; the kernels leave them at zero after every
+// call, and a fill kernel zeroes them once per device at set-up. Partials
+// follow at a fixed offset; they are needed only when a group is split into
+// several chunks.
+constexpr size_t kStaticScratchBytes = size_t(8) << 20;
+constexpr size_t kStaticCounterBytes = size_t(64) << 10;  // 16384 groups
+constexpr int kMaxDevices = 64;
+
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+
+struct DeviceScratch {
+  char* ptr = nullptr;   // the device address of `scratch` on this device
+  bool cleared = false;  // counters zeroed by an eager (not captured) fill
+};
+std::mutex g_scratch_mutex;
+DeviceScratch g_scratch[kMaxDevices];
+
+__global__ void zero_words(int32_t* p, int n) {
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) p[i] = 0;
+}
+
+// Bytes of `scratch` a decode of this layout uses, or 0 if it does not fit.
+size_t static_decode_bytes(const kvsp_layout& l) {
+  const DecodeGeometry g = decode_geometry(l);
+  const size_t groups = static_cast<size_t>(l.batch) * l.num_kv_heads * g.n_head_groups;
+  if (groups * sizeof(int32_t) > kStaticCounterBytes) return 0;
+  size_t need = kStaticCounterBytes;
+  if (g.max_chunks > 1) {
+    const size_t slots = static_cast<size_t>(g.total_items);
+    need += align_up(slots * g.gp * l.head_dim * sizeof(float)) + align_up(slots * g.gp * 2 * sizeof(float));
+  }
+  return need <= kStaticScratchBytes ? need : 0;
+}
+
+// The current device's copy of `scratch`, its counters zeroed on `stream`
+// ahead of first use.
+kvsp_status static_scratch(const kvsp_layout& l, hipStream_t stream, DecodeScratch* out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return KVSP_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return KVSP_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  DeviceScratch& d = g_scratch[dev];
+  if (d.ptr == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr)
+      return KVSP_ERR_HIP;
+    d.ptr = static_cast<char*>(p);
+  }
+  if (!d.cleared) {
+    // A fill kernel, not a memset, so that a captured first call records a
+    // kernel node; only an eager fill counts as done.
+    hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(stream, &cap) != hipSuccess) return KVSP_ERR_HIP;
+    constexpr int words = static_cast<int>(kStaticCounterBytes / sizeof(int32_t));
+    hipLaunchKernelGGL(zero_words, dim3(words / 256), dim3(256), 0, stream,
+                       reinterpret_cast<int32_t*>(d.ptr), words);
+    if (hipGetLastError() != hipSuccess) return KVSP_ERR_HIP;
+    if (cap == hipStreamCaptureStatusNone) d.cleared = true;
+  }
+  const DecodeGeometry g = decode_geometry(l);
+  const size_t slots = static_cast<size_t>(g.total_items);
+  char* acc = d.ptr + kStaticCounterBytes;
+  out->counters = reinterpret_cast<int32_t*>(d.ptr);
+  out->part_acc = reinterpret_cast<float*>(acc);
+  out->part_ml = reinterpret_cast<float*>(acc + align_up(slots * g.gp * l.head_dim * sizeof(float)));
+  return KVSP_OK;
+}
+
 // ---- DKV variant ------------------------------------------------------------------
 
 constexpr int kDkvRank = 32;
@@ -353,6 +426,7 @@ const char* kvsp_status_string(kvsp_status s) {
     case KVSP_ERR_UNSUPPORTED: return "unsupported shape or dtype";
     case KVSP_ERR_WORKSPACE: return "workspace missing or too small";
     case KVSP_ERR_HIP: return "HIP launch failed";
+    case KVSP_ERR_TOO_LARGE: return "layout needs more than the static scratch of kvsp_sparse_decode_noalloc";
   }
   return "unknown status";
 }
@@ -499,6 +573,24 @@ kvsp_status kvsp_sparse_decode(const kvsp_layout* layout, const kvsp_select_para
   return run_decode(layout, params, false, q, k_pool, v_pool, block_table, context_lens, spans,
                     num_spans, selected, num_selected, use_dense, scale, out, lse, workspace,
                     workspace_bytes, stream);
+}
+
+kvsp_status kvsp_sparse_decode_noalloc(const kvsp_layout* layout, const kvsp_select_params* params,
+                                       const void* q, const void* k_pool, const void* v_pool,
+                                       const int32_t* block_table, const int32_t* context_lens,
+                                       const int32_t* spans, const int32_t* num_spans,
+                                       const int32_t* selected, const int32_t* num_selected,
+                                       const int32_t* use_dense, float scale, float* out,
+                                       float* lse, hipStream_t stream) {
+  kvsp_status st = check_decode(layout, params, false, q, k_pool, v_pool, block_table,
+                                context_lens, spans, num_spans, selected, num_selected, out);
+  if (st != KVSP_OK) return st;
+  if (static_decode_bytes(*layout) == 0) return KVSP_ERR_TOO_LARGE;
+  DecodeScratch scr;
+  if ((st = static_scratch(*layout, stream, &scr)) != KVSP_OK) return st;
+  return launch_checked_decode(*layout, params, false, q, k_pool, v_pool, block_table, context_lens,
+                               spans, num_spans, selected, num_selected, use_dense, scale, out,
+                               lse, scr, stream);
 }
 
 kvsp_status kvsp_dense_decode(const kvsp_layout* layout, const void* q, const void* k_pool,

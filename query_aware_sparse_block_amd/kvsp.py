@@ -23,7 +23,7 @@ HEADER_PATH = os.path.join(os.path.dirname(_PKG), "include", "kvsp.h")
 
 KVSP_OK = 0
 STATUS_NAMES = {0: "KVSP_OK", -1: "KVSP_ERR_INVALID_ARG", -2: "KVSP_ERR_UNSUPPORTED",
-                -3: "KVSP_ERR_WORKSPACE", -4: "KVSP_ERR_HIP"}
+                -3: "KVSP_ERR_WORKSPACE", -4: "KVSP_ERR_HIP", -5: "KVSP_ERR_TOO_LARGE"}
 DTYPE_CODES = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}
 
 
@@ -85,6 +85,9 @@ def library() -> ctypes.CDLL:
         L.kvsp_sparse_decode.restype = ctypes.c_int
         L.kvsp_sparse_decode.argtypes = [LP, SP, P, P, P, P, P, P, P, P, P, P, ctypes.c_float, P,
                                          P, P, sz, P]
+        L.kvsp_sparse_decode_noalloc.restype = ctypes.c_int
+        L.kvsp_sparse_decode_noalloc.argtypes = [LP, SP, P, P, P, P, P, P, P, P, P, P,
+                                                 ctypes.c_float, P, P, P]
         L.kvsp_dense_decode.restype = ctypes.c_int
         L.kvsp_dense_decode.argtypes = [LP, P, P, P, P, P, ctypes.c_float, P, P, P, sz, P]
         DP = ctypes.POINTER(kvsp_dkv_params)
@@ -262,6 +265,24 @@ def kvsp_sparse_decode(layout, params: SelectParams, q, k_pool, v_pool, block_ta
         _ptr(num_selected, "num_selected", z.per_seq, I32), _ptr(use_dense, "use_dense", z.per_seq, I32),
         ctypes.c_float(scale), _ptr(out, "out", z.out, F32), _ptr(lse, "lse", z.lse, F32),
         _ptr(workspace, "workspace"), workspace.numel(), _stream(stream)))
+
+
+def kvsp_sparse_decode_noalloc(layout, params: SelectParams, q, k_pool, v_pool, block_table,
+                               context_lens, spans, num_spans, selected, num_selected, use_dense,
+                               scale, out, lse, stream=None):
+    """kvsp_sparse_decode without a workspace: the library's static device
+    scratch holds its counters and partials (see kvsp.h)."""
+    p = params.c()
+    z = _Sizes(layout)
+    _check("kvsp_sparse_decode_noalloc", library().kvsp_sparse_decode_noalloc(
+        ctypes.byref(layout), ctypes.byref(p), _ptr(q, "q", z.q, z.cache_dtype),
+        _ptr(k_pool, "k_pool", z.pool, z.cache_dtype), _ptr(v_pool, "v_pool", z.pool, z.cache_dtype),
+        _ptr(block_table, "block_table", z.table, I32),
+        _ptr(context_lens, "context_lens", z.per_seq, I32), _ptr(spans, "spans", z.spans, I32),
+        _ptr(num_spans, "num_spans", z.per_seq, I32), _ptr(selected, "selected", z.row, I32),
+        _ptr(num_selected, "num_selected", z.per_seq, I32), _ptr(use_dense, "use_dense", z.per_seq, I32),
+        ctypes.c_float(scale), _ptr(out, "out", z.out, F32), _ptr(lse, "lse", z.lse, F32),
+        _stream(stream)))
 
 
 def kvsp_dense_decode(layout, q, k_pool, v_pool, block_table, context_lens, scale, out, lse,

@@ -290,3 +290,29 @@ def test_budget_controller_rejects_bad_arguments_and_writes_nothing():
                                       None, ctypes.byref(num)) == 0
     with pytest.raises(kvsp.KvspError):
         kvsp.kvsp_budget_keep_ratio(_layout(), kvsp.BudgetModel(0.0, 1e14, 4096), 1024)
+
+
+def test_noalloc_decode_checks_arguments_before_any_device_call():
+    # the allocation-free decode rejects what kvsp_sparse_decode rejects, and
+    # layouts beyond its static scratch, before it looks the scratch up
+    lib = kvsp.library()
+    lay, par = _layout(), _params()
+    kept = [FAKE, FAKE, None, None]
+    assert lib.kvsp_sparse_decode_noalloc(ctypes.byref(lay), ctypes.byref(par), *([FAKE] * 5),
+                                          FAKE, FAKE, FAKE, FAKE, FAKE, ctypes.c_float(0), FAKE,
+                                          FAKE, None) == -1  # both forms of the kept blocks
+    assert lib.kvsp_sparse_decode_noalloc(ctypes.byref(lay), ctypes.byref(par), FAKE, None,
+                                          *([FAKE] * 3), *kept, FAKE, ctypes.c_float(0), FAKE,
+                                          FAKE, None) == -1  # no K pool
+    assert lib.kvsp_sparse_decode_noalloc(ctypes.byref(_layout(head_dim=96)), ctypes.byref(par),
+                                          *([FAKE] * 5), *kept, FAKE, ctypes.c_float(0), FAKE,
+                                          FAKE, None) == -2
+    assert lib.kvsp_sparse_decode_noalloc(ctypes.byref(lay), ctypes.byref(_params(keep_den=0)),
+                                          *([FAKE] * 5), *kept, FAKE, ctypes.c_float(0), FAKE,
+                                          FAKE, None) == -1
+    # 8192 sequences x 8 KV heads: 65536 completion counters, beyond the 16384
+    # the static scratch holds
+    big = _layout(batch=8192, num_kv_heads=8, num_q_heads=32)
+    assert lib.kvsp_sparse_decode_noalloc(ctypes.byref(big), ctypes.byref(par), *([FAKE] * 5),
+                                          *kept, FAKE, ctypes.c_float(0), FAKE, FAKE, None) == -5
+    assert "static scratch" in kvsp.status_string(-5)
