@@ -6,13 +6,11 @@ plain-copy reference the counters are scaled by.
       known-size reference for FETCH_SIZE / WRITE_SIZE scaling.
   python -m query_aware_sparse_block_amd.profiling stats STATS_CSV OUT_TXT "COMMAND"
       Text summary of a `rocprofv3 --kernel-trace --stats` kernel_stats.csv.
-  python -m query_aware_sparse_block_amd.profiling traffic WORKLOAD FETCH_CSV WRITE_CSV \
-          COPY_FETCH_CSV COPY_WRITE_CSV OUT_TXT "COMMANDS"
-      Per-launch HBM bytes of the decode kernel from two --pmc runs, scaled by
-      the copy reference, stamped with the digest of the decode sources.
-  python -m query_aware_sparse_block_amd.profiling dkv-traffic WORKLOAD FETCH_CSV WRITE_CSV \
-          COPY_FETCH_CSV COPY_WRITE_CSV OUT_TXT "COMMANDS"
-      The same for the DKV decode kernel (dkv_attend_kernel) and its sources.
+  python -m query_aware_sparse_block_amd.profiling traffic KERNEL WORKLOAD FETCH_CSV WRITE_CSV \
+          COPY_FETCH_CSV COPY_WRITE_CSV "COMMANDS"
+      Per-launch HBM bytes of KERNEL (attend, score or dkv_attend) from two
+      --pmc runs, scaled by the copy reference, stamped with the digest of the
+      kernel's sources; written to profiles/traffic_KERNEL_WORKLOAD.txt.
 """
 
 from __future__ import annotations
@@ -26,18 +24,27 @@ import sys
 _PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(_PKG)
 PROFILES = os.path.join(ROOT, "profiles")
-TRAFFIC_FILE = os.path.join(PROFILES, "attend_traffic.txt")
-DKV_TRAFFIC_FILE = os.path.join(PROFILES, "dkv_attend_traffic.txt")
 DECODE_SOURCES = ["csrc/kvsp_decode.hip", "csrc/kvsp_device.h", "csrc/kvsp_api.hip",
+                  "csrc/kvsp_internal.h"]
+SELECT_SOURCES = ["csrc/kvsp_select.hip", "csrc/kvsp_device.h", "csrc/kvsp_api.hip",
                   "csrc/kvsp_internal.h"]
 DKV_SOURCES = ["csrc/kvsp_dkv.hip", "csrc/kvsp_device.h", "csrc/kvsp_api.hip",
                "csrc/kvsp_internal.h"]
 COPY_BYTES = 1 << 30
-# Kernel-name prefixes as rocprofv3 prints them (the DKV kernel's name also
-# contains "attend_kernel", so the main one is matched with its namespace).
-DECODE_KERNEL = "kvsp::attend_kernel<"
-DKV_KERNEL = "dkv_attend_kernel<"
+# kernel key -> (name prefixes as rocprofv3 prints them, sources, title). The
+# DKV kernel's name also contains "attend_kernel", so the main one is matched
+# with its namespace.
+KERNELS = {
+    "attend": (["kvsp::attend_kernel<"], DECODE_SOURCES, "the decode kernel (attend_kernel)"),
+    "score": (["kvsp::score_select_kernel<", "kvsp::score_kernel<"], SELECT_SOURCES,
+              "the scoring kernel (score_select_kernel / score_kernel)"),
+    "dkv_attend": (["dkv_attend_kernel<"], DKV_SOURCES, "the DKV decode kernel (dkv_attend_kernel)"),
+}
 COPY_KERNEL = "__amd_rocclr_copyBuffer"
+
+
+def traffic_path(kernel: str, workload: str) -> str:
+    return os.path.join(PROFILES, f"traffic_{kernel}_{workload.replace('/', '_')}.txt")
 
 
 def source_digest(sources) -> str:
@@ -46,10 +53,6 @@ def source_digest(sources) -> str:
         with open(os.path.join(_PKG, rel), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
-
-
-def decode_source_digest() -> str:
-    return source_digest(DECODE_SOURCES)
 
 
 def copy_probe():
@@ -69,10 +72,11 @@ def _rows(path):
         return list(csv.DictReader(f))
 
 
-def counter_per_dispatch(path, kernel_substr, counter):
-    vals = [float(r["Counter_Value"]) for r in _rows(path)
-            if kernel_substr in r["Kernel_Name"] and r["Counter_Name"] == counter]
-    return vals
+def counter_per_dispatch(path, kernel_prefixes, counter):
+    if isinstance(kernel_prefixes, str):
+        kernel_prefixes = [kernel_prefixes]
+    return [float(r["Counter_Value"]) for r in _rows(path)
+            if any(k in r["Kernel_Name"] for k in kernel_prefixes) and r["Counter_Name"] == counter]
 
 
 def copy_scale(copy_csv, counter):
@@ -83,13 +87,13 @@ def copy_scale(copy_csv, counter):
     return COPY_BYTES / max(vals)
 
 
-def write_traffic(workload, fetch_csv, write_csv, copy_fetch_csv, copy_write_csv, out_txt,
-                  commands, kernel=DECODE_KERNEL, sources=DECODE_SOURCES,
-                  title="the decode kernel (attend_kernel)"):
-    fetch = counter_per_dispatch(fetch_csv, kernel, "FETCH_SIZE")
-    write = counter_per_dispatch(write_csv, kernel, "WRITE_SIZE")
+def write_traffic(kernel, workload, fetch_csv, write_csv, copy_fetch_csv, copy_write_csv,
+                  commands):
+    prefixes, sources, title = KERNELS[kernel]
+    fetch = counter_per_dispatch(fetch_csv, prefixes, "FETCH_SIZE")
+    write = counter_per_dispatch(write_csv, prefixes, "WRITE_SIZE")
     if not fetch or not write:
-        raise RuntimeError(f"no {kernel} dispatch in {fetch_csv} / {write_csv}")
+        raise RuntimeError(f"no {prefixes} dispatch in {fetch_csv} / {write_csv}")
     fs = copy_scale(copy_fetch_csv, "FETCH_SIZE")
     ws = copy_scale(copy_write_csv, "WRITE_SIZE")
     f_med = statistics.median(fetch)
@@ -97,24 +101,29 @@ def write_traffic(workload, fetch_csv, write_csv, copy_fetch_csv, copy_write_csv
     traffic = f_med * fs + w_med * ws
     lines = [
         f"# HBM traffic of {title}, per launch",
+        f"kernel = {kernel}",
         f"workload = {workload}",
-        f"decode_source_digest = {source_digest(sources)}",
-        f"fetch_size_median = {f_med:.1f}",
-        f"write_size_median = {w_med:.1f}",
+        f"source_digest = {source_digest(sources)}",
+        f"fetch_size_median_kib = {f_med:.1f}",
+        f"write_size_median_kib = {w_med:.1f}",
         f"dispatches = {len(fetch)} / {len(write)}",
         f"fetch_scale_bytes_per_unit = {fs:.4f}",
         f"write_scale_bytes_per_unit = {ws:.4f}",
+        f"bytes_read = {f_med * fs:.0f}",
+        f"bytes_written = {w_med * ws:.0f}",
         f"traffic_bytes = {traffic:.0f}",
         f"commands = {commands}",
     ]
+    out_txt = traffic_path(kernel, workload)
     with open(out_txt, "w") as f:
         f.write("\n".join(lines) + "\n")
     print("\n".join(lines))
 
 
-def recorded_traffic(workload, path=TRAFFIC_FILE, sources=DECODE_SOURCES):
-    """Traffic bytes recorded for `workload`, or None when absent or when the
-    kernel's sources changed since the counters were taken."""
+def recorded_traffic(workload, kernel="attend"):
+    """Traffic bytes recorded for `kernel` on `workload`, or None when absent
+    or when the kernel's sources changed since the counters were taken."""
+    path = traffic_path(kernel, workload)
     if not os.path.exists(path):
         return None
     kv = {}
@@ -122,7 +131,8 @@ def recorded_traffic(workload, path=TRAFFIC_FILE, sources=DECODE_SOURCES):
         if "=" in line and not line.startswith("#"):
             k, v = line.split("=", 1)
             kv[k.strip()] = v.strip()
-    if kv.get("workload") != workload or kv.get("decode_source_digest") != source_digest(sources):
+    sources = KERNELS[kernel][1]
+    if kv.get("workload") != workload or kv.get("source_digest") != source_digest(sources):
         return None
     return float(kv["traffic_bytes"])
 
@@ -155,9 +165,6 @@ def main(argv):
         write_stats(argv[1], argv[2], argv[3])
     elif cmd == "traffic":
         write_traffic(*argv[1:8])
-    elif cmd == "dkv-traffic":
-        write_traffic(*argv[1:8], kernel=DKV_KERNEL, sources=DKV_SOURCES,
-                      title="the DKV decode kernel (dkv_attend_kernel)")
     else:
         print(__doc__)
         return 2
