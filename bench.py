@@ -201,6 +201,7 @@ def dkv_record_payload(case, n_resid):
 
 def bench_dkv(args, capture, timed):
     """The DKV variant on its own workload (see the module docstring)."""
+    import numpy as np
     import torch
 
     from query_aware_sparse_block_amd import device as dev
@@ -230,6 +231,12 @@ def bench_dkv(args, capture, timed):
     t1.record()
     torch.cuda.synchronize()
     comp_us = t0.elapsed_time(t1) / n_comp * 1e3
+    # subspace-iteration rounds the codec chose per record (older blocks only)
+    lay = wl.dkv_record_layout(case.D, case.P, wl.ELEM_BYTES[case.dtype], n_resid)
+    C0 = max(0, int(case.ctx_lens[0]) - case.recent_window) // case.P
+    older = dc0.block_table[0, :C0].long()
+    rounds = recs0[older][:, :, lay["rounds"]:lay["rounds"] + 4].contiguous().view(torch.int32)
+    rounds = rounds.reshape(-1).cpu().numpy()
 
     # replicas of pool, summaries and records, rotated per step (cache hygiene
     # as for the headline workload)
@@ -289,7 +296,13 @@ def bench_dkv(args, capture, timed):
                                  "FETCH_SIZE and WRITE_SIZE per dkv_attend_kernel launch, scaled "
                                  "by a plain copy; null if the DKV decode sources changed)",
         "compress": {"us_per_launch": comp_us, "records": case.B * C * case.Hkv,
-                     "us_per_record": comp_us / (case.B * C * case.Hkv)},
+                     "us_per_record": comp_us / (case.B * C * case.Hkv),
+                     "rounds_min": int(rounds.min()), "rounds_median": float(np.median(rounds)),
+                     "rounds_max": int(rounds.max()),
+                     "records_at_round_cap": int((rounds >= 64).sum()),
+                     "rounds_note": "subspace-iteration rounds per record: 8, then as many as "
+                                    "the measured Ritz-value ratio needs for a 1e-6 reduction, "
+                                    "at most 64"},
         "step_us": dkv_s / steps * 1e6,
         "decode_us": dec_s / steps * 1e6,
         "decode_bytes": dkv_bytes,

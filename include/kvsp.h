@@ -315,6 +315,7 @@ kvsp_status kvsp_dense_decode(const kvsp_layout* layout, const void* q, const vo
  *   resid_k  [n_resid][head_dim]      layout dtype, right after coef
  *   resid_v  [n_resid][head_dim]      layout dtype, right after resid_k
  *   resid    [n_resid] int32          ascending token offsets within the block
+ *   rounds   int32                    the subspace-iteration rounds the codec ran
  *   padding to a multiple of 256 bytes.
  * E is the element size of the layout dtype. A compressed token t of the block
  * stands for the rows k_anchor + coef[t] . basis[:, :D] and
@@ -324,7 +325,8 @@ kvsp_status kvsp_dense_decode(const kvsp_layout* layout, const void* q, const vo
 typedef struct {
   int32_t rank;        /* must be 32 */
   int32_t n_resid;     /* exact residual tokens per block */
-  int32_t power_iters; /* kvsp_dkv_compress subspace iterations; 0 = default (10) */
+  int32_t power_iters; /* kvsp_dkv_compress rounds: > 0 exactly that many; 0 = per block
+                          from its measured spectrum (see kvsp_dkv_compress) */
 } kvsp_dkv_params;
 
 /* Bytes of one record (see above); 0 for unsupported arguments. */
@@ -338,13 +340,19 @@ size_t kvsp_dkv_workspace_bytes(const kvsp_layout* layout, const kvsp_dkv_params
 /* DKV codec: for every sequence b and every logical block j < C (C = floor(max(0,
  * L - recent_window) / P), the blocks wholly older than the window) writes the
  * record of (block_table[b][j], g) for every KV head g from the exact K/V rows
- * in the pools. The basis is computed by subspace iteration: power_iters
- * rounds of X^T X applied to it (float32 products), each followed by a
- * re-orthonormalisation (Cholesky QR in double of the column-scaled matrix),
- * started from a fixed pseudo-random basis. With a gap between the 32nd and
- * 33rd singular values of X it converges to the truncated SVD's subspace;
- * without one it spans a near-optimal 32-dimensional subspace. A direction
- * X does not have (rank below 32) gives a zero basis row. coef = X basis^T;
+ * in the pools. The basis is the top-32 right singular subspace of X, found by
+ * subspace iteration on 64 vectors (Q <- orth(X^T X Q): float32 products,
+ * Cholesky QR in double) followed by a Rayleigh-Ritz step (the symmetric
+ * eigenproblem of Q^T X^T X Q, cyclic Jacobi in double): the basis rows are
+ * the Ritz vectors of the 32 largest Ritz values. The 64-vector iterate
+ * converges to a subspace holding the top 32 at the rate (s_65 / s_32)^2 per
+ * round whatever the gap between s_32 and s_33, so the result is the
+ * truncated SVD's subspace wherever that is unique. Rounds: power_iters if
+ * positive; otherwise 8, then a Rayleigh-Ritz step whose Ritz values
+ * theta give the measured rate rho = theta_64 / theta_32, and
+ * ceil(log(1e-6) / log(rho)) rounds in all (at least 8, at most 64); the
+ * count is written to the record. A direction X does not have (Ritz value
+ * at most 1e-10 of the largest) gives a zero basis row. coef = X basis^T;
  * residual tokens are the n_resid rows with the largest float32
  * reconstruction error ||X_t - coef_t basis|| (ties to the lower offset);
  * anchor and residual rows are bit-exact copies. Records of other blocks are

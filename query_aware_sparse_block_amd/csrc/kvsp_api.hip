@@ -301,10 +301,9 @@ constexpr int kDkvMaxHeads = 16;      // query heads per KV head (MFMA columns)
 constexpr int kDkvTargetItems = 256;  // decode work items a launch aims for
 constexpr int kDkvMaxChunks = 32;     // compressed-block chunks per (sequence, KV head)
 constexpr int kDkvMaxWindowChunks = 32;  // window chunks per (sequence, KV head)
-constexpr int kDkvDefaultIters = 10;
 
 struct DkvRecordLayout {
-  int32_t off_basis, off_coef, off_rk, off_rv, off_ridx;
+  int32_t off_basis, off_coef, off_rk, off_rv, off_ridx, off_rounds;
   size_t bytes;
 };
 
@@ -327,6 +326,8 @@ DkvRecordLayout dkv_record_layout(const kvsp_layout& l, int n_resid) {
   off += static_cast<size_t>(n_resid) * D * E;
   r.off_ridx = static_cast<int32_t>(off);
   off += static_cast<size_t>(n_resid) * 4;
+  r.off_rounds = static_cast<int32_t>(off);
+  off += 4;
   r.bytes = align_to(off, 256);
   return r;
 }
@@ -634,6 +635,7 @@ kvsp_status kvsp_dkv_compress(const kvsp_layout* layout, const kvsp_dkv_params* 
   a.off_rk = r.off_rk;
   a.off_rv = r.off_rv;
   a.off_ridx = r.off_ridx;
+  a.off_rounds = r.off_rounds;
   a.B = l.batch;
   a.Hkv = l.num_kv_heads;
   a.P = l.block_size;
@@ -641,7 +643,7 @@ kvsp_status kvsp_dkv_compress(const kvsp_layout* layout, const kvsp_dkv_params* 
   a.num_phys = l.num_phys_blocks;
   a.recent_window = recent_window;
   a.n_resid = dkv->n_resid;
-  a.power_iters = dkv->power_iters > 0 ? dkv->power_iters : kDkvDefaultIters;
+  a.power_iters = dkv->power_iters;  // 0: rounds chosen per block from its Ritz values
   const hipError_t e = launch_dkv_compress(a, l.dtype, l.head_dim, stream);
   if (e == hipErrorNotSupported) return KVSP_ERR_UNSUPPORTED;
   return from_hip(e);

@@ -545,42 +545,64 @@ hipError_t launch_dkv_decode_d(const DkvDecodeArgs& a, int D, hipStream_t stream
 // ---- codec ----------------------------------------------------------------------
 // One workgroup (4 waves) per (sequence, block j < C, KV head). X = [K - k_a |
 // V - v_a] (P x N, N = 2D, anchor a = token 0) streams through LDS as float32
-// in 64-token chunks; the differences of two 16-bit values are exact there.
-// Subspace iteration keeps an orthonormal N x 32 basis Q and applies
-// Q <- orth(X^T (X Q)) power_iters times:
-//   Y = X Q   fp32 MFMA, wave w takes the chunk's tokens [16w, 16w + 16);
-//   Z += X^T Y  fp32 MFMA, wave w takes channels [N/4 w, N/4 (w + 1)); Z stays
-//             in registers across the chunks;
-//   orth(Z)   Cholesky QR in double of the column-scaled Z: Q = Z S R^-1
+// in 32-token chunks; the differences of two 16-bit values are exact there.
+// The top-32 right singular subspace of X comes from subspace iteration on a
+// block of 64 vectors followed by a Rayleigh-Ritz step: the 64-dimensional
+// iterate converges to a subspace holding the top 32 at the rate
+// (s_65 / s_32)^2 per round, whatever the gap between s_32 and s_33, and the
+// Rayleigh-Ritz step picks the top 32 out of it.
+//   Y = X Q    fp32 MFMA (N x 64 iterate Q, kept as Q^T in LDS);
+//   Z = X^T Y  fp32 MFMA, accumulated in registers across the chunks;
+//   Q = orth(Z)  Cholesky QR in double of the column-scaled Z: Q = Z S R^-1
 //             with S the inverse column norms and R^T R the Gram of Z S. A
 //             column whose squared pivot falls below kDropTol (its part
 //             independent of the earlier columns is under 1e-5 of its norm)
-//             is dropped, i.e. set to zero; so are zero columns. A zero basis
-//             row adds nothing to any reconstruction.
+//             is dropped, i.e. set to zero; so are zero columns.
+//   Rayleigh-Ritz: H = Y^T Y = Q^T X^T X Q (64 x 64, fp32 MFMA, then
+//             double), H = U diag(theta) U^T by cyclic Jacobi in double, and
+//             the basis rows are (Q U)^T for the 32 largest Ritz values theta;
+//             a row whose theta is at most kRitzDrop of the largest (a
+//             direction X does not have) is set to zero.
+// Rounds: with power_iters > 0 exactly that many. Otherwise kFirstRounds,
+// then a Rayleigh-Ritz step whose Ritz values estimate the rate:
+// rho = theta_64 / theta_32 (theta_64 <= s_64^2 and s_65 <= s_64, so rho
+// bounds the rate of the remaining rounds by the measured spectrum), and the
+// total becomes ceil(log(kConvTol) / log(rho)), between kFirstRounds and
+// kRoundCap. The rounds run are written to the record.
 // The start is a fixed pseudo-random matrix (murmur3's 32-bit finaliser of
 // the element index), orthonormalised the same way. A last pass writes
-// coef = X Q and each token's squared float32 reconstruction error
-// ||X_t - coef_t Q^T||^2; the n_resid largest (ties to the lower offset)
-// become the residual tokens.
-constexpr int kChunk = 64;
-constexpr int kZRow = 36;   // LDS row stride (floats) of Z and of Y
+// coef = X B^T and each token's squared float32 reconstruction error
+// ||X_t - coef_t B||^2; the n_resid largest (ties to the lower offset) become
+// the residual tokens.
+constexpr int kIterVecs = 64;   // vectors of the subspace iterate (twice the rank)
+constexpr int kXChunk = 32;     // tokens per X chunk in LDS
+constexpr int kYRow = kIterVecs + 4;
 constexpr double kDropTol = 1e-10;
+constexpr double kRitzDrop = 1e-10;
+constexpr int kFirstRounds = 8;
+constexpr int kRoundCap = 64;
+constexpr double kConvTol = 1e-6;
+constexpr int kJacobiSweeps = 16;
 
 template <int N>
 struct CodecShared {
+  float qt[kIterVecs][N + 4];  // Q^T (row i = iterate vector i); Z^T in place; the basis in rows 0..31
   union {
-    float x[kChunk][N + 4];  // X chunk
-    float z[N][kZRow];       // Z = X^T X Q before orthonormalisation
-  } u;
-  float qt[kRank][N + 4];    // Q^T: row r is basis vector r
-  float y[kChunk][kZRow];    // Y = X Q of the chunk
-  double g[kRank][kRank + 1];  // scaled Gram (upper part), R^T (strict lower part)
-  double rdiag[kRank];
-  double cs[kRank];          // column scales
-  float anc[N];              // anchor row [k_a | v_a]
-  float err2[256];           // per-token squared reconstruction error
+    float x[kXChunk][N + 4];                  // X chunk
+    double u[kIterVecs][kIterVecs + 1];       // Rayleigh-Ritz eigenvectors (columns)
+  } v;
+  float y[kXChunk][kYRow];                    // Y = X Q of the chunk
+  double g[kIterVecs][kIterVecs + 1];         // Gram of Z S (Cholesky QR) or H (Rayleigh-Ritz)
+  double rdiag[kIterVecs];
+  double cs[kIterVecs];                       // column scales
+  double jc[kIterVecs / 2], js[kIterVecs / 2];  // Jacobi rotations of one round
+  double red[2][4];
+  int32_t perm[kIterVecs];                    // Ritz vector index of the r-th largest value
+  float anc[N];                               // anchor row [k_a | v_a]
+  float err2[256];                            // per-token squared reconstruction error
   int32_t flag[256];
   int32_t ridx[kMaxResid];
+  int32_t rounds;
 };
 
 __device__ __forceinline__ float codec_start_value(uint32_t i) {
@@ -593,21 +615,27 @@ __device__ __forceinline__ float codec_start_value(uint32_t i) {
   return static_cast<float>(x >> 8) * (1.0f / 8388608.0f) - 1.0f;
 }
 
-// Q^T <- orth(Z) as described above; reads sh.u.z, writes sh.qt. Starts after
-// a barrier that published Z and ends with one.
+// Cholesky QR, in place, of the 32 vectors in rows [r0, r0 + 32) of sh.qt:
+// the Gram of the column-scaled vectors in double, a 32-step Cholesky with the
+// drop rule above, and a forward substitution per channel in double. Starts
+// after a barrier that published the rows and ends with one.
 template <int N>
-__device__ void codec_orthonormalize(CodecShared<N>& sh, int tid) {
+__device__ void codec_cholqr32(CodecShared<N>& sh, int tid, int r0) {
   {
     const int i = tid / 8, jq = tid % 8;
     double g0 = 0.0, g1 = 0.0, g2 = 0.0, g3 = 0.0;
-#pragma unroll 8
-    for (int c = 0; c < N; ++c) {
-      const double zi = sh.u.z[c][i];
-      const float4 zj = *reinterpret_cast<const float4*>(&sh.u.z[c][4 * jq]);
-      g0 += zi * static_cast<double>(zj.x);
-      g1 += zi * static_cast<double>(zj.y);
-      g2 += zi * static_cast<double>(zj.z);
-      g3 += zi * static_cast<double>(zj.w);
+#pragma unroll 4
+    for (int c = 0; c < N; c += 4) {
+      const float4 zi = *reinterpret_cast<const float4*>(&sh.qt[r0 + i][c]);
+      const float4 z0 = *reinterpret_cast<const float4*>(&sh.qt[r0 + 4 * jq + 0][c]);
+      const float4 z1 = *reinterpret_cast<const float4*>(&sh.qt[r0 + 4 * jq + 1][c]);
+      const float4 z2 = *reinterpret_cast<const float4*>(&sh.qt[r0 + 4 * jq + 2][c]);
+      const float4 z3 = *reinterpret_cast<const float4*>(&sh.qt[r0 + 4 * jq + 3][c]);
+      const double a0 = zi.x, a1 = zi.y, a2 = zi.z, a3 = zi.w;
+      g0 += a0 * z0.x + a1 * z0.y + a2 * z0.z + a3 * z0.w;
+      g1 += a0 * z1.x + a1 * z1.y + a2 * z1.z + a3 * z1.w;
+      g2 += a0 * z2.x + a1 * z2.y + a2 * z2.z + a3 * z2.w;
+      g3 += a0 * z3.x + a1 * z3.y + a2 * z3.z + a3 * z3.w;
     }
     sh.g[i][4 * jq + 0] = g0;
     sh.g[i][4 * jq + 1] = g1;
@@ -639,31 +667,189 @@ __device__ void codec_orthonormalize(CodecShared<N>& sh, int tid) {
     __syncthreads();
   }
   if (tid < N) {
+    const int c = tid;
     double x[kRank];
 #pragma unroll
     for (int j = 0; j < kRank; ++j) {
-      double s = static_cast<double>(sh.u.z[tid][j]) * sh.cs[j];
+      double s = static_cast<double>(sh.qt[r0 + j][c]) * sh.cs[j];
 #pragma unroll
       for (int i = 0; i < j; ++i) s -= x[i] * sh.g[j][i];
       const double r = sh.rdiag[j];
       x[j] = r > 0.0 ? s / r : 0.0;
     }
 #pragma unroll
-    for (int j = 0; j < kRank; ++j) sh.qt[j][tid] = static_cast<float>(x[j]);
+    for (int j = 0; j < kRank; ++j) sh.qt[r0 + j][c] = static_cast<float>(x[j]);
   }
   __syncthreads();
 }
 
-// X rows [64 ch, 64 ch + 64) of the tile pair: codec_issue_chunk requests
-// them into registers, codec_commit_chunk writes them to sh.u.x with the
-// anchor subtracted. (Requesting the next chunk while the current one is
-// computed measured no faster: the tiles are L2-resident after the first
-// round.)
+// Rows [32, 64) of sh.qt minus their projection on rows [0, 32), which are
+// orthonormal: W = Q1^T Z2 in double, then Z2 -= Q1 W per channel in double.
+template <int N>
+__device__ void codec_project_out(CodecShared<N>& sh, int tid) {
+  {
+    const int i = tid / 8, jq = tid % 8;
+    double w0 = 0.0, w1 = 0.0, w2 = 0.0, w3 = 0.0;
+#pragma unroll 4
+    for (int c = 0; c < N; c += 4) {
+      const float4 qi = *reinterpret_cast<const float4*>(&sh.qt[i][c]);
+      const float4 z0 = *reinterpret_cast<const float4*>(&sh.qt[kRank + 4 * jq + 0][c]);
+      const float4 z1 = *reinterpret_cast<const float4*>(&sh.qt[kRank + 4 * jq + 1][c]);
+      const float4 z2 = *reinterpret_cast<const float4*>(&sh.qt[kRank + 4 * jq + 2][c]);
+      const float4 z3 = *reinterpret_cast<const float4*>(&sh.qt[kRank + 4 * jq + 3][c]);
+      const double a0 = qi.x, a1 = qi.y, a2 = qi.z, a3 = qi.w;
+      w0 += a0 * z0.x + a1 * z0.y + a2 * z0.z + a3 * z0.w;
+      w1 += a0 * z1.x + a1 * z1.y + a2 * z1.z + a3 * z1.w;
+      w2 += a0 * z2.x + a1 * z2.y + a2 * z2.z + a3 * z2.w;
+      w3 += a0 * z3.x + a1 * z3.y + a2 * z3.z + a3 * z3.w;
+    }
+    sh.g[i][4 * jq + 0] = w0;
+    sh.g[i][4 * jq + 1] = w1;
+    sh.g[i][4 * jq + 2] = w2;
+    sh.g[i][4 * jq + 3] = w3;
+  }
+  __syncthreads();
+  if (tid < N) {
+    const int c = tid;
+    float q1[kRank];
+#pragma unroll
+    for (int i = 0; i < kRank; ++i) q1[i] = sh.qt[i][c];
+#pragma unroll 4
+    for (int j = 0; j < kRank; ++j) {
+      double z = sh.qt[kRank + j][c];
+#pragma unroll
+      for (int i = 0; i < kRank; ++i) z -= static_cast<double>(q1[i]) * sh.g[i][j];
+      sh.qt[kRank + j][c] = static_cast<float>(z);
+    }
+  }
+  __syncthreads();
+}
+
+// Q^T <- orth(Z^T) in place on sh.qt, 64 vectors: the first 32 by Cholesky
+// QR, the last 32 with the first 32 projected out (twice, so that what is
+// left is orthogonal to working precision) and then by Cholesky QR. Starts
+// after a barrier that published Z^T and ends with one.
+template <int N>
+__device__ void codec_orthonormalize(CodecShared<N>& sh, int tid) {
+  codec_cholqr32<N>(sh, tid, 0);
+  codec_project_out<N>(sh, tid);
+  codec_project_out<N>(sh, tid);
+  codec_cholqr32<N>(sh, tid, kRank);
+}
+
+// Members of pair m in round r of the circle tournament over 64 indices:
+// every round pairs each index once, and 63 rounds pair every two indices.
+__device__ __forceinline__ void jacobi_pair(int r, int m, int& p, int& q) {
+  if (m == 0) {
+    p = kIterVecs - 1;
+    q = r;
+  } else {
+    p = (r + m) % (kIterVecs - 1);
+    q = (r - m + kIterVecs - 1) % (kIterVecs - 1);
+  }
+}
+
+// Cyclic Jacobi on the symmetric sh.g (64 x 64, double): sweeps of 63 rounds
+// of 32 disjoint rotations until the off-diagonal part is negligible. The
+// eigenvalues end on the diagonal; with VECTORS the eigenvectors end in the
+// columns of sh.v.u. Starts after a barrier that published sh.g; ends with one.
+template <int N, bool VECTORS>
+__device__ void codec_jacobi(CodecShared<N>& sh, int tid) {
+  constexpr int V = kIterVecs;
+  if constexpr (VECTORS) {
+    for (int e = tid; e < V * V; e += 256) sh.v.u[e / V][e % V] = (e / V == e % V) ? 1.0 : 0.0;
+  }
+  __syncthreads();
+  for (int sweep = 0; sweep < kJacobiSweeps; ++sweep) {
+    // stop once the off-diagonal square sum is below 1e-24 of the total
+    double off = 0.0, all = 0.0;
+    for (int e = tid; e < V * V; e += 256) {
+      const double h = sh.g[e / V][e % V];
+      all += h * h;
+      if (e / V != e % V) off += h * h;
+    }
+    off = group_sum<kWave>(off);
+    all = group_sum<kWave>(all);
+    if (tid % kWave == 0) {
+      sh.red[0][tid / kWave] = off;
+      sh.red[1][tid / kWave] = all;
+    }
+    __syncthreads();
+    const double off_t = sh.red[0][0] + sh.red[0][1] + sh.red[0][2] + sh.red[0][3];
+    const double all_t = sh.red[1][0] + sh.red[1][1] + sh.red[1][2] + sh.red[1][3];
+    __syncthreads();
+    if (!(off_t > 1e-24 * all_t)) break;  // uniform: every thread read the same sums
+    for (int r = 0; r < V - 1; ++r) {
+      if (tid < V / 2) {
+        int p, q;
+        jacobi_pair(r, tid, p, q);
+        const double app = sh.g[p][p], aqq = sh.g[q][q], apq = sh.g[p][q];
+        double c = 1.0, sn = 0.0;
+        if (apq != 0.0) {
+          // the rotation that zeroes (p, q): t = tan of its angle, the
+          // smaller root of t^2 + 2 theta t - 1 = 0
+          const double theta = (aqq - app) / (2.0 * apq);
+          const double t = (theta >= 0.0 ? 1.0 : -1.0) / (fabs(theta) + sqrt(theta * theta + 1.0));
+          c = 1.0 / sqrt(t * t + 1.0);
+          sn = t * c;
+        }
+        sh.jc[tid] = c;
+        sh.js[tid] = sn;
+      }
+      __syncthreads();
+      // H <- P^T H P, by 2 x 2 blocks of (pair m rows, pair n columns); P
+      // maps (p, q) to (c p - s q, s p + c q)
+      for (int e = tid; e < (V / 2) * (V / 2); e += 256) {
+        const int m = e / (V / 2), n = e % (V / 2);
+        int pm, qm, pn, qn;
+        jacobi_pair(r, m, pm, qm);
+        jacobi_pair(r, n, pn, qn);
+        const double cm = sh.jc[m], sm = sh.js[m], cn = sh.jc[n], snn = sh.js[n];
+        const double h00 = sh.g[pm][pn], h01 = sh.g[pm][qn], h10 = sh.g[qm][pn], h11 = sh.g[qm][qn];
+        // rows: R_m^T B
+        const double b00 = cm * h00 - sm * h10, b01 = cm * h01 - sm * h11;
+        const double b10 = sm * h00 + cm * h10, b11 = sm * h01 + cm * h11;
+        // columns: (R_m^T B) R_n
+        sh.g[pm][pn] = cn * b00 - snn * b01;
+        sh.g[pm][qn] = snn * b00 + cn * b01;
+        sh.g[qm][pn] = cn * b10 - snn * b11;
+        sh.g[qm][qn] = snn * b10 + cn * b11;
+      }
+      if constexpr (VECTORS) {
+        for (int e = tid; e < V * (V / 2); e += 256) {
+          const int i = e / (V / 2), n = e % (V / 2);
+          int pn, qn;
+          jacobi_pair(r, n, pn, qn);
+          const double cn = sh.jc[n], snn = sh.js[n];
+          const double up = sh.v.u[i][pn], uq = sh.v.u[i][qn];
+          sh.v.u[i][pn] = cn * up - snn * uq;
+          sh.v.u[i][qn] = snn * up + cn * uq;
+        }
+      }
+      __syncthreads();
+    }
+  }
+  // ranks of the eigenvalues, descending (ties to the lower index)
+  if (tid < V) {
+    const double t = sh.g[tid][tid];
+    int rank = 0;
+    for (int j = 0; j < V; ++j) {
+      const double u = sh.g[j][j];
+      rank += (u > t) || (u == t && j < tid);
+    }
+    sh.perm[rank] = tid;
+  }
+  __syncthreads();
+}
+
+// X rows [32 ch, 32 ch + 32) of the tile pair: codec_issue_chunk requests
+// them into registers, codec_commit_chunk writes them to sh.v.x with the
+// anchor subtracted.
 template <typename T, int D>
 struct CodecChunk {
   static constexpr int VPR = D * T::kBytes / 16;   // 16-byte vectors per K (or V) row
-  static constexpr int VPC = kChunk * VPR;          // per pool and chunk
-  static constexpr int PER_THREAD = 2 * VPC / 256;  // K and V vectors per thread
+  static constexpr int VPC = kXChunk * VPR;         // per pool and chunk
+  static constexpr int PER_THREAD = (2 * VPC + 255) / 256;  // K and V vectors per thread
   uint4 v[PER_THREAD];
 };
 
@@ -673,12 +859,12 @@ __device__ __forceinline__ void codec_issue_chunk(CodecChunk<T, D>& cc, const ch
   using CC = CodecChunk<T, D>;
 #pragma unroll
   for (int u = 0; u < CC::PER_THREAD; ++u) {
-    const int v = tid + 256 * u;
+    const int v = min(tid + 256 * u, 2 * CC::VPC - 1);
     const bool isv = v >= CC::VPC;
     const int w = isv ? v - CC::VPC : v;
     const int row = w / CC::VPR;
     const int col = (w % CC::VPR) * T::kPerVec;
-    cc.v[u] = load16((isv ? vtile : ktile) + (static_cast<int64_t>(kChunk * ch + row) * D + col) * T::kBytes);
+    cc.v[u] = load16((isv ? vtile : ktile) + (static_cast<int64_t>(kXChunk * ch + row) * D + col) * T::kBytes);
   }
 }
 
@@ -690,6 +876,7 @@ __device__ __forceinline__ void codec_commit_chunk(CodecShared<2 * D>& sh, const
 #pragma unroll
   for (int u = 0; u < CC::PER_THREAD; ++u) {
     const int v = tid + 256 * u;
+    if (v >= 2 * CC::VPC) continue;
     const bool isv = v >= CC::VPC;
     const int w = isv ? v - CC::VPC : v;
     const int row = w / CC::VPR;
@@ -704,18 +891,47 @@ __device__ __forceinline__ void codec_commit_chunk(CodecShared<2 * D>& sh, const
       o.y = f[e + 1] - sh.anc[c0 + e + 1];
       o.z = f[e + 2] - sh.anc[c0 + e + 2];
       o.w = f[e + 3] - sh.anc[c0 + e + 3];
-      *reinterpret_cast<float4*>(&sh.u.x[row][c0 + e]) = o;
+      *reinterpret_cast<float4*>(&sh.v.x[row][c0 + e]) = o;
     }
   }
+}
+
+// Y = X Q for the chunk in sh.v.x: wave w computes token tile w % 2 against
+// iterate vectors [32 (w / 2), 32 (w / 2) + 32) (two 16 x 16 tiles) and
+// stores them in sh.y. BT basis tiles are used in total (4: the iterate; 2:
+// the final 32-row basis, then only waves with w / 2 == 0 have work).
+template <int N, int BT>
+__device__ __forceinline__ void codec_y(CodecShared<N>& sh, int wave, int hl, int gi) {
+  constexpr int NCG = N / 16;
+  const int tt = wave % 2;
+  const int bt0 = 2 * (wave / 2);
+  if (bt0 >= BT) return;  // uniform per wave
+  floatx4 yv[2] = {floatx4{0.f, 0.f, 0.f, 0.f}, floatx4{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll 4
+  for (int cg = 0; cg < NCG; ++cg) {
+    const float4 xa = *reinterpret_cast<const float4*>(&sh.v.x[16 * tt + hl][16 * cg + 4 * gi]);
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt) {
+      const float4 qb = *reinterpret_cast<const float4*>(&sh.qt[16 * (bt0 + rt) + hl][16 * cg + 4 * gi]);
+      yv[rt] = mfma4(xa.x, qb.x, yv[rt]);
+      yv[rt] = mfma4(xa.y, qb.y, yv[rt]);
+      yv[rt] = mfma4(xa.z, qb.z, yv[rt]);
+      yv[rt] = mfma4(xa.w, qb.w, yv[rt]);
+    }
+  }
+#pragma unroll
+  for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) sh.y[16 * tt + 4 * gi + v][16 * (bt0 + rt) + hl] = yv[rt][v];
 }
 
 template <typename T, int D>
 __global__ __launch_bounds__(256) void dkv_compress_kernel(DkvCompressArgs a) {
   constexpr int E = T::kBytes;
   constexpr int N = 2 * D;
-  constexpr int NCG = N / 16;      // 16-channel groups (contraction of Y)
   constexpr int NCT = N / 64;      // 16-channel Z tiles per wave
   constexpr int VPR = D * E / 16;  // 16-byte vectors per K (or V) row
+  constexpr int V = kIterVecs;
   __shared__ CodecShared<N> sh;
 
   const int tid = threadIdx.x;
@@ -724,7 +940,7 @@ __global__ __launch_bounds__(256) void dkv_compress_kernel(DkvCompressArgs a) {
   const int hl = lane % 16;
   const int gi = lane / 16;
   const int64_t total = static_cast<int64_t>(a.B) * a.max_blocks * a.Hkv;
-  const int n_chunks = a.P / kChunk;
+  const int n_chunks = a.P / kXChunk;
   const int R = a.n_resid;
 
   for (int64_t item = blockIdx.x; item < total; item += gridDim.x) {
@@ -743,97 +959,169 @@ __global__ __launch_bounds__(256) void dkv_compress_kernel(DkvCompressArgs a) {
     // anchor: float32 copy for the differences, raw copy into the record
     for (int c = tid; c < N; c += 256) sh.anc[c] = c < D ? T::load1(ktile, c) : T::load1(vtile, c - D);
     if (tid < 2 * VPR) store16(rec + tid * 16, load16((tid < VPR ? ktile : vtile) + (tid % VPR) * 16));
-    for (int e = tid; e < N * kRank; e += 256) sh.u.z[e / kRank][e % kRank] = codec_start_value(e);
+    for (int e = tid; e < V * N; e += 256) sh.qt[e / N][e % N] = codec_start_value(e);
     __syncthreads();
     codec_orthonormalize<N>(sh, tid);
 
-    for (int it = 0; it <= a.power_iters; ++it) {
-      const bool last = it == a.power_iters;
-      floatx4 zacc[NCT][2];
+    // Passes over X: Z^T = (X^T X Q)^T into sh.qt (RITZ false), or H = Q^T
+    // X^T X Q into sh.g (RITZ true).
+    auto x_pass = [&](bool ritz) {
+      floatx4 zacc[NCT][4];
 #pragma unroll
-      for (int ct = 0; ct < NCT; ++ct) zacc[ct][0] = zacc[ct][1] = floatx4{0.f, 0.f, 0.f, 0.f};
+      for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+        for (int bt = 0; bt < 4; ++bt) zacc[ct][bt] = floatx4{0.f, 0.f, 0.f, 0.f};
       for (int ch = 0; ch < n_chunks; ++ch) {
         CodecChunk<T, D> now;
         codec_issue_chunk<T, D>(now, ktile, vtile, ch, tid);
         codec_commit_chunk<T, D>(sh, now, tid);
         __syncthreads();
-        // Y = X Q for tokens [16 wave, 16 wave + 16) of the chunk
-        floatx4 yv[2] = {floatx4{0.f, 0.f, 0.f, 0.f}, floatx4{0.f, 0.f, 0.f, 0.f}};
-#pragma unroll 4
-        for (int cg = 0; cg < NCG; ++cg) {
-          const float4 xa = *reinterpret_cast<const float4*>(&sh.u.x[16 * wave + hl][16 * cg + 4 * gi]);
-#pragma unroll
-          for (int rt = 0; rt < 2; ++rt) {
-            const float4 qb = *reinterpret_cast<const float4*>(&sh.qt[16 * rt + hl][16 * cg + 4 * gi]);
-            yv[rt] = mfma4(xa.x, qb.x, yv[rt]);
-            yv[rt] = mfma4(xa.y, qb.y, yv[rt]);
-            yv[rt] = mfma4(xa.z, qb.z, yv[rt]);
-            yv[rt] = mfma4(xa.w, qb.w, yv[rt]);
-          }
-        }
-#pragma unroll
-        for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-          for (int v = 0; v < 4; ++v) {
-            const int t = 16 * wave + 4 * gi + v;
-            sh.y[t][16 * rt + hl] = yv[rt][v];
-            if (last)
-              reinterpret_cast<float*>(rec + a.off_coef)[(kChunk * ch + t) * kRank + 16 * rt + hl] = yv[rt][v];
-          }
+        codec_y<N, 4>(sh, wave, hl, gi);
         __syncthreads();
-        if (!last) {
-          // Z += X^T Y over the chunk; k-slot gi of step s is token 4 s + gi
-#pragma unroll 4
-          for (int s = 0; s < kChunk / 4; ++s) {
+        if (!ritz) {
+          // Z^T += (X^T Y)^T: wave w takes channel tiles [NCT w, NCT (w + 1));
+          // k-slot gi of step s is token 4 s + gi
+#pragma unroll 2
+          for (int s = 0; s < kXChunk / 4; ++s) {
             const int t = 4 * s + gi;
-            const float yb0 = sh.y[t][hl];
-            const float yb1 = sh.y[t][16 + hl];
+            float yb[4];
+#pragma unroll
+            for (int bt = 0; bt < 4; ++bt) yb[bt] = sh.y[t][16 * bt + hl];
 #pragma unroll
             for (int ct = 0; ct < NCT; ++ct) {
-              const float xa = sh.u.x[t][16 * (wave * NCT + ct) + hl];
-              zacc[ct][0] = mfma4(xa, yb0, zacc[ct][0]);
-              zacc[ct][1] = mfma4(xa, yb1, zacc[ct][1]);
+              const float xa = sh.v.x[t][16 * (wave * NCT + ct) + hl];
+#pragma unroll
+              for (int bt = 0; bt < 4; ++bt) zacc[ct][bt] = mfma4(xa, yb[bt], zacc[ct][bt]);
             }
           }
         } else {
-          // squared error of X - Y Q^T for tokens [16 wave, 16 wave + 16)
-          float sq[4] = {0.f, 0.f, 0.f, 0.f};
-          for (int ct = 0; ct < NCG; ++ct) {
-            floatx4 xh = {0.f, 0.f, 0.f, 0.f};
+          // H += Y^T Y: wave w takes row tile w, all four column tiles
+#pragma unroll 2
+          for (int s = 0; s < kXChunk / 4; ++s) {
+            const int t = 4 * s + gi;
+            const float ya = sh.y[t][16 * wave + hl];
 #pragma unroll
-            for (int rg = 0; rg < 2; ++rg) {
-              const float4 ya = *reinterpret_cast<const float4*>(&sh.y[16 * wave + hl][16 * rg + 4 * gi]);
-              const int r0 = 16 * rg + 4 * gi;
-              xh = mfma4(ya.x, sh.qt[r0 + 0][16 * ct + hl], xh);
-              xh = mfma4(ya.y, sh.qt[r0 + 1][16 * ct + hl], xh);
-              xh = mfma4(ya.z, sh.qt[r0 + 2][16 * ct + hl], xh);
-              xh = mfma4(ya.w, sh.qt[r0 + 3][16 * ct + hl], xh);
-            }
-#pragma unroll
-            for (int v = 0; v < 4; ++v) {
-              const float e = sh.u.x[16 * wave + 4 * gi + v][16 * ct + hl] - xh[v];
-              sq[v] += e * e;
-            }
-          }
-#pragma unroll
-          for (int v = 0; v < 4; ++v) {
-            sq[v] = group_sum<16>(sq[v]);
-            if (hl == 0) sh.err2[kChunk * ch + 16 * wave + 4 * gi + v] = sq[v];
+            for (int bt = 0; bt < 4; ++bt) zacc[0][bt] = mfma4(ya, sh.y[t][16 * bt + hl], zacc[0][bt]);
           }
         }
         __syncthreads();  // x and y are overwritten next
       }
-      if (!last) {
+      if (!ritz) {
 #pragma unroll
         for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
-          for (int rt = 0; rt < 2; ++rt)
+          for (int bt = 0; bt < 4; ++bt)
 #pragma unroll
             for (int v = 0; v < 4; ++v)
-              sh.u.z[16 * (wave * NCT + ct) + 4 * gi + v][16 * rt + hl] = zacc[ct][rt][v];
-        __syncthreads();
-        codec_orthonormalize<N>(sh, tid);
+              sh.qt[16 * bt + hl][16 * (wave * NCT + ct) + 4 * gi + v] = zacc[ct][bt][v];
+      } else {
+#pragma unroll
+        for (int bt = 0; bt < 4; ++bt)
+#pragma unroll
+          for (int v = 0; v < 4; ++v)
+            sh.g[16 * wave + 4 * gi + v][16 * bt + hl] = static_cast<double>(zacc[0][bt][v]);
       }
+      __syncthreads();
+    };
+
+    int rounds = a.power_iters > 0 ? a.power_iters : kRoundCap;
+    for (int k = 0;; ++k) {
+      if (a.power_iters == 0 && k == kFirstRounds) {
+        // Ritz values of the current iterate: the measured rate sets the rounds
+        x_pass(true);
+        codec_jacobi<N, false>(sh, tid);
+        const double t32 = sh.g[sh.perm[kRank - 1]][sh.perm[kRank - 1]];
+        const double t64 = sh.g[sh.perm[V - 1]][sh.perm[V - 1]];
+        const double rho = t32 > 0.0 ? fmax(t64, 0.0) / t32 : 0.0;
+        int want = kFirstRounds;
+        if (rho >= 1.0) {
+          want = kRoundCap;
+        } else if (rho > 0.0) {
+          const double need = ceil(log(kConvTol) / log(rho));
+          want = need > kRoundCap ? kRoundCap : (need < kFirstRounds ? kFirstRounds : static_cast<int>(need));
+        }
+        rounds = want;  // the same on every thread (LDS values after a barrier)
+        __syncthreads();
+      }
+      if (k >= rounds) break;
+      x_pass(false);
+      codec_orthonormalize<N>(sh, tid);
+    }
+
+    // Rayleigh-Ritz: basis rows = (Q U)^T for the 32 largest Ritz values
+    x_pass(true);
+    codec_jacobi<N, true>(sh, tid);
+    {
+      const double tmax = sh.g[sh.perm[0]][sh.perm[0]];
+      if (tid < N) {
+        const int c = tid;
+        float qc[V];
+#pragma unroll
+        for (int i = 0; i < V; ++i) qc[i] = sh.qt[i][c];
+#pragma unroll 1
+        for (int r = 0; r < kRank; ++r) {
+          const int pr = sh.perm[r];
+          double acc = 0.0;
+#pragma unroll
+          for (int i = 0; i < V; ++i) acc += static_cast<double>(qc[i]) * sh.v.u[i][pr];
+          const bool live = sh.g[pr][pr] > kRitzDrop * tmax && tmax > 0.0;
+          sh.qt[r][c] = live ? static_cast<float>(acc) : 0.f;
+        }
+      }
+    }
+    __syncthreads();
+
+    // last pass: coef = X B^T and the per-token squared errors
+    for (int ch = 0; ch < n_chunks; ++ch) {
+      CodecChunk<T, D> now;
+      codec_issue_chunk<T, D>(now, ktile, vtile, ch, tid);
+      codec_commit_chunk<T, D>(sh, now, tid);
+      __syncthreads();
+      codec_y<N, 2>(sh, wave, hl, gi);
+      __syncthreads();
+      for (int e = tid; e < kXChunk * kRank; e += 256) {
+        const int t = e / kRank, r = e % kRank;
+        reinterpret_cast<float*>(rec + a.off_coef)[(kXChunk * ch + t) * kRank + r] = sh.y[t][r];
+      }
+      // squared error of X - Y B for tokens [16 (w % 2), 16 (w % 2) + 16),
+      // channel tiles of parity w / 2
+      {
+        const int tt = wave % 2;
+        float sq[4] = {0.f, 0.f, 0.f, 0.f};
+        for (int ct = wave / 2; ct < N / 16; ct += 2) {
+          floatx4 xh = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int rg = 0; rg < 2; ++rg) {
+            const float4 ya = *reinterpret_cast<const float4*>(&sh.y[16 * tt + hl][16 * rg + 4 * gi]);
+            const int r0 = 16 * rg + 4 * gi;
+            xh = mfma4(ya.x, sh.qt[r0 + 0][16 * ct + hl], xh);
+            xh = mfma4(ya.y, sh.qt[r0 + 1][16 * ct + hl], xh);
+            xh = mfma4(ya.z, sh.qt[r0 + 2][16 * ct + hl], xh);
+            xh = mfma4(ya.w, sh.qt[r0 + 3][16 * ct + hl], xh);
+          }
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            const float e = sh.v.x[16 * tt + 4 * gi + v][16 * ct + hl] - xh[v];
+            sq[v] += e * e;
+          }
+        }
+#pragma unroll
+        for (int v = 0; v < 4; ++v) sq[v] = group_sum<16>(sq[v]);
+        // the two channel halves of a token tile are summed through LDS:
+        // waves 0/1 write, waves 2/3 add after the barrier
+        if (wave < 2) {
+#pragma unroll
+          for (int v = 0; v < 4; ++v)
+            if (hl == 0) sh.err2[kXChunk * ch + 16 * tt + 4 * gi + v] = sq[v];
+        }
+        __syncthreads();
+        if (wave >= 2) {
+#pragma unroll
+          for (int v = 0; v < 4; ++v)
+            if (hl == 0) sh.err2[kXChunk * ch + 16 * tt + 4 * gi + v] += sq[v];
+        }
+      }
+      __syncthreads();  // x and y are overwritten next
     }
 
     // basis rows
@@ -860,6 +1148,7 @@ __global__ __launch_bounds__(256) void dkv_compress_kernel(DkvCompressArgs a) {
     }
     __syncthreads();
     if (tid < R) reinterpret_cast<int32_t*>(rec + a.off_ridx)[tid] = sh.ridx[tid];
+    if (tid == 0) *reinterpret_cast<int32_t*>(rec + a.off_rounds) = rounds;
     for (int v = tid; v < R * 2 * VPR; v += 256) {
       const int row = v / (2 * VPR);
       const int w = v % (2 * VPR);
@@ -877,7 +1166,7 @@ hipError_t launch_dkv_compress_d(const DkvCompressArgs& a, int D, hipStream_t st
   const int64_t total = static_cast<int64_t>(a.B) * a.max_blocks * a.Hkv;
   if (total <= 0) return hipSuccess;
   const int grid = total < 1024 ? static_cast<int>(total) : 1024;
-  if (a.P % kChunk != 0 || a.P > 256) return hipErrorInvalidValue;
+  if (a.P % kXChunk != 0 || a.P > 256) return hipErrorInvalidValue;
   if (D == 64) {
     hipLaunchKernelGGL((dkv_compress_kernel<T, 64>), dim3(grid), dim3(256), 0, stream, a);
   } else if (D == 128) {

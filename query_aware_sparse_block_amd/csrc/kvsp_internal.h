@@ -111,6 +111,8 @@ struct DkvDecodeArgs {
   float scale_log2;
 };
 // DKV codec: one work item per (sequence, candidate block, KV head).
+// power_iters > 0: exactly that many subspace-iteration rounds; 0: rounds
+// chosen per block from the Ritz values after the first rounds.
 struct DkvCompressArgs {
   const void* k_pool;
   const void* v_pool;
@@ -118,7 +120,7 @@ struct DkvCompressArgs {
   const int32_t* context_lens;
   char* records;
   int64_t rec_bytes;
-  int32_t off_basis, off_coef, off_rk, off_rv, off_ridx;
+  int32_t off_basis, off_coef, off_rk, off_rv, off_ridx, off_rounds;
   int32_t B, Hkv, P, max_blocks, num_phys, recent_window, n_resid, power_iters;
 };
 hipError_t launch_dkv_decode(const DkvDecodeArgs& a, int dtype, int D, hipStream_t stream);

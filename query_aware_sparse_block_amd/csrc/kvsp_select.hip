@@ -103,18 +103,22 @@ __device__ __forceinline__ int score_blocks(const ScoreArgs& a, double* qbar, in
   const int nvec = row / 4;
   // Large summary sets are read once per call with non-temporal loads
   // (a.stream_rows, uniform); small ones may stay cached between calls.
-  auto issue = [&](int jb, float4 (&sv)[VPL], bool direct) {
+  auto issue = [&](int jb, float4 (&sv)[VPL], bool direct, bool repeat = false) {
     const int j = jb + slot;
     if (STREAM && !direct) {
       // Later streamed passes: no load behind a per-lane branch (such a load
       // is waited for alone, and the next pass's loads could not stay in
       // flight). A row past j1 reads the last live row of the range and a
       // vector past the row's end the row's last vector; consume masks both.
+      // A repeat (the pipeline's pass past the end, whose data is never
+      // used) keeps the instruction count, which the waits depend on, but
+      // points every lane at the row's first vector: one line per load
+      // instead of re-reading the rows.
       const int64_t phys = phys_lds[min(j, j1 - 1) - first];
       const float4* srow = reinterpret_cast<const float4*>(a.summaries + phys * row);
 #pragma unroll
       for (int v = 0; v < VPL; ++v)
-        sv[v] = __builtin_bit_cast(float4, load16_stream(srow + min(gl + LG * v, nvec - 1)));
+        sv[v] = __builtin_bit_cast(float4, load16_stream(srow + (repeat ? 0 : min(gl + LG * v, nvec - 1))));
       return;
     }
     int64_t phys = 0;
@@ -183,12 +187,12 @@ __device__ __forceinline__ int score_blocks(const ScoreArgs& a, double* qbar, in
       // this pass's arithmetic, which would otherwise be hoisted above them.
       while (jb < j1) {
         const int jn = jb + BPP;
-        issue(jn < j1 ? jn : jb, buf1, false);
+        issue(jn < j1 ? jn : jb, buf1, false, jn >= j1);
         __builtin_amdgcn_sched_barrier(0);
         consume(jb, buf0);
         if (jn >= j1) break;
         const int jn2 = jn + BPP;
-        issue(jn2 < j1 ? jn2 : jn, buf0, false);
+        issue(jn2 < j1 ? jn2 : jn, buf0, false, jn2 >= j1);
         __builtin_amdgcn_sched_barrier(0);
         consume(jn, buf1);
         jb = jn2;

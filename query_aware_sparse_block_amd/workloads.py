@@ -407,7 +407,8 @@ def dkv_record_layout(D: int, P: int, elem_bytes: int, n_resid: int, rank: int =
     """Byte offsets of one (block, KV head) record and its padded size:
     anchor K and V rows (cache dtype), basis [rank][2D] fp32, coefficients
     [P][rank] fp32, residual K rows and V rows [n_resid][D] (cache dtype),
-    residual token offsets [n_resid] int32; the record is padded to 256 B."""
+    residual token offsets [n_resid] int32, the codec's subspace-iteration
+    rounds (int32); the record is padded to 256 B."""
     def up(x, a):
         return (x + a - 1) // a * a
     off = {"anchor": 0}
@@ -416,14 +417,16 @@ def dkv_record_layout(D: int, P: int, elem_bytes: int, n_resid: int, rank: int =
     off["resid_k"] = off["coef"] + P * rank * 4
     off["resid_v"] = off["resid_k"] + n_resid * D * elem_bytes
     off["resid"] = off["resid_v"] + n_resid * D * elem_bytes
-    off["bytes"] = up(off["resid"] + 4 * n_resid, 256)
+    off["rounds"] = off["resid"] + 4 * n_resid
+    off["bytes"] = up(off["rounds"] + 4, 256)
     return off
 
 
 def dkv_pack(fields: dict, dtype: str, P: int, n_resid: int) -> np.ndarray:
     """One record as uint8 bytes. ``fields`` hold stored values: anchor_k,
     anchor_v, resid_k, resid_v as the cache dtype's raw patterns (uint16 or
-    float32), basis and coef as float32, resid as int."""
+    float32), basis and coef as float32, resid as int; an optional
+    ``rounds`` (int, default 0)."""
     D = fields["anchor_k"].shape[0]
     E = ELEM_BYTES[dtype]
     lay = dkv_record_layout(D, P, E, n_resid)
@@ -440,6 +443,7 @@ def dkv_pack(fields: dict, dtype: str, P: int, n_resid: int) -> np.ndarray:
     put(lay["resid_k"], fields["resid_k"])
     put(lay["resid_v"], fields["resid_v"])
     put(lay["resid"], np.asarray(fields["resid"], np.int32))
+    put(lay["rounds"], np.asarray([fields.get("rounds", 0)], np.int32))
     return buf
 
 
@@ -461,6 +465,7 @@ def dkv_unpack(buf: np.ndarray, dtype: str, D: int, P: int, n_resid: int) -> dic
         resid_k=get(lay["resid_k"], n_resid * D, raw_t).reshape(n_resid, D),
         resid_v=get(lay["resid_v"], n_resid * D, raw_t).reshape(n_resid, D),
         resid=get(lay["resid"], n_resid, np.int32),
+        rounds=int(get(lay["rounds"], 1, np.int32)[0]),
     )
 
 

@@ -1,8 +1,9 @@
 """GPU parity of the DKV block codec (DKV abstract) through the C ABI.
 
-kvsp_dkv_compress computes the rank-32 basis by float32 subspace iteration,
-not by an SVD, so a record is compared with the oracle's codec through what
-the abstract fixes, not bit by bit:
+kvsp_dkv_compress computes the rank-32 basis by subspace iteration on 64
+vectors with a Rayleigh-Ritz step (float32 products, double
+orthonormalisation and eigensolver), not by an SVD, so a record is compared
+with the oracle's codec through what the abstract fixes, not bit by bit:
 
 * always: the anchor rows and the residual rows are byte copies of the pool;
   the residual offsets ascend; records of blocks inside the window are not
@@ -11,15 +12,16 @@ the abstract fixes, not bit by bit:
   float64) within 1e-5 of the block's largest row norm; the residual tokens
   are the n_resid largest reconstruction errors of the record itself, up to a
   band of 1e-4 of the largest row norm (errors that close may order either
-  way in float32); the captured energy is within 10% of the Eckart-Young
-  optimum (the oracle's SVD) and never above it;
-* on blocks with a clear spectral gap at rank 32, where the truncated
-  subspace is unique and subspace iteration has converged (singular values
-  with (s_33 / s_32)^(2 rounds) <= 1e-5; the planted low-rank blocks of the
-  cases below, checked per block): the basis spans the oracle's subspace
-  (projectors within 1e-3), the residual set is the oracle's, and decoding
-  the GPU records equals decoding the oracle's records (the codec bar: 2e-3
-  for every dtype);
+  way in float32); the captured energy never exceeds the Eckart-Young
+  optimum (the oracle's SVD); the record's round count is the one asked
+  for, or, by default, between the first 8 rounds and the cap of 64;
+* with the default rounds, on every block: the captured energy is within
+  1e-4 of the optimum; where the truncated subspace is numerically unique
+  (s_32^2 - s_33^2 at least 1e-4 of s_32^2, as on iid, per-channel-scaled and
+  planted low-rank blocks alike) the basis spans the oracle's subspace
+  (projectors within 1e-3) and the residual tokens are the oracle's up to a
+  band of 1e-3 of the largest row norm; and decoding the GPU records equals
+  decoding the oracle's records (the codec bar: 2e-3 for every dtype);
 * end to end: kvsp_dkv_decode over GPU-compressed records matches the oracle
   decode of the same records at the exact-path bars (2e-3 for 16-bit caches,
   1e-5 for fp32 caches; lse 1e-4).
@@ -49,11 +51,12 @@ pytestmark = pytest.mark.gpu
 ORTHO_TOL = 1e-5
 COEF_REL = 1e-5
 ERR_BAND_REL = 1e-4
-ENERGY_SLACK = 1.10
+ENERGY_REL = 1e-4
 SUBSPACE_TOL = 1e-3
+RESID_BAND_REL = 1e-3
+UNIQUE_GAP = 1e-4
 CODEC_OUT_TOL = 2e-3
-GAP_FACTOR = 1e-5
-DEFAULT_ROUNDS = 10
+FIRST_ROUNDS, ROUND_CAP = 8, 64
 POISON = 0x5A
 
 
@@ -90,9 +93,10 @@ def pools_f64(case):
             wl.decode_f32(case.v_pool, case.dtype).astype(np.float64))
 
 
-def check_record(case, raw, fields, K, V, n_resid, gapped, slack=ENERGY_SLACK, rounds=DEFAULT_ROUNDS):
+def check_record(case, raw, fields, K, V, n_resid, iters=0):
     """The property checks of the module docstring for one record; returns the
-    oracle's codec of the block."""
+    oracle's codec of the block and whether it was compared subspace to
+    subspace."""
     D, P = case.D, case.P
     X = DKV.block_delta(K, V)
     xmax = np.linalg.norm(X, axis=1).max()
@@ -103,6 +107,11 @@ def check_record(case, raw, fields, K, V, n_resid, gapped, slack=ENERGY_SLACK, r
     assert np.all(np.diff(resid) > 0) and (n_resid == 0 or (resid[0] >= 0 and resid[-1] < P))
     assert np.array_equal(fields["resid_k"], raw_k[resid])
     assert np.array_equal(fields["resid_v"], raw_v[resid])
+    # rounds
+    if iters:
+        assert fields["rounds"] == iters, fields["rounds"]
+    else:
+        assert FIRST_ROUNDS <= fields["rounds"] <= ROUND_CAP, fields["rounds"]
     # basis: orthonormal rows or zero rows
     Bm = fields["basis"].astype(np.float64)
     norms = np.linalg.norm(Bm, axis=1)
@@ -128,24 +137,36 @@ def check_record(case, raw, fields, K, V, n_resid, gapped, slack=ENERGY_SLACK, r
     got = float(np.sum((X - X @ Bm.T @ Bm) ** 2))
     scale = float(np.sum(X * X))
     assert got >= opt - 1e-6 * scale
-    if slack is not None:
-        assert got <= slack * opt + 1e-6 * scale, (got, opt)
-    if gapped:
+    compared = False
+    if iters == 0:
+        assert got <= opt + ENERGY_REL * max(opt, 1e-30) + 1e-6 * scale, (got, opt)
         sv = np.linalg.svd(X, compute_uv=False)
-        assert (sv[32] / sv[31]) ** (2 * rounds) <= GAP_FACTOR, "test data: no clear gap at rank 32"
-        Pg = Bm.T @ Bm
-        Po = ref["basis"].T @ ref["basis"]
-        assert np.abs(Pg - Po).max() <= SUBSPACE_TOL
-        assert np.array_equal(resid, ref["resid"]), (resid, ref["resid"])
-    return ref
+        full = len(sv) > 32 and sv[31] > 1e-6 * sv[0]
+        if full and sv[31] ** 2 - sv[32] ** 2 >= UNIQUE_GAP * sv[31] ** 2:
+            Pg = Bm.T @ Bm
+            Po = ref["basis"].T @ ref["basis"]
+            assert np.abs(Pg - Po).max() <= SUBSPACE_TOL, np.abs(Pg - Po).max()
+            if n_resid:
+                eo = ref["err"]
+                kth_o = np.sort(eo)[::-1][n_resid - 1]
+                tau_o = RESID_BAND_REL * max(xmax, 1e-30)
+                chosen = np.zeros(P, bool)
+                chosen[resid] = True
+                assert np.all(chosen[eo > kth_o + tau_o]), "the oracle keeps a clearly larger error"
+                assert not np.any(chosen[eo < kth_o - tau_o]), "the oracle drops this token"
+            compared = True
+    return ref, compared
 
 
 def raw_rows(case, phys, g):
     return case.k_pool[phys, g], case.v_pool[phys, g]
 
 
-def run_codec_parity(case, n_resid, gapped, iters=0, decode=True, slack=ENERGY_SLACK):
-    H.note(f"dkv compress {case.name} R={n_resid} iters={iters} gapped={gapped}")
+def run_codec_parity(case, n_resid, iters=0, decode=True, min_compared=0.9):
+    """Compress every older block on the GPU, check each record (see
+    check_record), require the subspace comparison on at least `min_compared`
+    of them, and decode end to end."""
+    H.note(f"dkv compress {case.name} R={n_resid} iters={iters}")
     dc, dkv, recs, host = compress_on_gpu(case, n_resid, iters)
     kp, vp = pools_f64(case)
     older = older_blocks(case)
@@ -155,13 +176,17 @@ def run_codec_parity(case, n_resid, gapped, iters=0, decode=True, slack=ENERGY_S
             if (phys, g) not in written:
                 assert np.all(host[phys, g] == POISON), f"record ({phys}, {g}) was touched"
     oracle_recs, gpu_recs = {}, {}
+    n_cmp = 0
     for _, _, phys in older:
         for g in range(case.Hkv):
             f = wl.dkv_unpack(host[phys, g], case.dtype, case.D, case.P, n_resid)
-            ref = check_record(case, raw_rows(case, phys, g), f, kp[phys, g], vp[phys, g], n_resid,
-                               gapped, slack, iters or DEFAULT_ROUNDS)
+            ref, compared = check_record(case, raw_rows(case, phys, g), f, kp[phys, g], vp[phys, g],
+                                         n_resid, iters)
+            n_cmp += compared
             oracle_recs[(phys, g)] = ref
             gpu_recs[(phys, g)] = f
+    if iters == 0 and older:
+        assert n_cmp >= min_compared * len(older) * case.Hkv, (n_cmp, len(older) * case.Hkv)
     if not decode:
         return
     # end to end: decode every older block of every sequence
@@ -187,7 +212,7 @@ def run_codec_parity(case, n_resid, gapped, iters=0, decode=True, slack=ENERGY_S
     assert np.abs(out - ref).max() <= H.OUT_TOL[case.dtype]
     fin = np.isfinite(ref_lse)
     assert np.abs(lse[fin] - ref_lse[fin]).max(initial=0.0) <= H.LSE_TOL
-    if gapped:
+    if iters == 0:
         ref2, _ = DKV.decode(q, kp, vp, oracle_recs, case.block_table, case.ctx_lens, sel, nsel,
                              **args)
         assert np.abs(ref - ref2).max() <= CODEC_OUT_TOL
@@ -199,30 +224,33 @@ def run_codec_parity(case, n_resid, gapped, iters=0, decode=True, slack=ENERGY_S
     ("fp32", 64, 256, 1, 8),
     ("bf16", 64, 256, 3, 8),
 ])
-def test_compress_gapped_blocks_match_the_svd(dtype, D, P, Hkv, R):
+def test_compress_planted_low_rank_blocks_match_the_svd(dtype, D, P, Hkv, R):
     case = codec_case(dtype, D, P, 2 * Hkv, Hkv, [5 * P + 17, 3 * P], W=P, seed=800 + D + P,
                       n_spikes=R)
-    run_codec_parity(case, R, gapped=True)
+    run_codec_parity(case, R, min_compared=1.0)
 
 
 @pytest.mark.parametrize("dtype,D,P,values,R", [
     ("bf16", 128, 64, "lowrank", 8),
     ("fp16", 64, 64, "iid", 16),
     ("bf16", 128, 256, "iid", 0),
+    ("bf16", 128, 256, "iid", 16),     # the DKV shape without a planted gap
+    ("bf16", 128, 256, "chscale", 16),
     ("fp32", 128, 128, "iid", 64),
+    ("fp16", 64, 128, "chscale", 8),
     ("bf16", 128, 256, "lowrank", 40),  # more residual tokens than planted spikes
     ("bf16", 64, 64, "iid", 64),        # every token residual: the decode is exact attention
 ])
-def test_compress_properties_without_a_gap(dtype, D, P, values, R):
+def test_compress_matches_the_svd_without_a_planted_gap(dtype, D, P, values, R):
     case = codec_case(dtype, D, P, 4, 2, [6 * P + 3, 2 * P + P // 2], W=P // 2,
                       seed=820 + D + P + R, values=values, n_spikes=8)
-    run_codec_parity(case, R, gapped=False)
+    run_codec_parity(case, R)
 
 
 def test_compress_after_one_round_keeps_the_properties():
     case = codec_case("bf16", 128, 256, 2, 2, [4 * 256], W=0, seed=841, values="iid")
     # one round is far from converged: no bound on the captured energy
-    run_codec_parity(case, 16, gapped=False, iters=1, slack=None)
+    run_codec_parity(case, 16, iters=1)
 
 
 def test_compress_constant_and_rank_deficient_blocks():
@@ -256,13 +284,13 @@ def test_compress_constant_and_rank_deficient_blocks():
         assert rec_err <= 1e-5 * np.abs(X).max(), rec_err
         norms = np.linalg.norm(Bm, axis=1)
         assert np.all((np.abs(norms - 1.0) < 1e-5) | (norms == 0.0))
-    run_codec_parity(case, R, gapped=False)
+    run_codec_parity(case, R, min_compared=0.0)
 
 
 def test_compress_skips_window_blocks_and_empty_sequences():
     # sequence 1 is empty, sequence 2 lies wholly inside the window
     case = codec_case("bf16", 128, 64, 8, 2, [10 * 64 + 5, 0, 100], W=128, seed=843, values="iid")
-    run_codec_parity(case, 4, gapped=False)
+    run_codec_parity(case, 4)
 
 
 def test_dkv_workload_full_size():
@@ -282,8 +310,9 @@ def test_dkv_workload_full_size():
     for _, _, phys in sample:
         for g in range(case.Hkv):
             f = wl.dkv_unpack(host[phys, g], case.dtype, case.D, case.P, 16)
-            check_record(case, raw_rows(case, phys, g), f, kp[phys, g], vp[phys, g], 16,
-                         gapped=True)
+            _, compared = check_record(case, raw_rows(case, phys, g), f, kp[phys, g], vp[phys, g],
+                                       16)
+            assert compared
     buf = dev.alloc_buffers(dc)
     dev.build_summaries(dc, buf)
     dev.score_topk(dc, buf)
@@ -328,4 +357,4 @@ def test_compress_random_configurations(i):
     W = int(rng.integers(0, 2 * P))
     case = codec_case(dtype, D, P, 2 * Hkv, Hkv, ctx, W, seed=98_000 + i, values=values,
                       n_spikes=max(R, 1))
-    run_codec_parity(case, R, gapped=False)
+    run_codec_parity(case, R)
