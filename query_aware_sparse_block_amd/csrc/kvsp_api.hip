@@ -199,6 +199,11 @@ kvsp_status launch_checked_decode(const kvsp_layout& l, const kvsp_select_params
   a.n_head_groups = g.n_head_groups;
   a.max_chunks = g.max_chunks;
   a.total_items = g.total_items;
+  // Several head groups per KV head re-read its tiles: keep each chunk's
+  // groups on one XCD (the renumbering needs whole rounds of 8 XCDs x groups
+  // and a grid that is a multiple of 8).
+  a.xcd_share = (g.n_head_groups > 1 && g.total_items % (8 * g.n_head_groups) == 0 &&
+                 g.num_wgs % 8 == 0) ? 1 : 0;
   const float s = scale > 0.f ? scale : 1.0f / __builtin_sqrtf(static_cast<float>(l.head_dim));
   a.scale_log2 = s * 1.4426950408889634f;
   return from_hip(launch_decode(a, l.dtype, g.gp, g.num_wgs, stream));

@@ -78,6 +78,7 @@ struct DecodeShape {
 };
 
 constexpr int kDecodeWaves = 4;
+constexpr int kXcds = 8;  // accelerator complex dies of the MI355X, each with its own L2
 
 struct SeqWork {
   int32_t L, Cw, k, dense, A, T, CT, nc;
@@ -279,7 +280,23 @@ __global__ __launch_bounds__(256) void attend_kernel(DecodeArgs a) {
       coherent_rsrc(a.part_acc, static_cast<uint32_t>(static_cast<int64_t>(a.total_items) * GP * D * sizeof(float)));
 
   const int n_groups = a.total_items / a.max_chunks;
-  for (int item = blockIdx.x; item < a.total_items; item += gridDim.x) {
+  for (int wg = blockIdx.x; wg < a.total_items; wg += gridDim.x) {
+    // The dispatcher deals consecutive workgroups round-robin to the 8 XCDs
+    // (XCD = wg % 8 while the grid is a multiple of 8), each with its own L2.
+    // When several head groups read one KV head (xcd_share), the workgroups
+    // that share a (sequence, KV head, chunk) get consecutive slots of one
+    // XCD, so its L2 serves their common tiles after the first read;
+    // otherwise the item is the workgroup index itself.
+    int item = wg;
+    if (a.xcd_share) {
+      const int slot = wg / kXcds;
+      const int hg_w = slot % a.n_head_groups;
+      const int unit = (slot / a.n_head_groups) * kXcds + wg % kXcds;  // (pair, chunk), chunk-major
+      const int n_pairs = n_groups / a.n_head_groups;
+      const int c_w = unit / n_pairs;
+      const int pair = unit - c_w * n_pairs;
+      item = c_w * n_groups + pair * a.n_head_groups + hg_w;
+    }
 #if KVSP_CHUNK_MAJOR
     // Chunk-major order: consecutive workgroups (which the dispatcher deals
     // round-robin to the XCDs) take the same chunk of different groups, so

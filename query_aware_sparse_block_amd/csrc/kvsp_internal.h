@@ -80,6 +80,7 @@ struct DecodeArgs {
   int32_t n_head_groups;        // ceil(G / GP)
   int32_t max_chunks;
   int32_t total_items;          // B * Hkv * n_head_groups * max_chunks
+  int32_t xcd_share;            // 1: the head groups of a KV head's chunk share an XCD
   float scale_log2;             // softmax scale * log2(e)
 };
 
