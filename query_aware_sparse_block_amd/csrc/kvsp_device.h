@@ -252,6 +252,13 @@ __device__ __forceinline__ void store_coherent4(__amdgpu_buffer_rsrc_t r, uint32
   __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, byte_off, 0, kCachePolicySc1);
 }
 
+__device__ __forceinline__ void store_coherent1(__amdgpu_buffer_rsrc_t r, uint32_t byte_off, float v) {
+  __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, byte_off, 0, kCachePolicySc1);
+}
+
+// A buffer offset past every range: a store there is dropped by the hardware.
+constexpr uint32_t kDroppedOffset = 0xFFFFFFF0u;
+
 // Waits until every memory access this wavefront issued has completed.
 __device__ __forceinline__ void wait_stores_done() {
   __atomic_signal_fence(__ATOMIC_SEQ_CST);

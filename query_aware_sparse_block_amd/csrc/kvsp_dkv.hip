@@ -425,7 +425,7 @@ __global__ __launch_bounds__(256) void dkv_attend_kernel(DkvDecodeArgs a) {
     }
 
     // ---- merge the chunks of (b, g) ------------------------------------------------
-    const int64_t slot = static_cast<int64_t>(pair) * S + idx;
+    // (chunk idx's partial lives at slot pair * S + idx)
     if (n_act == 1) {
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
@@ -440,15 +440,29 @@ __global__ __launch_bounds__(256) void dkv_attend_kernel(DkvDecodeArgs a) {
       }
       continue;
     }
+    {
+      // Rows of padding heads (h >= G) are never merged: their stores get an
+      // offset past the buffer's range, which the hardware drops (no branch,
+      // no memory traffic).
+      const int64_t pbase = static_cast<int64_t>(pair) * S * 16;
+      const __amdgpu_buffer_rsrc_t wacc =
+          coherent_rsrc(a.part_acc + pbase * D, static_cast<uint32_t>(S * 16 * D * sizeof(float)));
+      const __amdgpu_buffer_rsrc_t wml =
+          coherent_rsrc(a.part_ml + pbase * 2, static_cast<uint32_t>(S * 16 * 2 * sizeof(float)));
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const int h = 4 * gi + v;
+      for (int v = 0; v < 4; ++v) {
+        const int h = 4 * gi + v;
+        const bool real = h < G;
 #pragma unroll
-      for (int dt = 0; dt < NDT; ++dt)
-        store_coherent(a.part_acc + (slot * 16 + h) * D + dbase + 16 * dt + hl, acc[dt][v]);
-      if (wave == 0 && hl == 0) {
-        store_coherent(a.part_ml + (slot * 16 + h) * 2 + 0, m_run[v]);
-        store_coherent(a.part_ml + (slot * 16 + h) * 2 + 1, l_run[v]);
+        for (int dt = 0; dt < NDT; ++dt) {
+          const uint32_t off = static_cast<uint32_t>(((idx * 16 + h) * D + dbase + 16 * dt + hl) * sizeof(float));
+          store_coherent1(wacc, real ? off : kDroppedOffset, acc[dt][v]);
+        }
+        if (wave == 0 && hl == 0) {
+          const uint32_t off = static_cast<uint32_t>((idx * 16 + h) * 2 * sizeof(float));
+          store_coherent1(wml, real ? off : kDroppedOffset, m_run[v]);
+          store_coherent1(wml, real ? off + 4 : kDroppedOffset, l_run[v]);
+        }
       }
     }
     wait_stores_done();  // the partial is at the device coherence point before it is counted
