@@ -38,7 +38,9 @@
  *     hipHostGetDevicePointer returns. The kernels then read, across PCIe,
  *     only the tiles they touch (for kvsp_sparse_decode: the kept blocks and
  *     the window), which is the offloaded-cache setting of the SparPR page;
- *     results are bit-identical to a device-resident pool.
+ *     results are bit-identical to a device-resident pool. The decode entry
+ *     points ask HIP (hipPointerGetAttributes) whether k_pool is host memory
+ *     and then read K in whole rows, which PCIe carries in larger requests.
  *   - Work is enqueued on `stream` (0 = the null stream) and returns without
  *     waiting for it. No entry point allocates memory, synchronises the host
  *     or copies device data to the host. The library keeps no pointer after

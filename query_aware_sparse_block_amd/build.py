@@ -17,7 +17,7 @@ INCLUDE = os.path.join(ROOT, "include")
 OBJDIR = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libkvsp.so")
 SOURCES = ["kvsp_api.hip", "kvsp_summaries.hip", "kvsp_append.hip", "kvsp_select.hip",
-           "kvsp_decode.hip", "kvsp_dkv.hip"]
+           "kvsp_decode.hip", "kvsp_decode_host.hip", "kvsp_dkv.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 

@@ -126,6 +126,18 @@ WorkspaceLayout workspace_layout(const kvsp_layout& l) {
 
 kvsp_status from_hip(hipError_t e) { return e == hipSuccess ? KVSP_OK : KVSP_ERR_HIP; }
 
+// True if p lies in host memory mapped for the device (a pool kept in host
+// RAM): there the decode reads K row-major, in larger PCIe requests.
+// Device memory, and anything HIP does not know, count as device memory.
+bool in_host_memory(const void* p) {
+  hipPointerAttribute_t attr;
+  if (hipPointerGetAttributes(&attr, p) != hipSuccess) {
+    (void)hipGetLastError();  // clear the sticky error of an unknown pointer
+    return false;
+  }
+  return attr.type == hipMemoryTypeHost;
+}
+
 // Host checks shared by every decode entry point (no HIP call).
 kvsp_status check_decode(const kvsp_layout* layout, const kvsp_select_params* params, bool all_dense,
                          const void* q, const void* k_pool, const void* v_pool,
@@ -206,6 +218,7 @@ kvsp_status launch_checked_decode(const kvsp_layout& l, const kvsp_select_params
                  g.num_wgs % 8 == 0) ? 1 : 0;
   const float s = scale > 0.f ? scale : 1.0f / __builtin_sqrtf(static_cast<float>(l.head_dim));
   a.scale_log2 = s * 1.4426950408889634f;
+  if (in_host_memory(k_pool)) return from_hip(launch_decode_host(a, l.dtype, g.gp, g.num_wgs, stream));
   return from_hip(launch_decode(a, l.dtype, g.gp, g.num_wgs, stream));
 }
 

@@ -137,6 +137,9 @@ hipError_t launch_score_select(const ScoreArgs& sa, const TopkArgs& ta, int32_t*
                                int dtype, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs& a, int dtype, int group_pad, int num_wgs,
                          hipStream_t stream);
+// The same for a K pool in host memory (row-major K loads; kvsp_decode_host.hip).
+hipError_t launch_decode_host(const DecodeArgs& a, int dtype, int group_pad, int num_wgs,
+                              hipStream_t stream);
 
 // Host-side sizing shared by the entry points and kvsp_workspace_bytes.
 int decode_group_pad(const kvsp_layout& l);  // GP: heads per work item (1, 2, 4, 8 or 16)

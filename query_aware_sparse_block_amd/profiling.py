@@ -24,8 +24,8 @@ import sys
 _PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(_PKG)
 PROFILES = os.path.join(ROOT, "profiles")
-DECODE_SOURCES = ["csrc/kvsp_decode.hip", "csrc/kvsp_device.h", "csrc/kvsp_api.hip",
-                  "csrc/kvsp_internal.h"]
+DECODE_SOURCES = ["csrc/kvsp_attend.h", "csrc/kvsp_decode.hip", "csrc/kvsp_device.h",
+                  "csrc/kvsp_api.hip", "csrc/kvsp_internal.h"]
 SELECT_SOURCES = ["csrc/kvsp_select.hip", "csrc/kvsp_device.h", "csrc/kvsp_api.hip",
                   "csrc/kvsp_internal.h"]
 DKV_SOURCES = ["csrc/kvsp_dkv.hip", "csrc/kvsp_device.h", "csrc/kvsp_api.hip",
