@@ -80,3 +80,50 @@ def test_dkv_codec_and_decode_from_host_pool():
                       buf.lse.cpu().numpy())
     for a, b, name in zip(got["device"], got["host"], ("records", "selected", "out", "lse")):
         assert np.array_equal(a, b), name
+
+
+def _decode_forms(dc):
+    """Summaries, selection and the decode in both forms of the kept blocks."""
+    buf = dev.alloc_buffers(dc)
+    dev.build_summaries(dc, buf)
+    dev.score_topk(dc, buf)
+    res = {}
+    for form in ("spans", "selected"):
+        out = torch.full_like(buf.out, float("nan"))
+        dev.sparse_decode(dc, buf, form=form, out=out)
+        torch.cuda.synchronize()
+        res[form] = out.cpu().numpy()
+    return res
+
+
+# every row length the host-memory K path transposes (D * E = 128, 256 and
+# 512 bytes) with one-head, four-head and sixteen-head items
+_SHAPES = (("bf16", 64, 16), ("fp16", 64, 1), ("fp32", 128, 4), ("fp32", 64, 16),
+           ("bf16", 128, 16), ("fp16", 128, 8))
+_N_RANDOM = 24
+
+
+def _shape_case(idx):
+    """The first _N_RANDOM of the random-shape test's cases, then _SHAPES."""
+    if idx < _N_RANDOM:
+        from tests.test_gpu_random_shapes import random_case
+        return random_case(idx)
+    dtype, D, G = _SHAPES[idx - _N_RANDOM]
+    return wl.make_case(f"host-{dtype}-D{D}-G{G}", seed=97_000 + D + G, B=3, Hq=2 * G, Hkv=2, D=D,
+                        P=32, dtype=dtype, ctx_lens=[1000, 640, 31], top_k=5, keep_floor=2,
+                        recent_window=40)
+
+
+@pytest.mark.parametrize("idx", range(_N_RANDOM + len(_SHAPES)))
+def test_host_pool_decode_shapes_match_device_pool(idx):
+    # The decode reads K row-major from a host-memory pool and puts it in the
+    # MFMA layout through LDS: the outputs must be bit-identical to the
+    # device pool's for every dtype, head dim and head-group size, in both
+    # forms of the kept blocks.
+    case = _shape_case(idx)
+    H.note(f"[host pool] shape {case.name}")
+    dc = dev.upload(case)
+    on_device = _decode_forms(dc)
+    on_host = _decode_forms(dev.with_host_pool(dc))
+    for form in ("spans", "selected"):
+        assert np.array_equal(on_device[form], on_host[form], equal_nan=True), form
