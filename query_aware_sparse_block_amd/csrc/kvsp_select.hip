@@ -38,16 +38,36 @@ namespace kvsp {
 // returns C (the sequence's candidate count). COHERENT stores make the scores
 // visible to other workgroups of the same launch.
 
+// The group-summed queries in LDS. A lane of a group takes summary vectors
+// gl, gl + LG, ... and multiplies each vector's 4 components by the matching
+// query sums. Stored row-major (element x at qbar[x]), those reads have a
+// 32-byte stride across the lanes and pile several lanes onto each bank
+// (measured: a quarter of the serving call's time stalled on LDS bank
+// conflicts). So when the group's LG * VPL vectors are at most 1024 (32 KiB
+// of doubles), they are stored component-major with stride QS = LG * VPL:
+// component c of vector i at qbar[c * QS + i], zero for i past the row's
+// end, and a lane's reads are consecutive doubles across the group, at
+// offsets known when compiling. Longer rows keep the row-major layout
+// (QS = 0), which uses less LDS.
+template <int LG, int VPL>
+__host__ __device__ constexpr int qbar_stride() { return VPL <= 16 ? LG * VPL : 0; }
+template <int LG, int VPL>
+__host__ __device__ constexpr int qbar_doubles(int row) {
+  return qbar_stride<LG, VPL>() ? 4 * qbar_stride<LG, VPL>() : row;
+}
+
 // STREAM (a.stream_rows as a template parameter) reads the summary rows with
 // non-temporal loads and runs the passes as a branch-free pipeline.
 template <typename T, int LG, int VPL, bool COHERENT, bool STREAM>
 __device__ __forceinline__ int score_blocks(const ScoreArgs& a, double* qbar, int b) {
+  constexpr int QS = qbar_stride<LG, VPL>();
   const int lane = threadIdx.x % kWave;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int per_wg = 4 * a.blocks_per_wave;
   const int first = blockIdx.x * per_wg;
   const int row = a.Hkv * a.D;
-  int32_t* phys_lds = reinterpret_cast<int32_t*>(qbar + row);
+  const int nvec = row / 4;
+  int32_t* phys_lds = reinterpret_cast<int32_t*>(qbar + qbar_doubles<LG, VPL>(row));
   const int64_t trow = static_cast<int64_t>(b) * a.max_blocks;
   // Block-table entries of this workgroup's range (in bounds of the row
   // whatever the context length; entries past C are never used).
@@ -84,7 +104,19 @@ __device__ __forceinline__ int score_blocks(const ScoreArgs& a, double* qbar, in
       }
     }
 #pragma unroll
-    for (int e = 0; e < EPV; ++e) qbar[v * EPV + e] = s[e];
+    for (int e = 0; e < EPV; ++e) {
+      const int x = v * EPV + e;
+      if constexpr (QS != 0) {
+        qbar[(x % 4) * QS + x / 4] = s[e];
+      } else {
+        qbar[x] = s[e];
+      }
+    }
+  }
+  if constexpr (QS != 0) {
+    for (int i = nvec + threadIdx.x; i < QS; i += blockDim.x)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) qbar[c * QS + i] = 0.0;
   }
   const SelectArgs sel{a.top_k, a.keep_num, a.keep_den, a.keep_floor, a.recent_window,
                        a.gamma_num, a.gamma_den};
@@ -100,7 +132,6 @@ __device__ __forceinline__ int score_blocks(const ScoreArgs& a, double* qbar, in
   // LG * VPL >= nvec of them and the lanes past the row's end contribute 0.
   // The first pass reads its block-table entries itself (`direct`), so its
   // summary loads leave before the workgroup barrier that publishes qbar.
-  const int nvec = row / 4;
   // Large summary sets are read once per call with non-temporal loads
   // (a.stream_rows, uniform); small ones may stay cached between calls.
   auto issue = [&](int jb, float4 (&sv)[VPL], bool direct, bool repeat = false) {
@@ -144,22 +175,32 @@ __device__ __forceinline__ int score_blocks(const ScoreArgs& a, double* qbar, in
       // sum starts at +0.0, so its bits are those of the sum over the row).
 #pragma unroll
       for (int v = 0; v < VPL; ++v) {
-        const double in = gl + LG * v < nvec ? 1.0 : 0.0;
-        const double* qv = qbar + 4 * min(gl + LG * v, nvec - 1);
-        acc += (qv[0] * in) * static_cast<double>(sv[v].x);
-        acc += (qv[1] * in) * static_cast<double>(sv[v].y);
-        acc += (qv[2] * in) * static_cast<double>(sv[v].z);
-        acc += (qv[3] * in) * static_cast<double>(sv[v].w);
+        if constexpr (QS != 0) {
+          // past the row's end the query sums are 0.0
+          const double* qv = qbar + gl + LG * v;
+          acc += qv[0] * static_cast<double>(sv[v].x);
+          acc += qv[QS] * static_cast<double>(sv[v].y);
+          acc += qv[2 * QS] * static_cast<double>(sv[v].z);
+          acc += qv[3 * QS] * static_cast<double>(sv[v].w);
+        } else {
+          const double in = gl + LG * v < nvec ? 1.0 : 0.0;
+          const double* qv = qbar + 4 * min(gl + LG * v, nvec - 1);
+          acc += (qv[0] * in) * static_cast<double>(sv[v].x);
+          acc += (qv[1] * in) * static_cast<double>(sv[v].y);
+          acc += (qv[2] * in) * static_cast<double>(sv[v].z);
+          acc += (qv[3] * in) * static_cast<double>(sv[v].w);
+        }
       }
     } else {
 #pragma unroll
       for (int v = 0; v < VPL; ++v) {
         if (gl + LG * v < nvec) {
-          const double* qv = qbar + 4 * (gl + LG * v);
+          constexpr int CS = QS != 0 ? QS : 1;  // stride between a vector's components
+          const double* qv = QS != 0 ? qbar + gl + LG * v : qbar + 4 * (gl + LG * v);
           acc += qv[0] * static_cast<double>(sv[v].x);
-          acc += qv[1] * static_cast<double>(sv[v].y);
-          acc += qv[2] * static_cast<double>(sv[v].z);
-          acc += qv[3] * static_cast<double>(sv[v].w);
+          acc += qv[CS] * static_cast<double>(sv[v].y);
+          acc += qv[2 * CS] * static_cast<double>(sv[v].z);
+          acc += qv[3 * CS] * static_cast<double>(sv[v].w);
         }
       }
     }
@@ -225,7 +266,7 @@ __device__ __forceinline__ int score_blocks(const ScoreArgs& a, double* qbar, in
 
 template <typename T, int LG, int VPL, bool STREAM>
 __global__ __launch_bounds__(256) void score_kernel(ScoreArgs a) {
-  extern __shared__ double qbar[];  // [Hkv * D] group-summed queries, then [4 * bpw] ints
+  extern __shared__ double qbar[];  // group-summed queries (qbar_doubles), then [4 * bpw] ints
   score_blocks<T, LG, VPL, false, STREAM>(a, qbar, blockIdx.y);
 }
 
@@ -233,7 +274,8 @@ template <typename T, int LG, int VPL>
 static hipError_t launch_score_v(const ScoreArgs& a, hipStream_t stream) {
   const int per_wg = 4 * a.blocks_per_wave;
   dim3 grid((a.max_blocks + per_wg - 1) / per_wg, a.B);
-  const size_t lds = static_cast<size_t>(a.Hkv) * a.D * sizeof(double) + per_wg * sizeof(int32_t);
+  const size_t lds = static_cast<size_t>(qbar_doubles<LG, VPL>(a.Hkv * a.D)) * sizeof(double) +
+                     per_wg * sizeof(int32_t);
   if (a.stream_rows)
     hipLaunchKernelGGL((score_kernel<T, LG, VPL, true>), grid, dim3(256), lds, stream, a);
   else
@@ -603,7 +645,8 @@ static hipError_t launch_fused_v(const ScoreArgs& sa, const TopkArgs& ta, int32_
                                  hipStream_t stream) {
   const int per_wg = 4 * sa.blocks_per_wave;
   dim3 grid((sa.max_blocks + per_wg - 1) / per_wg, sa.B);
-  const size_t score_lds = static_cast<size_t>(sa.Hkv) * sa.D * sizeof(double) + per_wg * sizeof(int32_t);
+  const size_t score_lds = static_cast<size_t>(qbar_doubles<LG, VPL>(sa.Hkv * sa.D)) * sizeof(double) +
+                           per_wg * sizeof(int32_t);
   const size_t topk_lds = sizeof(TopkShared);
   const size_t lds = (std::max(score_lds, topk_lds) + 7) / 8 * 8;
   if (sa.stream_rows)

@@ -11,6 +11,11 @@ plain-copy reference the counters are scaled by.
       Per-launch HBM bytes of KERNEL (attend, score or dkv_attend) from two
       --pmc runs, scaled by the copy reference, stamped with the digest of the
       kernel's sources; written to profiles/traffic_KERNEL_WORKLOAD.txt.
+  python -m query_aware_sparse_block_amd.profiling counters KERNEL WORKLOAD "COMMANDS" CSV [CSV ...]
+      The median per launch of every counter the --pmc runs' CSVs hold for
+      KERNEL (rocprofv3's derived metrics: VALUBusy, OccupancyPercent, ...),
+      stamped with the sources' digest; written to
+      profiles/counters_KERNEL_WORKLOAD.txt.
 """
 
 from __future__ import annotations
@@ -137,6 +142,30 @@ def recorded_traffic(workload, kernel="attend"):
     return float(kv["traffic_bytes"])
 
 
+def write_counters(kernel, workload, commands, *csvs):
+    prefixes, sources, title = KERNELS[kernel]
+    values = {}
+    for path in csvs:
+        for r in _rows(path):
+            if any(k in r["Kernel_Name"] for k in prefixes):
+                values.setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+    if not values:
+        raise RuntimeError(f"no {prefixes} dispatch in {csvs}")
+    lines = [f"# rocprofv3 counters of {title}, median per launch",
+             f"kernel = {kernel}",
+             f"workload = {workload}",
+             f"source_digest = {source_digest(sources)}"]
+    for name in sorted(values):
+        v = values[name]
+        lines.append(f"{name} = {statistics.median(v):.2f}  (dispatches {len(v)}, "
+                     f"min {min(v):.2f}, max {max(v):.2f})")
+    lines.append(f"commands = {commands}")
+    out_txt = os.path.join(PROFILES, f"counters_{kernel}_{workload.replace('/', '_')}.txt")
+    with open(out_txt, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def write_stats(stats_csv, out_txt, command, top=12):
     rows = _rows(stats_csv)
     rows.sort(key=lambda r: -float(r["TotalDurationNs"]))
@@ -165,6 +194,8 @@ def main(argv):
         write_stats(argv[1], argv[2], argv[3])
     elif cmd == "traffic":
         write_traffic(*argv[1:8])
+    elif cmd == "counters":
+        write_counters(*argv[1:])
     else:
         print(__doc__)
         return 2
