@@ -35,6 +35,8 @@ SELECT_SOURCES = ["csrc/kvsp_select.hip", "csrc/kvsp_device.h", "csrc/kvsp_api.h
                   "csrc/kvsp_internal.h"]
 DKV_SOURCES = ["csrc/kvsp_dkv.hip", "csrc/kvsp_device.h", "csrc/kvsp_api.hip",
                "csrc/kvsp_internal.h"]
+SUMMARY_SOURCES = ["csrc/kvsp_summaries.hip", "csrc/kvsp_device.h", "csrc/kvsp_api.hip",
+                   "csrc/kvsp_internal.h"]
 COPY_BYTES = 1 << 30
 # kernel key -> (name prefixes as rocprofv3 prints them, sources, title). The
 # DKV kernel's name also contains "attend_kernel", so the main one is matched
@@ -44,6 +46,9 @@ KERNELS = {
     "score": (["kvsp::score_select_kernel<", "kvsp::score_kernel<"], SELECT_SOURCES,
               "the scoring kernel (score_select_kernel / score_kernel)"),
     "dkv_attend": (["dkv_attend_kernel<"], DKV_SOURCES, "the DKV decode kernel (dkv_attend_kernel)"),
+    "dkv_compress": (["dkv_compress_kernel<"], DKV_SOURCES, "the DKV codec kernel (dkv_compress_kernel)"),
+    "summaries": (["build_summaries_kernel<"], SUMMARY_SOURCES,
+                  "the summary build kernel (build_summaries_kernel)"),
 }
 COPY_KERNEL = "__amd_rocclr_copyBuffer"
 
