@@ -132,7 +132,7 @@ kvsp_status from_hip(hipError_t e) { return e == hipSuccess ? KVSP_OK : KVSP_ERR
 bool in_host_memory(const void* p) {
   hipPointerAttribute_t attr;
   if (hipPointerGetAttributes(&attr, p) != hipSuccess) {
-    (void)hipGetLastError();  // clear the sticky error of an unknown pointer
+    (void)hipGetLastError();  // consumed here, so the launch check does not report it
     return false;
   }
   return attr.type == hipMemoryTypeHost;
