@@ -629,33 +629,38 @@ __device__ __forceinline__ float codec_start_value(uint32_t i) {
   return static_cast<float>(x >> 8) * (1.0f / 8388608.0f) - 1.0f;
 }
 
+typedef double doublex4 __attribute__((ext_vector_type(4)));
+
+// W[i][j] = sum over the N channels of sh.qt[ra + i][c] * sh.qt[rb + j][c],
+// i, j < 32, in double on v_mfma_f64_16x16x4f64, into sh.g: wave w (of 4)
+// takes the 16 x 16 tile (w / 2, w % 2), four channels per step (lane l
+// supplies row l % 16 of each operand at channel 4 s + l / 16, widened to
+// double; result i of lane l is row 4 i + l / 16, column l % 16 of the tile,
+// the layout of this instruction's output on gfx950, checked on the device).
+template <int N>
+__device__ __forceinline__ void codec_dot32(CodecShared<N>& sh, int tid, int ra, int rb) {
+  const int wave = tid / kWave, lane = tid % kWave;
+  const int ti = wave / 2, tj = wave % 2;
+  const int m = lane % 16, kk = lane / 16;
+  const float* arow = &sh.qt[ra + 16 * ti + m][kk];
+  const float* brow = &sh.qt[rb + 16 * tj + m][kk];
+  doublex4 acc = {0.0, 0.0, 0.0, 0.0};
+#pragma unroll 8
+  for (int c = 0; c < N; c += 4)
+    acc = __builtin_amdgcn_mfma_f64_16x16x4f64(static_cast<double>(arow[c]), static_cast<double>(brow[c]),
+                                               acc, 0, 0, 0);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) sh.g[16 * ti + 4 * i + kk][16 * tj + m] = acc[i];
+}
+
 // Cholesky QR, in place, of the 32 vectors in rows [r0, r0 + 32) of sh.qt:
-// the Gram of the column-scaled vectors in double, a 32-step Cholesky with the
+// the Gram of the column-scaled vectors in double (codec_dot32, then scaled),
+// a 32-step Cholesky with the
 // drop rule above, and a forward substitution per channel in double. Starts
 // after a barrier that published the rows and ends with one.
 template <int N>
 __device__ void codec_cholqr32(CodecShared<N>& sh, int tid, int r0) {
-  {
-    const int i = tid / 8, jq = tid % 8;
-    double g0 = 0.0, g1 = 0.0, g2 = 0.0, g3 = 0.0;
-#pragma unroll 4
-    for (int c = 0; c < N; c += 4) {
-      const float4 zi = *reinterpret_cast<const float4*>(&sh.qt[r0 + i][c]);
-      const float4 z0 = *reinterpret_cast<const float4*>(&sh.qt[r0 + 4 * jq + 0][c]);
-      const float4 z1 = *reinterpret_cast<const float4*>(&sh.qt[r0 + 4 * jq + 1][c]);
-      const float4 z2 = *reinterpret_cast<const float4*>(&sh.qt[r0 + 4 * jq + 2][c]);
-      const float4 z3 = *reinterpret_cast<const float4*>(&sh.qt[r0 + 4 * jq + 3][c]);
-      const double a0 = zi.x, a1 = zi.y, a2 = zi.z, a3 = zi.w;
-      g0 += a0 * z0.x + a1 * z0.y + a2 * z0.z + a3 * z0.w;
-      g1 += a0 * z1.x + a1 * z1.y + a2 * z1.z + a3 * z1.w;
-      g2 += a0 * z2.x + a1 * z2.y + a2 * z2.z + a3 * z2.w;
-      g3 += a0 * z3.x + a1 * z3.y + a2 * z3.z + a3 * z3.w;
-    }
-    sh.g[i][4 * jq + 0] = g0;
-    sh.g[i][4 * jq + 1] = g1;
-    sh.g[i][4 * jq + 2] = g2;
-    sh.g[i][4 * jq + 3] = g3;
-  }
+  codec_dot32<N>(sh, tid, r0, r0);
   __syncthreads();
   if (tid < kRank) {
     const double d = sh.g[tid][tid];
@@ -698,30 +703,11 @@ __device__ void codec_cholqr32(CodecShared<N>& sh, int tid, int r0) {
 }
 
 // Rows [32, 64) of sh.qt minus their projection on rows [0, 32), which are
-// orthonormal: W = Q1^T Z2 in double, then Z2 -= Q1 W per channel in double.
+// orthonormal: W = Q1^T Z2 in double (codec_dot32), then Z2 -= Q1 W per
+// channel in double.
 template <int N>
 __device__ void codec_project_out(CodecShared<N>& sh, int tid) {
-  {
-    const int i = tid / 8, jq = tid % 8;
-    double w0 = 0.0, w1 = 0.0, w2 = 0.0, w3 = 0.0;
-#pragma unroll 4
-    for (int c = 0; c < N; c += 4) {
-      const float4 qi = *reinterpret_cast<const float4*>(&sh.qt[i][c]);
-      const float4 z0 = *reinterpret_cast<const float4*>(&sh.qt[kRank + 4 * jq + 0][c]);
-      const float4 z1 = *reinterpret_cast<const float4*>(&sh.qt[kRank + 4 * jq + 1][c]);
-      const float4 z2 = *reinterpret_cast<const float4*>(&sh.qt[kRank + 4 * jq + 2][c]);
-      const float4 z3 = *reinterpret_cast<const float4*>(&sh.qt[kRank + 4 * jq + 3][c]);
-      const double a0 = qi.x, a1 = qi.y, a2 = qi.z, a3 = qi.w;
-      w0 += a0 * z0.x + a1 * z0.y + a2 * z0.z + a3 * z0.w;
-      w1 += a0 * z1.x + a1 * z1.y + a2 * z1.z + a3 * z1.w;
-      w2 += a0 * z2.x + a1 * z2.y + a2 * z2.z + a3 * z2.w;
-      w3 += a0 * z3.x + a1 * z3.y + a2 * z3.z + a3 * z3.w;
-    }
-    sh.g[i][4 * jq + 0] = w0;
-    sh.g[i][4 * jq + 1] = w1;
-    sh.g[i][4 * jq + 2] = w2;
-    sh.g[i][4 * jq + 3] = w3;
-  }
+  codec_dot32<N>(sh, tid, 0, kRank);
   __syncthreads();
   if (tid < N) {
     const int c = tid;
