@@ -761,7 +761,10 @@ __device__ void codec_jacobi(CodecShared<N>& sh, int tid) {
   }
   __syncthreads();
   for (int sweep = 0; sweep < kJacobiSweeps; ++sweep) {
-    // stop once the off-diagonal square sum is below 1e-24 of the total
+    // stop once the off-diagonal square sum is below kOff of the total: 1e-24
+    // for the Ritz vectors, 1e-12 when only the Ritz values are wanted (they
+    // set the round count, which needs far less than 1e-6 relative accuracy)
+    constexpr double kOff = VECTORS ? 1e-24 : 1e-12;
     double off = 0.0, all = 0.0;
     for (int e = tid; e < V * V; e += 256) {
       const double h = sh.g[e / V][e % V];
@@ -778,7 +781,7 @@ __device__ void codec_jacobi(CodecShared<N>& sh, int tid) {
     const double off_t = sh.red[0][0] + sh.red[0][1] + sh.red[0][2] + sh.red[0][3];
     const double all_t = sh.red[1][0] + sh.red[1][1] + sh.red[1][2] + sh.red[1][3];
     __syncthreads();
-    if (!(off_t > 1e-24 * all_t)) break;  // uniform: every thread read the same sums
+    if (!(off_t > kOff * all_t)) break;  // uniform: every thread read the same sums
     for (int r = 0; r < V - 1; ++r) {
       if (tid < V / 2) {
         int p, q;
