@@ -607,7 +607,7 @@ struct CodecShared {
   } v;
   float y[kXChunk][kYRow];                    // Y = X Q of the chunk
   double g[kIterVecs][kIterVecs + 1];         // Gram of Z S (Cholesky QR) or H (Rayleigh-Ritz)
-  double rdiag[kIterVecs];
+  double rdiag[kIterVecs];                     // 1 / the Cholesky diagonal (0 where dropped)
   double cs[kIterVecs];                       // column scales
   double jc[kIterVecs / 2], js[kIterVecs / 2];  // Jacobi rotations of one round
   double red[2][4];
@@ -682,7 +682,7 @@ __device__ void codec_cholqr32(CodecShared<N>& sh, int tid, int r0) {
       if (i > k && j >= i) sh.g[i][j] -= (sh.g[k][i] * inv) * (sh.g[k][j] * inv);
     }
     if (tid > k && tid < kRank) sh.g[tid][k] = sh.g[k][tid] * inv;
-    if (tid == k) sh.rdiag[k] = rkk;
+    if (tid == k) sh.rdiag[k] = inv;  // the substitution multiplies by 1 / r (0 if dropped)
     __syncthreads();
   }
   if (tid < N) {
@@ -693,8 +693,7 @@ __device__ void codec_cholqr32(CodecShared<N>& sh, int tid, int r0) {
       double s = static_cast<double>(sh.qt[r0 + j][c]) * sh.cs[j];
 #pragma unroll
       for (int i = 0; i < j; ++i) s -= x[i] * sh.g[j][i];
-      const double r = sh.rdiag[j];
-      x[j] = r > 0.0 ? s / r : 0.0;
+      x[j] = s * sh.rdiag[j];
     }
 #pragma unroll
     for (int j = 0; j < kRank; ++j) sh.qt[r0 + j][c] = static_cast<float>(x[j]);
@@ -703,23 +702,33 @@ __device__ void codec_cholqr32(CodecShared<N>& sh, int tid, int r0) {
 }
 
 // Rows [32, 64) of sh.qt minus their projection on rows [0, 32), which are
-// orthonormal: W = Q1^T Z2 in double (codec_dot32), then Z2 -= Q1 W per
-// channel in double.
+// orthonormal: W = Q1^T Z2 in double (codec_dot32), then Z2 -= Q1 W in
+// double, both on f64 MFMA.
 template <int N>
 __device__ void codec_project_out(CodecShared<N>& sh, int tid) {
   codec_dot32<N>(sh, tid, 0, kRank);
   __syncthreads();
-  if (tid < N) {
-    const int c = tid;
-    float q1[kRank];
+  // Z2 -= Q1 W on v_mfma_f64_16x16x4f64, over the (channel, vector) plane of
+  // Z2 in 16 x 16 tiles, tile t = (channels 16 (t / 2).., vectors 16 (t % 2)..)
+  // taken by wave t % 4: the accumulator starts at Z2 and the A operand is
+  // -Q1 (lane l supplies channel l % 16 of vector 4 s + l / 16), the B
+  // operand W (row 4 s + l / 16, column l % 16); result i of lane l is
+  // channel 4 i + l / 16, vector l % 16 of the tile.
+  {
+    const int wave = tid / kWave, lane = tid % kWave;
+    const int m = lane % 16, kk = lane / 16;
+    constexpr int NT = (N / 16) * (kRank / 16);
+    for (int t = wave; t < NT; t += 4) {
+      const int c0 = 16 * (t / 2), j0 = 16 * (t % 2);
+      doublex4 acc;
 #pragma unroll
-    for (int i = 0; i < kRank; ++i) q1[i] = sh.qt[i][c];
-#pragma unroll 4
-    for (int j = 0; j < kRank; ++j) {
-      double z = sh.qt[kRank + j][c];
+      for (int i = 0; i < 4; ++i) acc[i] = static_cast<double>(sh.qt[kRank + j0 + m][c0 + 4 * i + kk]);
 #pragma unroll
-      for (int i = 0; i < kRank; ++i) z -= static_cast<double>(q1[i]) * sh.g[i][j];
-      sh.qt[kRank + j][c] = static_cast<float>(z);
+      for (int s = 0; s < kRank / 4; ++s)
+        acc = __builtin_amdgcn_mfma_f64_16x16x4f64(-static_cast<double>(sh.qt[4 * s + kk][c0 + m]),
+                                                   sh.g[4 * s + kk][j0 + m], acc, 0, 0, 0);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sh.qt[kRank + j0 + m][c0 + 4 * i + kk] = static_cast<float>(acc[i]);
     }
   }
   __syncthreads();
