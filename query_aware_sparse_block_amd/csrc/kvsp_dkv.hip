@@ -774,7 +774,7 @@ __device__ void codec_jacobi(CodecShared<N>& sh, int tid) {
     // for the Ritz vectors (an off-diagonal norm of 1e-8 of H's moves the
     // 32-vector subspace by 1e-8 over the relative gap at 32, far below the
     // float32 basis it feeds wherever that subspace is well defined), 1e-12
-    // when only the Ritz values are wanted (they set the round count)
+    // when only the Ritz values are wanted
     constexpr double kOff = VECTORS ? 1e-16 : 1e-12;
     double off = 0.0, all = 0.0;
     for (int e = tid; e < V * V; e += 256) {
@@ -1039,11 +1039,14 @@ __global__ __launch_bounds__(256) void dkv_compress_kernel(DkvCompressArgs a) {
     };
 
     int rounds = a.power_iters > 0 ? a.power_iters : kRoundCap;
+    bool ritz_done = false;  // uniform: the final Rayleigh-Ritz is already in sh
     for (int k = 0;; ++k) {
       if (a.power_iters == 0 && k == kFirstRounds) {
-        // Ritz values of the current iterate: the measured rate sets the rounds
+        // Rayleigh-Ritz of the current iterate: its values (the measured
+        // rate) set the rounds, and when no more rounds are needed its
+        // vectors are the final ones (the iterate does not change again)
         x_pass(true);
-        codec_jacobi<N, false>(sh, tid);
+        codec_jacobi<N, true>(sh, tid);
         const double t32 = sh.g[sh.perm[kRank - 1]][sh.perm[kRank - 1]];
         const double t64 = sh.g[sh.perm[V - 1]][sh.perm[V - 1]];
         const double rho = t32 > 0.0 ? fmax(t64, 0.0) / t32 : 0.0;
@@ -1055,6 +1058,7 @@ __global__ __launch_bounds__(256) void dkv_compress_kernel(DkvCompressArgs a) {
           want = need > kRoundCap ? kRoundCap : (need < kFirstRounds ? kFirstRounds : static_cast<int>(need));
         }
         rounds = want;  // the same on every thread (LDS values after a barrier)
+        ritz_done = rounds <= k;
         __syncthreads();
       }
       if (k >= rounds) break;
@@ -1063,8 +1067,10 @@ __global__ __launch_bounds__(256) void dkv_compress_kernel(DkvCompressArgs a) {
     }
 
     // Rayleigh-Ritz: basis rows = (Q U)^T for the 32 largest Ritz values
-    x_pass(true);
-    codec_jacobi<N, true>(sh, tid);
+    if (!ritz_done) {
+      x_pass(true);
+      codec_jacobi<N, true>(sh, tid);
+    }
     {
       const double tmax = sh.g[sh.perm[0]][sh.perm[0]];
       if (tid < N) {
