@@ -449,8 +449,9 @@ __device__ __forceinline__ void select_sequence_r(const TopkArgs& a, int b, Topk
   const uint32_t key_prev = has_prev ? order_key(raw_prev) : 0u;
   const uint32_t key_next = has_next ? order_key(raw_next) : 0u;
 
-  // Radix select of the k-th largest key T (only when 0 < k < C): after the
-  // last pass, `take_equal` of the `eq_total` keys equal to T are kept.
+  // Radix select of the k-th largest key T (only when 0 < k < C), 8 bits a
+  // pass from the top: after the last pass, `take_equal` of the `eq_total`
+  // keys equal to T are kept.
   uint32_t thresh = 0;
   int take_equal = 0, eq_total = 0;
   const bool partial = k > 0 && k < C;
@@ -494,6 +495,15 @@ __device__ __forceinline__ void select_sequence_r(const TopkArgs& a, int b, Topk
       eq_total = static_cast<int>(__builtin_amdgcn_readlane(n_sel, src));
       prefix |= digit << shift;
       mask |= 0xFFu << shift;
+      // The digit's keys are all needed: the k best are exactly the keys
+      // whose prefix is at least this one, so the threshold is the prefix
+      // with zero low bits and no tie is cut (uniform: every wave reads the
+      // same histogram).
+      if (krem == eq_total) {
+        krem = 0;
+        eq_total = 0;
+        break;
+      }
     }
     thresh = prefix;
     take_equal = krem;
