@@ -273,7 +273,7 @@ __global__ __launch_bounds__(256) void attend_kernel(DecodeArgs a) {
   __shared__ int32_t mark_lds[kDecodeWaves][SPANS ? kWave : 1];  // per-wave window marks
   __shared__ float alpha_lds[kDecodeWaves][16];
   __shared__ float ml_lds[kDecodeWaves][2][16];
-  __shared__ float xacc[kDecodeWaves - 1][GP * D];
+  __shared__ float xacc[kDecodeWaves][GP * D];
   // HOSTK: a sub-tile's K rows, each padded by 16 bytes so that the reads in
   // the A layout (16 rows at one column) fall in different banks.
   constexpr int KROW = D * E + 16;
@@ -594,84 +594,79 @@ __global__ __launch_bounds__(256) void attend_kernel(DecodeArgs a) {
 #pragma unroll
       for (int e = 0; e < S::EPV; ++e) acc[h][e] = fold_sum<S::LPR>(acc[h][e]);
 
-    // Merge the four wavefronts: M = max_w m_w, weights 2^(m_w - M).
+    // Merge the four wavefronts. Each leaves its (m, l) per head and its
+    // unscaled sums for the heads its row groups own in LDS; after one
+    // barrier every thread takes OPT consecutive outputs (one head, channels
+    // d0 .. d0 + OPT) and combines the four waves: M = max_w m_w, weights
+    // 2^(m_w - M), summed in wave order. The outputs (or the chunk's partial)
+    // are thus written by all four waves at once.
     if (lane < 16) {
       ml_lds[wave][0][hl] = m_run;
       ml_lds[wave][1][hl] = l_run;
     }
-    __syncthreads();
-    float scale_h[GP];
 #pragma unroll
     for (int h = 0; h < GP; ++h) {
-      float M = NEG_INF;
+      if (h % S::NRG != rg) continue;
 #pragma unroll
-      for (int v = 0; v < kDecodeWaves; ++v) M = fmaxf(M, ml_lds[v][0][h]);
-      scale_h[h] = M == NEG_INF ? 0.f : __builtin_amdgcn_exp2f(ml_lds[wave][0][h] - M);
-    }
-    if (wave > 0) {
-#pragma unroll
-      for (int h = 0; h < GP; ++h) {
-        if (h % S::NRG != rg) continue;
-#pragma unroll
-        for (int e = 0; e < S::EPV; ++e) xacc[wave - 1][h * D + col + e] = acc[h][e] * scale_h[h];
-      }
+      for (int e = 0; e < S::EPV; ++e) xacc[wave][h * D + col + e] = acc[h][e];
     }
     __syncthreads();
-    if (wave == 0) {
-      // lanes of row group rg own heads h with h % NRG == rg
-      float mh_lane, lh_lane;  // merged (m, l) of head hl
-      {
+    {
+      constexpr int OUTS = GP * D;
+      constexpr int OPT = OUTS >= 2048 ? 8 : (OUTS >= 256 ? OUTS / 256 : 1);
+      const int o0 = threadIdx.x * OPT;
+      if (o0 < OUTS) {
+        const int h = o0 / D;
+        const int d0 = o0 % D;
+        float mw[kDecodeWaves], lw[kDecodeWaves];
         float M = NEG_INF;
 #pragma unroll
-        for (int v = 0; v < kDecodeWaves; ++v) M = fmaxf(M, ml_lds[v][0][hl]);
+        for (int v = 0; v < kDecodeWaves; ++v) {
+          mw[v] = ml_lds[v][0][h];
+          lw[v] = ml_lds[v][1][h];
+          M = fmaxf(M, mw[v]);
+        }
+        float o[OPT];
+#pragma unroll
+        for (int e = 0; e < OPT; ++e) o[e] = 0.f;
         float Ls = 0.f;
-        if (M != NEG_INF) {
 #pragma unroll
-          for (int v = 0; v < kDecodeWaves; ++v)
-            Ls += ml_lds[v][1][hl] * __builtin_amdgcn_exp2f(ml_lds[v][0][hl] - M);
+        for (int v = 0; v < kDecodeWaves; ++v) {
+          const float wv = M == NEG_INF ? 0.f : __builtin_amdgcn_exp2f(mw[v] - M);
+          Ls += lw[v] * wv;
+#pragma unroll
+          for (int e = 0; e < OPT; ++e) o[e] += xacc[v][o0 + e] * wv;
         }
-        mh_lane = M;
-        lh_lane = Ls;
+        const int hq = g * G + hg * GP + h;
+        if (hg * GP + h < G) {
+          if (w.nc == 1) {
+            const float inv = Ls > 0.f ? 1.f / Ls : 0.f;
+            float* dst = a.out + (static_cast<int64_t>(b) * a.Hq + hq) * D + d0;
+#pragma unroll
+            for (int e = 0; e < OPT; ++e) dst[e] = o[e] * inv;
+            if (d0 == 0 && a.lse != nullptr)
+              a.lse[static_cast<int64_t>(b) * a.Hq + hq] =
+                  Ls > 0.f ? (M + __builtin_log2f(Ls)) * 0.69314718055994531f : NEG_INF;
+          } else {
+            const int64_t slot = static_cast<int64_t>(grp) * a.max_chunks + c;
+            const uint32_t off = static_cast<uint32_t>(((slot * GP + h) * D + d0) * sizeof(float));
+            if constexpr (OPT >= 4) {
+#pragma unroll
+              for (int e = 0; e < OPT; e += 4)
+                store_coherent4(part_rsrc, off + e * sizeof(float), make_float4(o[e], o[e + 1], o[e + 2], o[e + 3]));
+            } else {
+#pragma unroll
+              for (int e = 0; e < OPT; ++e) store_coherent1(part_rsrc, off + e * sizeof(float), o[e]);
+            }
+          }
+        }
+        if (w.nc > 1 && d0 == 0) {
+          const int64_t slot = static_cast<int64_t>(grp) * a.max_chunks + c;
+          store_coherent(a.part_ml + (slot * GP + h) * 2 + 0, M);
+          store_coherent(a.part_ml + (slot * GP + h) * 2 + 1, Ls);
+        }
       }
-      if (lane < 16) alpha_lds[0][hl] = lh_lane;  // l of every head, for the normalisation
-      wave_lds_sync();
-      const int64_t slot = static_cast<int64_t>(grp) * a.max_chunks + c;
-#pragma unroll
-      for (int h = 0; h < GP; ++h) {
-        if (h % S::NRG != rg || hg * GP + h >= G) continue;
-        float o[S::EPV];
-#pragma unroll
-        for (int e = 0; e < S::EPV; ++e) {
-          float s = acc[h][e] * scale_h[h];
-#pragma unroll
-          for (int v = 1; v < kDecodeWaves; ++v) s += xacc[v - 1][h * D + col + e];
-          o[e] = s;
-        }
-        if (w.nc == 1) {
-          const float lh = alpha_lds[0][h];
-          const float inv = lh > 0.f ? 1.f / lh : 0.f;
-          float* dst = a.out + (static_cast<int64_t>(b) * a.Hq + g * G + hg * GP + h) * D + col;
-#pragma unroll
-          for (int e = 0; e < S::EPV; ++e) dst[e] = o[e] * inv;
-        } else {
-          const uint32_t off = static_cast<uint32_t>(((slot * GP + h) * D + col) * sizeof(float));
-#pragma unroll
-          for (int e = 0; e < S::EPV; e += 4)
-            store_coherent4(part_rsrc, off + e * sizeof(float), make_float4(o[e], o[e + 1], o[e + 2], o[e + 3]));
-        }
-      }
-      if (w.nc == 1) {
-        if (a.lse != nullptr && head_ok && lane < 16)
-          a.lse[static_cast<int64_t>(b) * a.Hq + hq_lane] =
-              lh_lane > 0.f ? (mh_lane + __builtin_log2f(lh_lane)) * 0.69314718055994531f
-                            : NEG_INF;
-      } else {
-        if (lane < GP) {
-          store_coherent(a.part_ml + (slot * GP + lane) * 2 + 0, mh_lane);
-          store_coherent(a.part_ml + (slot * GP + lane) * 2 + 1, lh_lane);
-        }
-        wait_stores_done();  // the partial is at the device coherence point before it is counted
-      }
+      if (w.nc > 1) wait_stores_done();  // the partial is at the device coherence point before it is counted
     }
     if (w.nc > 1) {
       __syncthreads();
