@@ -520,22 +520,32 @@ __global__ __launch_bounds__(256) void attend_kernel(DecodeArgs a) {
       if (lane < 16) alpha_lds[wave][hl] = alpha;
       wave_lds_sync();
 
+      // alpha is exactly 1 for every head whose running max did not move, and
+      // scaling by 1 changes no bit: the rescale is skipped when that holds
+      // for all heads (wave-uniform).
+      if (__ballot(alpha != 1.f) != 0) {
 #pragma unroll
-      for (int h = 0; h < GP; ++h) {
-        const float al = alpha_lds[wave][h];
+        for (int h = 0; h < GP; ++h) {
+          const float al = alpha_lds[wave][h];
 #pragma unroll
-        for (int e = 0; e < S::EPV; ++e) acc[h][e] *= al;
+          for (int e = 0; e < S::EPV; ++e) acc[h][e] *= al;
+        }
       }
-      const bool partial = i0 + S::SUB > end;  // wave-uniform
+      // Rows past `end` (only in a chunk's last sub-tile, wave-uniform) may
+      // hold any bits: their packed values are zeroed before use.
+      uint4 vraw[S::VLD];
+#pragma unroll
+      for (int r = 0; r < S::VLD; ++r) vraw[r] = st.vv[r];
+      if (i0 + S::SUB > end) {
+#pragma unroll
+        for (int r = 0; r < S::VLD; ++r)
+          if (i0 + r * S::RPL + rg >= end) vraw[r] = make_uint4(0, 0, 0, 0);
+      }
 #pragma unroll
       for (int r = 0; r < S::VLD; ++r) {
         const int rr = r * S::RPL + rg;
         float vf[S::EPV];
-        T::widen(st.vv[r], vf);
-        if (partial && i0 + rr >= end) {
-#pragma unroll
-          for (int e = 0; e < S::EPV; ++e) vf[e] = 0.f;  // stale rows may hold any bits
-        }
+        T::widen(vraw[r], vf);
         const float* prow = &p_lds[wave][rr * S::PROW];
 #pragma unroll
         for (int h = 0; h < GP; ++h) {
