@@ -473,13 +473,28 @@ __global__ __launch_bounds__(256) void dkv_attend_kernel(DkvDecodeArgs a) {
     }
     __syncthreads();
     if (!last_flag) continue;
-    // Every chunk's (m, l) at once: a wave per head, a lane per chunk; the
-    // chunk weights 2^(m_c - M) go to LDS.
+    // Every chunk's (m, l) at once: a wave per head (heads wave, wave + 4,
+    // ... all requested together), a lane per chunk; lanes past n_act read
+    // the last chunk and are masked. The chunk weights 2^(m_c - M) go to LDS.
     const int64_t slot0 = static_cast<int64_t>(pair) * S;
-    for (int h = wave; h < G; h += 4) {
+    constexpr int kHeadsPerWave = 16 / 4;  // at most 16 heads per KV head (the MFMA columns)
+    float m_in[kHeadsPerWave], l_in[kHeadsPerWave];
+    {
+      const int cl = min(lane, n_act - 1);
+#pragma unroll
+      for (int i = 0; i < kHeadsPerWave; ++i) {
+        const int h = min(wave + 4 * i, G - 1);
+        m_in[i] = load_coherent(a.part_ml + ((slot0 + cl) * 16 + h) * 2);
+        l_in[i] = load_coherent(a.part_ml + ((slot0 + cl) * 16 + h) * 2 + 1);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < kHeadsPerWave; ++i) {
+      const int h = wave + 4 * i;
+      if (h >= G) break;  // wave-uniform
       const bool has = lane < n_act;
-      const float mc = has ? load_coherent(a.part_ml + ((slot0 + lane) * 16 + h) * 2) : NEG_INF;
-      const float lc = has ? load_coherent(a.part_ml + ((slot0 + lane) * 16 + h) * 2 + 1) : 0.f;
+      const float mc = has ? m_in[i] : NEG_INF;
+      const float lc = has ? l_in[i] : 0.f;
       const bool valid = lc > 0.f;
       const float M = group_max<64>(valid ? mc : NEG_INF);
       const float wc = valid ? __builtin_amdgcn_exp2f(mc - M) : 0.f;
