@@ -1,4 +1,4 @@
-"""GPU parity on seeded random configurations. A hundred shapes drawn from a
+"""GPU parity on seeded random configurations. Three hundred shapes drawn from a
 fixed seed cover combinations that the hand-picked cases do not: every
 dtype, head dims 64 and 128, block sizes 16 to 256, 1 to 8 KV heads with 1 to
 20 query heads each, 1 to 6 sequences of ragged lengths (some empty, some
@@ -16,7 +16,7 @@ from tests import gpu_helpers as H
 
 pytestmark = pytest.mark.gpu
 
-N_CASES = 100
+N_CASES = 300
 
 
 def random_case(i):
