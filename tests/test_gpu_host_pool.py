@@ -127,3 +127,19 @@ def test_host_pool_decode_shapes_match_device_pool(idx):
     on_host = _decode_forms(dev.with_host_pool(dc))
     for form in ("spans", "selected"):
         assert np.array_equal(on_device[form], on_host[form], equal_nan=True), form
+
+
+def test_host_pool_sixteen_head_fp32_items():
+    # fp32, D = 128, 16 heads per KV head and enough (sequence, KV head)
+    # pairs that items keep all 16 heads: the host-memory kernel with the
+    # most LDS (row-major K staging plus the four waves' 16-head sums).
+    case = wl.make_case("host-fp32-D128-G16-B4", seed=97_500, B=4, Hq=32, Hkv=2, D=128, P=32,
+                        dtype="fp32", ctx_lens=[900, 1000, 33, 640], top_k=5, keep_floor=2,
+                        recent_window=40)
+    H.note(f"[host pool] shape {case.name}")
+    dc = dev.upload(case)
+    on_device = _decode_forms(dc)
+    on_host = _decode_forms(dev.with_host_pool(dc))
+    for form in ("spans", "selected"):
+        assert np.array_equal(on_device[form], on_host[form], equal_nan=True), form
+    H.full_parity(case)
