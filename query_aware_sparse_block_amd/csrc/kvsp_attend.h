@@ -494,12 +494,20 @@ __global__ __launch_bounds__(256) void attend_kernel(DecodeArgs a) {
 #pragma unroll
         for (int s = 0; s < S::KLD; ++s) sc = QkMfma<T>::step(kt[t][s], qop[s], sc);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int tok = i0 + 16 * t + 4 * (lane / 16) + i;
-          s2[t][i] = tok < end ? sc[i] * a.scale_log2 : NEG_INF;
-          mloc = fmaxf(mloc, s2[t][i]);
-        }
+        for (int i = 0; i < 4; ++i) s2[t][i] = sc[i] * a.scale_log2;
       }
+      // Tokens past `end` exist only in a chunk's last sub-tile (wave-uniform).
+      if (i0 + S::SUB > end) {
+#pragma unroll
+        for (int t = 0; t < S::TILES; ++t)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (i0 + 16 * t + 4 * (lane / 16) + i >= end) s2[t][i] = NEG_INF;
+      }
+#pragma unroll
+      for (int t = 0; t < S::TILES; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) mloc = fmaxf(mloc, s2[t][i]);
       mloc = fold_max<16>(mloc);  // over the four lanes holding head hl
       const float m_new = fmaxf(m_run, mloc);
       const bool none = m_new == NEG_INF;
