@@ -573,7 +573,7 @@ kvsp_status kvsp_score_topk(const kvsp_layout* layout, const kvsp_select_params*
   ta.recent_window = p.recent_window;
   ta.gamma_num = p.gamma_num;
   ta.gamma_den = p.gamma_den;
-  if (fused_select_supported(l.max_blocks_per_seq)) {
+  if (fused_select_supported(l.max_blocks_per_seq, score_workgroups(sa))) {
     int32_t* counters = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + wl.select_counters);
     return from_hip(launch_score_select(sa, ta, counters, l.dtype, stream));
   }

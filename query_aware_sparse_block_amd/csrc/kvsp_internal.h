@@ -130,9 +130,11 @@ hipError_t launch_append(const AppendArgs& a, int dtype, int D, hipStream_t stre
 hipError_t launch_build_summaries(const SummaryArgs& a, int dtype, int D, hipStream_t stream);
 hipError_t launch_score(const ScoreArgs& a, int dtype, hipStream_t stream);
 hipError_t launch_topk(const TopkArgs& a, hipStream_t stream);
-// Scores and Top-k in one launch (max_blocks within fused_select_supported);
+// Scores and Top-k in one launch (when fused_select_supported for the table
+// length and the scoring workgroups of the whole batch, score_workgroups);
 // counters: [B] ints, zero between calls.
-bool fused_select_supported(int max_blocks);
+int64_t score_workgroups(const ScoreArgs& sa);
+bool fused_select_supported(int max_blocks, int64_t workgroups);
 hipError_t launch_score_select(const ScoreArgs& sa, const TopkArgs& ta, int32_t* counters,
                                int dtype, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs& a, int dtype, int group_pad, int num_wgs,

@@ -648,7 +648,25 @@ __global__ __launch_bounds__(256) void score_select_kernel(ScoreArgs sa, TopkArg
   if (threadIdx.x == 0) store_coherent_i(counters + b, 0);
 }
 
-constexpr int kFusedSelectMaxBlocks = 4 * kWave * kTopkMaxPerThread;
+// The Top-k runs in the scoring launch (by the last scoring workgroup of a
+// sequence, four waves) only for tables of at most KVSP_FUSED_SELECT_MAX_BLOCKS
+// blocks scored by at most KVSP_FUSED_SELECT_MAX_WORKGROUPS workgroups in all;
+// otherwise the scores are written and a Top-k launch of its own follows,
+// with KVSP_TOPK_PER_THREAD candidates a thread (up to sixteen waves). Measured:
+// with many scoring workgroups per sequence their completion atomics and the
+// four-wave Top-k of a long table cost more than a second launch.
+#ifndef KVSP_FUSED_SELECT_MAX_BLOCKS
+#define KVSP_FUSED_SELECT_MAX_BLOCKS 512
+#endif
+#ifndef KVSP_FUSED_SELECT_MAX_WORKGROUPS
+#define KVSP_FUSED_SELECT_MAX_WORKGROUPS 64
+#endif
+#ifndef KVSP_TOPK_PER_THREAD
+#define KVSP_TOPK_PER_THREAD 2
+#endif
+constexpr int kFusedSelectMaxBlocks = KVSP_FUSED_SELECT_MAX_BLOCKS;
+static_assert(kFusedSelectMaxBlocks <= 4 * kWave * kTopkMaxPerThread,
+              "the fused Top-k holds at most 16 candidates a thread");
 
 template <typename T, int LG, int VPL>
 static hipError_t launch_fused_v(const ScoreArgs& sa, const TopkArgs& ta, int32_t* counters,
@@ -684,7 +702,14 @@ static hipError_t launch_fused_t(const ScoreArgs& sa, const TopkArgs& ta, int32_
   return with_score_shape(sa.Hkv, sa.D, FusedLauncher<T>{sa, ta, counters, stream});
 }
 
-bool fused_select_supported(int max_blocks) { return max_blocks <= kFusedSelectMaxBlocks; }
+bool fused_select_supported(int max_blocks, int64_t workgroups) {
+  return max_blocks <= kFusedSelectMaxBlocks && workgroups <= KVSP_FUSED_SELECT_MAX_WORKGROUPS;
+}
+
+int64_t score_workgroups(const ScoreArgs& sa) {
+  const int per_wg = 4 * sa.blocks_per_wave;
+  return static_cast<int64_t>((sa.max_blocks + per_wg - 1) / per_wg) * sa.B;
+}
 
 hipError_t launch_score_select(const ScoreArgs& sa, const TopkArgs& ta, int32_t* counters,
                                int dtype, hipStream_t stream) {
@@ -693,9 +718,10 @@ hipError_t launch_score_select(const ScoreArgs& sa, const TopkArgs& ta, int32_t*
   return launch_fused_t<BF16>(sa, ta, counters, stream);
 }
 
-// The fewest wavefronts that hold every candidate at 16 per thread.
+// The fewest wavefronts that hold every candidate at KVSP_TOPK_PER_THREAD a
+// thread (at most sixteen waves, which then hold up to 16 a thread).
 hipError_t launch_topk(const TopkArgs& a, hipStream_t stream) {
-  const int per_wave = kWave * kTopkMaxPerThread;
+  const int per_wave = kWave * KVSP_TOPK_PER_THREAD;
   const int waves = (a.max_blocks + per_wave - 1) / per_wave;
   if (waves <= 1) return launch_topk_w<1>(a, stream);
   if (waves <= 2) return launch_topk_w<2>(a, stream);
