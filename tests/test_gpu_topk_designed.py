@@ -1,8 +1,9 @@
 """Top-k on designed scores. The radix select takes the k-th key's top byte
 first and stops at the first pass whose digit is needed whole; these cases
 place that pass at each of the four bytes, cut exact ties, take ties whole,
-mix signs and zeros, and tie every candidate, on the fused selection (one
-and several candidates per thread) and on the two-kernel path of long tables.
+mix signs and zeros, and tie every candidate, on the fused selection (a short
+table scored by few workgroups) and on the separate Top-k launch (two and
+five candidates a thread).
 
 Scores are made exact: the group-summed query is e_0 (head 0 of the group
 holds 1.0 in channel 0, every other query element is 0) and every summary is
