@@ -2,8 +2,8 @@
 first and stops at the first pass whose digit is needed whole; these cases
 place that pass at each of the four bytes, cut exact ties, take ties whole,
 mix signs and zeros, and tie every candidate, on the fused selection (a short
-table scored by few workgroups) and on the separate Top-k launch (two and
-five candidates a thread).
+table scored by few workgroups, one and two candidates a thread) and on the
+separate Top-k launch (two and five candidates a thread).
 
 Scores are made exact: the group-summed query is e_0 (head 0 of the group
 holds 1.0 in channel 0, every other query element is 0) and every summary is
@@ -69,7 +69,8 @@ KINDS = ("whole-at-byte-0", "whole-at-byte-1", "whole-at-byte-2", "all-bytes", "
          "tie-whole", "signs-and-zeros", "all-equal")
 
 
-@pytest.mark.parametrize("C,k", [(200, 1), (200, 37), (1500, 20), (1500, 300), (5000, 37)])
+@pytest.mark.parametrize("C,k", [(200, 1), (200, 37), (500, 37), (500, 200), (1500, 20), (1500, 300),
+                                 (5000, 37)])
 def test_designed_scores_select_exactly(C, k):
     case = wl.make_case(f"designed-C{C}-k{k}", seed=88_000 + C + k, B=1, Hq=2, Hkv=1, D=64, P=16,
                         dtype="fp32", ctx_lens=[16 * C], shuffle=True, top_k=k, keep_floor=1,

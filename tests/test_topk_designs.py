@@ -31,7 +31,7 @@ EXPECTED = {"whole-at-byte-0": 0, "whole-at-byte-1": 1, "whole-at-byte-2": 2, "a
             "tie-whole": 0}
 
 
-@pytest.mark.parametrize("C,k", [(200, 37), (1500, 20), (1500, 300), (5000, 37)])
+@pytest.mark.parametrize("C,k", [(200, 37), (500, 37), (500, 200), (1500, 20), (1500, 300), (5000, 37)])
 def test_designs_reach_their_pass(C, k):
     rng = np.random.default_rng(C * 1000 + k)
     for kind in KINDS:
