@@ -25,6 +25,10 @@ def _snapshot(buf):
     ("serving-small", lambda: wl.c5(keep="1/32", B=8, L=4096)),
     ("serving-small-dense", lambda: wl.c5(keep="7/10", B=8, L=4096)),
     ("minicpm-small", lambda: wl.c3(keep="1/16", L=16384)),
+    # scored by more than 64 workgroups / a table longer than 512 blocks: the
+    # Top-k runs in a launch of its own
+    ("serving-b16", lambda: wl.c5(keep="1/32", B=16, L=4096)),
+    ("minicpm-long-table", lambda: wl.c3(keep="1/16", L=65536)),
 ])
 def test_graph_replays_match_eager(name, make):
     H.note(f"[graph] {name}")
