@@ -46,9 +46,11 @@ constexpr int kDecodeMaxChunks = 64;
 #define KVSP_DECODE_MIN_GP 4
 #endif
 // Scoring workgroups a launch aims for (a sequence's candidates are split
-// into whole waves' worth of blocks).
+// into whole waves' worth of blocks; short tables keep one pass per wave).
+// Measured on the serving shape with the separate Top-k launch: 1024 (four
+// workgroups per CU) scores faster than 512, 768 or 1536.
 #ifndef KVSP_SCORE_TARGET_WORKGROUPS
-#define KVSP_SCORE_TARGET_WORKGROUPS 512
+#define KVSP_SCORE_TARGET_WORKGROUPS 1024
 #endif
 constexpr int kScoreTargetWorkgroups = KVSP_SCORE_TARGET_WORKGROUPS;
 // Calls reading more summary bytes than this use non-temporal loads for them:
