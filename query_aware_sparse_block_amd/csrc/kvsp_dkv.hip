@@ -48,7 +48,6 @@ constexpr int kCRow = 36;  // LDS row stride (floats) of staged coefficient rows
 // floats apart put the 16 heads' 16-byte reads on distinct banks.
 constexpr int kQRow = 36;
 constexpr int kQaRow = 20;  // per-head anchor partials (16 used), same reasoning
-constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.69314718055994531f;
 
 __device__ __forceinline__ floatx4 mfma4(float a, float b, floatx4 c) {

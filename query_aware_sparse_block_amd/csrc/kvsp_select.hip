@@ -287,7 +287,6 @@ static hipError_t launch_score_v(const ScoreArgs& a, hipStream_t stream) {
 // least 16): LG, the largest power of two <= 64 with 8 * LG <= nvec lanes
 // per block, and VPL, the fewest of 8, 16 or 32 vectors per lane that cover
 // the row (16 at most below 64 lanes).
-constexpr int kScoreVecPerLane = 8;
 #ifndef KVSP_SCORE_MIN_VPL
 #define KVSP_SCORE_MIN_VPL 8
 #endif
